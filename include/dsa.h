@@ -1,0 +1,165 @@
+/*
+ * dsa.h — C ABI of the MI355X (gfx950) DeepSeek Sparse Attention hot path.
+ *
+ * The operations follow these pages (cited by title and section):
+ *   [R] "Техотчёт DeepSeek-V3.2 (2025): разреженное внимание DSA и
+ *       масштабирование RL" (ai.flicky.cc):
+ *         "Молниеносный индексатор" — index score
+ *             I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]) over a few FP8 heads,
+ *             q and w from the current token, k from an earlier one;
+ *         "Отбор и основное внимание" — u_t = Attn(h_t, {c_s : I[t,s] in
+ *             Top-k(I[t,:])}), k = 2048, computed in MLA's MQA mode: one
+ *             latent KV row is shared by every query head.
+ *   [N] neurosova.ru news item on DeepSeek-V3.2, "DeepSeek Sparse Attention":
+ *       a low-precision indexer over all token pairs, a selector keeping the
+ *       top-k key/value positions per query, MQA + MLA on the selected set.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Pointers named in the argument lists are DEVICE pointers owned by the
+ *    caller.  The library never allocates, frees or retains them, and keeps no
+ *    state between calls besides its loaded code objects.  Calls only enqueue
+ *    work on `stream` (a hipStream_t passed as void*, NULL = default stream)
+ *    and return; outputs are ready once the caller synchronises the stream.
+ *  * Host-side validation runs before any launch: a null pointer, a size or
+ *    stride that does not fit, a misaligned pointer (16 bytes for every
+ *    array except the batch arrays) or an unsupported shape returns an error
+ *    status and launches nothing.  Errors reported by the HIP runtime at
+ *    launch return DSA_ERR_HIP; faults inside kernels surface when the caller
+ *    synchronises.  No C++ exception crosses this interface.
+ *  * Supported shapes: indexer heads HI = 64 of dim DI = 128 (FP8 E4M3FN, the
+ *    OCP format, max 448); query heads H = 128 over D = 576 bf16 dims
+ *    (512 latent + 64 rope), value = the first Dv = 512 dims; 1 <= k <= 2048.
+ *    Anything else returns DSA_ERR_UNSUPPORTED.
+ *  * Positions: score columns and idx entries are positions local to their
+ *    sequence (0 = the sequence's first cache row).  Query row cu_q[b]+i sits
+ *    at absolute position pos0[b]+i and sees the keys 0..min(pos, ctx_b-1)
+ *    (the key of its own position included), where ctx_b = cu_kv[b+1]-cu_kv[b].
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, stride or alignment */
+    DSA_ERR_UNSUPPORTED = 2,   /* shape outside the supported set above */
+    DSA_ERR_WORKSPACE = 3,     /* workspace null or smaller than required */
+    DSA_ERR_HIP = 4            /* the HIP runtime rejected a launch */
+} dsa_status;
+
+/* Ragged batch of B sequences.  The scalars are host values (used for
+ * validation and grid sizing); the three arrays are device arrays that must
+ * agree with them.  Kernels clamp every cache access to [0, total_kv), so a
+ * descriptor whose arrays disagree with its scalars yields wrong values but
+ * no out-of-bounds access. */
+typedef struct {
+    int32_t batch;           /* B >= 1 */
+    int32_t total_q;         /* T = cu_q[B] >= 0 */
+    int32_t max_q;           /* max over b of cu_q[b+1]-cu_q[b] */
+    int32_t max_kv;          /* max over b of ctx_b, <= 2^24 */
+    int64_t total_kv;        /* N = cu_kv[B] */
+    const int32_t *cu_q;     /* [B+1] device, non-decreasing, cu_q[0] = 0 */
+    const int64_t *cu_kv;    /* [B+1] device, non-decreasing, cu_kv[0] = 0 */
+    const int32_t *pos0;     /* [B]   device, position of each sequence's first query */
+} dsa_batch;
+
+/* Index scores, [R] "Молниеносный индексатор":
+ *   I[t,s] = k_scale[s] * sum_j (w[t,j] * q_scale[t,j]) * max(0, sum_d q[t,j,d] * k[s,d])
+ * which equals eq. I on the dequantised inputs q[t,j,:]*q_scale[t,j] and
+ * k[s,:]*k_scale[s] (the scales are positive and ReLU is positively
+ * homogeneous).  FP8 products accumulate in fp32 on the matrix cores.
+ *   q_fp8   [T, HI, DI] uint8 E4M3FN codes      q_scale [T, HI] fp32 (> 0)
+ *   w       [T, HI]     fp32 head weights
+ *   k_fp8   [N, DI]     uint8 E4M3FN codes      k_scale [N] fp32 (> 0)
+ *   scores  [T, ld]     fp32 out: columns s < ctx_b of row t are written,
+ *                       -inf where s > pos (causally masked); columns >= ctx_b
+ *                       are left untouched.  ld >= max_kv.                    */
+dsa_status dsa_indexer_scores(const dsa_batch *batch,
+                              const uint8_t *q_fp8, const float *q_scale, const float *w,
+                              const uint8_t *k_fp8, const float *k_scale,
+                              int HI, int DI, float *scores, int64_t ld, void *stream);
+
+/* Top-k selection, [R] "Отбор и основное внимание" (Top-k(I[t,:])):
+ * for every query row, the k largest scores among its visible columns
+ * s <= min(pos, ctx_b-1), compared as fp32 values (-0 == +0), ties to the
+ * lower s; every visible column when there are at most k.  Output idx [T, k]
+ * int32: the selected positions in ascending order, padded with -1.
+ * Scores must be NaN-free.  Rows longer than 32768 columns are selected in
+ * 32768-column chunks whose exact local top-k candidates are merged; this
+ * needs workspace (dsa_workspace_size(DSA_WS_TOPK, ...)); ws may be NULL
+ * when that size is 0. */
+dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld, int k,
+                    int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/* Sparse attention in MLA's MQA mode, [R] "Отбор и основное внимание", eq. u,
+ * and [N]: for each query row t and head h,
+ *   z_s = scale * sum_{d<D} q[t,h,d] * kv[s,d]   over s in idx[t,:]
+ *   out[t,h,c] = sum_s softmax(z)_s * kv[s,c]     for c < Dv
+ *   lse[t,h]   = ln sum_s exp(z_s)
+ * Every head uses the same selected rows.  Entries of idx that are -1 or
+ * outside [0, ctx_b) are skipped; a row with no valid entry gives out = 0 and
+ * lse = -inf.  Accumulation in fp32 (online softmax), output rounded to bf16.
+ *   q   [T, H, D] bf16      kv [N, D] bf16 (latent rows; value = first Dv)
+ *   idx [T, k] int32        out [T, H, Dv] bf16        lse [T, H] fp32
+ * Workspace (dsa_workspace_size(DSA_WS_SPARSE_MLA, ...)) holds split-KV
+ * partial results when the batch has few query rows; it may be 0 bytes. */
+dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv,
+                              const int32_t *idx, int k, int H, int D, int Dv, float scale,
+                              uint16_t *out, float *lse, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* All inputs of one DSA forward (indexer + top-k + sparse MQA attention). */
+typedef struct {
+    dsa_batch batch;
+    const uint8_t *q_fp8;    /* [T, HI, DI] */
+    const float *q_scale;    /* [T, HI] */
+    const float *w;          /* [T, HI] */
+    const uint8_t *k_fp8;    /* [N, DI] indexer key cache */
+    const float *k_scale;    /* [N] */
+    const uint16_t *q;       /* [T, H, D] bf16 */
+    const uint16_t *kv;      /* [N, D] bf16 latent cache */
+    int32_t HI, DI, H, D, Dv, k;
+    float scale;             /* softmax scale, e.g. 1/sqrt(D) */
+} dsa_fwd_args;
+
+/* The whole hot path in one call, following the data flow of [R]
+ * "Отбор и основное внимание" (cheap selection first, then attention over the
+ * k selected rows): index scores -> top-k -> sparse MQA attention.  Results
+ * equal dsa_indexer_scores + dsa_topk + dsa_sparse_mla_fwd on the same inputs.
+ * dsa_prefill_fwd is tuned for many query rows per sequence (prefill, chunked
+ * prefill); dsa_decode_fwd for one or a few query rows per sequence over long
+ * contexts (split-KV).  Both accept any batch.
+ *   out [T, H, Dv] bf16, lse [T, H] fp32, idx_out [T, k] int32 (nullable:
+ *   the selected positions, as dsa_topk returns them).
+ * Workspace: dsa_workspace_size(DSA_WS_PREFILL or DSA_WS_DECODE, ...). */
+dsa_status dsa_prefill_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse,
+                           int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
+dsa_status dsa_decode_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse,
+                          int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
+
+typedef enum {
+    DSA_WS_TOPK = 0,
+    DSA_WS_SPARSE_MLA = 1,
+    DSA_WS_PREFILL = 2,
+    DSA_WS_DECODE = 3
+} dsa_ws_entry;
+
+/* Workspace bytes the given entry point needs for this batch (host only; reads
+ * only the host scalars of the batch).  Returns 0 on invalid arguments. */
+size_t dsa_workspace_size(dsa_ws_entry entry, const dsa_batch *batch, int k, int H, int Dv);
+
+const char *dsa_status_string(dsa_status status);
+const char *dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

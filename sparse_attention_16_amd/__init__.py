@@ -1,0 +1,201 @@
+"""MI355X (gfx950) DeepSeek Sparse Attention hot path: Python binding.
+
+Thin ctypes layer over ``libdsa.so`` (the C ABI declared in ``include/dsa.h``):
+it marshals torch device tensors into pointers and calls the library; every
+step of the path runs in the library's HIP kernels.  PyTorch provides device
+memory and streams only.  Importing this package fails loudly when the built
+library is missing: there is no fallback implementation.
+
+Entry points (same names as the C ABI, without the ``dsa_`` prefix):
+    indexer_scores, topk, sparse_mla_fwd, prefill_fwd, decode_fwd,
+    workspace_size, status_string, version
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m sparse_attention_16_amd.build` "
+        "(hipcc, gfx950) before importing sparse_attention_16_amd")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE = range(4)
+
+EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_fwd",
+           "dsa_decode_fwd", "dsa_workspace_size", "dsa_status_string", "dsa_version")
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class dsa_batch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("total_q", ctypes.c_int32),
+                ("max_q", ctypes.c_int32), ("max_kv", ctypes.c_int32),
+                ("total_kv", ctypes.c_int64), ("cu_q", ctypes.c_void_p),
+                ("cu_kv", ctypes.c_void_p), ("pos0", ctypes.c_void_p)]
+
+
+class dsa_fwd_args(ctypes.Structure):
+    _fields_ = [("batch", dsa_batch), ("q_fp8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
+                ("w", ctypes.c_void_p), ("k_fp8", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p),
+                ("HI", ctypes.c_int32), ("DI", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("Dv", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+_P, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_BP = ctypes.POINTER(dsa_batch)
+_lib.dsa_indexer_scores.argtypes = [_BP, _P, _P, _P, _P, _P, _I, _I, _P, _I64, _P]
+_lib.dsa_topk.argtypes = [_BP, _P, _I64, _I, _P, _P, _SZ, _P]
+_lib.dsa_sparse_mla_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
+_lib.dsa_prefill_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
+_lib.dsa_decode_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
+_lib.dsa_workspace_size.argtypes = [_I, _BP, _I, _I, _I]
+_lib.dsa_workspace_size.restype = _SZ
+_lib.dsa_status_string.argtypes = [_I]
+_lib.dsa_status_string.restype = ctypes.c_char_p
+_lib.dsa_version.restype = ctypes.c_char_p
+for _name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_fwd",
+              "dsa_decode_fwd"):
+    getattr(_lib, _name).restype = ctypes.c_int
+
+
+def status_string(status: int) -> str:
+    return _lib.dsa_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return _lib.dsa_version().decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, what: str):
+    if status != DSA_OK:
+        raise DsaError(status, what)
+
+
+class Batch:
+    """Device-side ragged batch descriptor (cu_q, cu_kv, pos0 on the GPU) plus
+    the host scalars the C ABI wants.  Build from host arrays with
+    ``Batch.from_host(cu_q, cu_kv, pos0, device)``."""
+
+    def __init__(self, cu_q, cu_kv, pos0, total_q, max_q, total_kv, max_kv):
+        self.cu_q, self.cu_kv, self.pos0 = cu_q, cu_kv, pos0
+        self.B = int(pos0.numel())
+        self.total_q, self.max_q = int(total_q), int(max_q)
+        self.total_kv, self.max_kv = int(total_kv), int(max_kv)
+        self.c = dsa_batch(self.B, self.total_q, self.max_q, self.max_kv, self.total_kv,
+                           _ptr(cu_q), _ptr(cu_kv), _ptr(pos0))
+
+    @staticmethod
+    def from_host(cu_q, cu_kv, pos0, device="cuda"):
+        import numpy as np
+        cu_q = np.asarray(cu_q, np.int32)
+        cu_kv = np.asarray(cu_kv, np.int64)
+        pos0 = np.asarray(pos0, np.int32)
+        nq = cu_q[1:] - cu_q[:-1]
+        nkv = cu_kv[1:] - cu_kv[:-1]
+        return Batch(torch.from_numpy(cu_q).to(device), torch.from_numpy(cu_kv).to(device),
+                     torch.from_numpy(pos0).to(device), cu_q[-1], nq.max() if len(nq) else 0,
+                     cu_kv[-1], nkv.max() if len(nkv) else 0)
+
+
+def workspace_size(entry: int, batch: Batch, k: int, H: int = 128, Dv: int = 512) -> int:
+    return int(_lib.dsa_workspace_size(int(entry), ctypes.byref(batch.c), int(k), int(H), int(Dv)))
+
+
+def _workspace(entry, batch, k, ws, device):
+    need = workspace_size(entry, batch, k)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, (ws.numel() * ws.element_size() if ws is not None else 0)
+
+
+def indexer_scores(batch: Batch, q_fp8, q_scale, w, k_fp8, k_scale, scores, ld=None, stream=None):
+    """Index scores into ``scores`` [T, ld] fp32 (see dsa_indexer_scores)."""
+    ld = scores.shape[1] if ld is None else ld
+    st = _lib.dsa_indexer_scores(ctypes.byref(batch.c), _ptr(q_fp8), _ptr(q_scale), _ptr(w),
+                                 _ptr(k_fp8), _ptr(k_scale), q_fp8.shape[1], q_fp8.shape[2],
+                                 _ptr(scores), int(ld), _stream(stream))
+    _check(st, "dsa_indexer_scores")
+    return scores
+
+
+def topk(batch: Batch, scores, k: int, idx, ld=None, ws=None, stream=None):
+    """Top-k columns per row into ``idx`` [T, k] int32 (see dsa_topk)."""
+    ld = scores.shape[1] if ld is None else ld
+    ws, nbytes = _workspace(WS_TOPK, batch, k, ws, scores.device)
+    st = _lib.dsa_topk(ctypes.byref(batch.c), _ptr(scores), int(ld), int(k), _ptr(idx), _ptr(ws),
+                       nbytes, _stream(stream))
+    _check(st, "dsa_topk")
+    return idx
+
+
+def sparse_mla_fwd(batch: Batch, q, kv, idx, scale: float, out, lse, Dv: int = 512, ws=None,
+                   stream=None):
+    """Sparse MQA-mode attention over idx rows (see dsa_sparse_mla_fwd)."""
+    k = idx.shape[1]
+    ws, nbytes = _workspace(WS_SPARSE_MLA, batch, k, ws, q.device)
+    st = _lib.dsa_sparse_mla_fwd(ctypes.byref(batch.c), _ptr(q), _ptr(kv), _ptr(idx), int(k),
+                                 q.shape[1], q.shape[2], int(Dv), float(scale), _ptr(out), _ptr(lse),
+                                 _ptr(ws), nbytes, _stream(stream))
+    _check(st, "dsa_sparse_mla_fwd")
+    return out, lse
+
+
+def fwd_args(batch: Batch, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, k: int, scale: float,
+             Dv: int = 512) -> dsa_fwd_args:
+    return dsa_fwd_args(batch.c, _ptr(q_fp8), _ptr(q_scale), _ptr(w), _ptr(k_fp8), _ptr(k_scale),
+                        _ptr(q), _ptr(kv), q_fp8.shape[1], q_fp8.shape[2], q.shape[1], q.shape[2],
+                        int(Dv), int(k), float(scale))
+
+
+def _fwd(fn, entry, what, args: dsa_fwd_args, batch: Batch, out, lse, idx_out, ws, stream):
+    ws, nbytes = _workspace(entry, batch, args.k, ws, out.device)
+    st = fn(ctypes.byref(args), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), nbytes,
+            _stream(stream))
+    _check(st, what)
+    return out, lse
+
+
+def prefill_fwd(args: dsa_fwd_args, batch: Batch, out, lse, idx_out=None, ws=None, stream=None):
+    """Whole hot path (indexer -> top-k -> sparse MLA), prefill-tuned."""
+    return _fwd(_lib.dsa_prefill_fwd, WS_PREFILL, "dsa_prefill_fwd", args, batch, out, lse,
+                idx_out, ws, stream)
+
+
+def decode_fwd(args: dsa_fwd_args, batch: Batch, out, lse, idx_out=None, ws=None, stream=None):
+    """Whole hot path (indexer -> top-k -> sparse MLA), decode-tuned (split-KV)."""
+    return _fwd(_lib.dsa_decode_fwd, WS_DECODE, "dsa_decode_fwd", args, batch, out, lse,
+                idx_out, ws, stream)
+
+
+def raw_lib():
+    """The loaded ctypes library (for symbol checks and direct C-ABI calls)."""
+    return _lib

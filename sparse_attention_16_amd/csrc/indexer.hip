@@ -1,0 +1,260 @@
+// indexer.hip — lightning-indexer scores on gfx950 matrix cores.
+//
+// Computes, for every visible (query row t, key s) pair,
+//   I[t,s] = k_scale[s] * sum_j (w[t,j] * q_scale[t,j]) * max(0, sum_d q[t,j,d] k[s,d])
+// which is the index score of the page "Техотчёт DeepSeek-V3.2 (2025):
+// разреженное внимание DSA и масштабирование RL", section "Молниеносный
+// индексатор" (the I_{t,s} equation), evaluated on FP8 inputs as that section
+// prescribes.  Folding both dequantisation scales outside the ReLU is exact in
+// real arithmetic because the scales are positive.
+//
+// Mapping onto the 16x16x128 FP8 MFMA: the contraction dim (128) is one
+// instruction; A = 16 indexer heads of one query row (held in registers for
+// the whole kernel), B = 16 keys.  The C tile holds 4 heads per lane for one
+// key column, so the ReLU and the weighted head sum run in registers (16
+// terms per lane per row) followed by a two-step cross-lane add over the four
+// 16-lane groups.  Only the final fp32 score leaves the registers.
+#include "dsa_device.h"
+#include "kernels.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int HI = 64;
+constexpr int DI = 128;
+constexpr int ROW_BYTES = HI * DI;  // one query row of FP8 indexer queries
+
+// Loads the A operands (4 head groups) and folded weights of one query row.
+__device__ __forceinline__ void load_query(const IndexerParams &p, int64_t t, bool valid,
+                                           i32x8 (&qa)[4], float (&wq)[4][4]) {
+    const int l = lane_id();
+    const int row = l & 15, grp = l >> 4;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        if (valid) {
+            const uint8_t *src = p.q + t * ROW_BYTES + (16 * m + row) * DI + 32 * grp;
+            const i32x4 *s4 = reinterpret_cast<const i32x4 *>(src);
+            i32x4 lo = s4[0], hi = s4[1];
+            qa[m] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+            qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = 16 * m + 4 * grp + i;
+            wq[m][i] = valid ? p.w[t * HI + j] * p.q_scale[t * HI + j] : 0.0f;
+        }
+    }
+}
+
+// ReLU + weighted head sum of one 16-key column block, reduced over the four
+// lane groups; every lane returns the sum for key column (lane % 16).
+__device__ __forceinline__ float score_block(const i32x8 (&qa)[4], const float (&wq)[4][4],
+                                             const i32x8 &kb) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    float part = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        f32x4 c = mfma_f8_16x16x128(qa[m], kb, zero);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = fmaf(wq[m][i], fmaxf(c[i], 0.f), part);
+    }
+    part += shfl_xor_f(part, 16);
+    part += shfl_xor_f(part, 32);
+    return part;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Prefill variant: one workgroup = 16 consecutive query rows of one sequence
+// (8 waves x 2 rows) x one chunk of keys.  Key tiles of 128 rows are staged
+// once per workgroup in LDS (row pitch 144 B so that the 16 rows read by one
+// B operand land on disjoint banks) and shared by all 16 query rows.
+// Grid: x = row block, y = key chunk, z = sequence.
+// ---------------------------------------------------------------------------
+constexpr int PF_ROWS = 16;
+constexpr int PF_KT = 128;
+constexpr int PF_PITCH = 144;
+
+__global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[PF_KT * PF_PITCH];
+    __shared__ float kscale[PF_KT];
+
+    const int b = blockIdx.z;
+    const int q0 = p.cu_q[b];
+    const int nq = p.cu_q[b + 1] - q0;
+    const int tb = blockIdx.x * PF_ROWS;
+    if (tb >= nq) return;
+    int64_t kv0 = p.cu_kv[b], kv1 = p.cu_kv[b + 1];
+    kv0 = kv0 < 0 ? 0 : (kv0 > p.total_kv ? p.total_kv : kv0);
+    kv1 = kv1 < kv0 ? kv0 : (kv1 > p.total_kv ? p.total_kv : kv1);
+    const int ctx = (int)((kv1 - kv0) > p.max_kv ? p.max_kv : (kv1 - kv0));
+    const int last = (tb + PF_ROWS < nq ? tb + PF_ROWS : nq) - 1;
+    int vis_max = p.pos0[b] + last + 1;
+    vis_max = vis_max < 0 ? 0 : (vis_max > ctx ? ctx : vis_max);
+
+    const int c0 = blockIdx.y * p.key_chunk;
+    const int c_end = c0 + p.key_chunk;
+    const int comp_end = c_end < vis_max ? c_end : vis_max;      // keys needing the MFMA
+    const int fill_end = p.fill_masked ? (c_end < ctx ? c_end : ctx) : comp_end;
+    if (c0 >= fill_end) return;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int l = lane_id();
+
+    // two query rows per wave
+    i32x8 qa[2][4];
+    float wq[2][4][4];
+    int pos[2];
+    bool valid[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int tl = tb + 2 * wave + r;
+        valid[r] = tl < nq;
+        pos[r] = p.pos0[b] + tl;
+        load_query(p, (int64_t)(q0 + tl), valid[r], qa[r], wq[r]);
+    }
+
+    // register staging of the next key tile: 1024 16-byte chunks over 512 threads
+    i32x4 stage[2];
+    float sstage = 0.f;
+    auto fetch = [&](int kbase) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int c = tid + 512 * r;
+            const int key = c >> 3, byte = (c & 7) * 16;
+            if (kbase + key < comp_end)
+                stage[r] = *reinterpret_cast<const i32x4 *>(p.k + (kv0 + kbase + key) * DI + byte);
+            else
+                stage[r] = i32x4{0, 0, 0, 0};
+        }
+        if (tid < PF_KT) sstage = (kbase + tid < comp_end) ? p.k_scale[kv0 + kbase + tid] : 0.f;
+    };
+
+    if (c0 < comp_end) fetch(c0);
+    for (int kbase = c0; kbase < comp_end; kbase += PF_KT) {
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int c = tid + 512 * r;
+            *reinterpret_cast<i32x4 *>(&ktile[(c >> 3) * PF_PITCH + (c & 7) * 16]) = stage[r];
+        }
+        if (tid < PF_KT) kscale[tid] = sstage;
+        __syncthreads();
+        if (kbase + PF_KT < comp_end) fetch(kbase + PF_KT);
+
+        const int nsub = (comp_end - kbase + 15) >> 4;  // 16-key column blocks with work
+        float keep[2] = {0.f, 0.f};
+        for (int st = 0; st < PF_KT / 16; ++st) {
+            if (st < nsub) {
+                const uint8_t *src = &ktile[(16 * st + (l & 15)) * PF_PITCH + 32 * (l >> 4)];
+                const i32x4 lo = *reinterpret_cast<const i32x4 *>(src);
+                const i32x4 hi = *reinterpret_cast<const i32x4 *>(src + 16);
+                const i32x8 kb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    if (valid[r]) {
+                        const float v = score_block(qa[r], wq[r], kb);
+                        if ((st & 3) == (l >> 4)) keep[r] = v;
+                    }
+                }
+            }
+            if ((st & 3) == 3) {
+                // lane l now holds the score of key kbase + 16*(st-3) + l
+                const int key = kbase + 16 * (st - 3) + l;
+                if (key < fill_end) {
+                    const float ks = key < comp_end ? kscale[16 * (st - 3) + l] : 0.f;
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        if (valid[r]) {
+                            const float v = key <= pos[r] && key < comp_end ? keep[r] * ks : -INFINITY;
+                            p.scores[(int64_t)(q0 + tb + 2 * wave + r) * p.ld + key] = v;
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // keys of this chunk that no row of the block can see: -inf when requested
+    const int fill_start = comp_end > c0 ? comp_end : c0;
+    if (fill_start < fill_end) {
+        for (int r = 0; r < PF_ROWS; ++r) {
+            const int tl = tb + r;
+            if (tl >= nq) break;
+            for (int s = fill_start + tid; s < fill_end; s += 512)
+                p.scores[(int64_t)(q0 + tl) * p.ld + s] = -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode variant: one workgroup = one query row x one chunk of keys; the 4
+// waves split the chunk and stream their keys straight from HBM into the B
+// operand registers (a key is used by a single query row, so staging it in
+// LDS would buy nothing).  Grid: x = query row, y = key chunk.
+// ---------------------------------------------------------------------------
+constexpr int DC_WAVES = 4;
+
+__global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
+    const int t = blockIdx.x;
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    const int c0 = blockIdx.y * p.key_chunk;
+    const int c_end = c0 + p.key_chunk;
+    const int comp_end = c_end < ri.nvis ? c_end : ri.nvis;
+    const int fill_end = p.fill_masked ? (c_end < ri.ctx ? c_end : ri.ctx) : comp_end;
+    if (c0 >= fill_end) return;
+
+    const int wave = threadIdx.x >> 6;
+    const int l = lane_id();
+    i32x8 qa[4];
+    float wq[4][4];
+    load_query(p, t, true, qa, wq);
+
+    // each wave owns 64-key groups wave, wave + 4, ... of the chunk
+    const int row = l & 15, grp = l >> 4;
+    for (int g0 = c0 + 64 * wave; g0 < fill_end; g0 += 64 * DC_WAVES) {
+        i32x8 kb[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int key = g0 + 16 * st + row;
+            if (key < comp_end) {
+                const i32x4 *s4 = reinterpret_cast<const i32x4 *>(p.k + (ri.kv0 + key) * DI + 32 * grp);
+                const i32x4 lo = s4[0], hi = s4[1];
+                kb[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                kb[st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+        const int key = g0 + l;
+        const float ks = key < comp_end ? p.k_scale[ri.kv0 + key] : 0.f;
+        float keep = 0.f;
+        if (g0 < comp_end) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const float v = score_block(qa, wq, kb[st]);
+                if (st == grp) keep = v;
+            }
+        }
+        if (key < fill_end)
+            p.scores[(int64_t)t * p.ld + key] = key < comp_end ? keep * ks : -INFINITY;
+    }
+}
+
+hipError_t launch_indexer(const IndexerParams &p, int T, int max_q, bool decode_variant,
+                          hipStream_t s) {
+    if (T <= 0 || p.max_kv <= 0) return hipSuccess;
+    const int nchunk = (p.max_kv + p.key_chunk - 1) / p.key_chunk;
+    if (decode_variant) {
+        hipLaunchKernelGGL(indexer_decode_kernel, dim3(T, nchunk), dim3(64 * DC_WAVES), 0, s, p);
+    } else {
+        const dim3 g((max_q + PF_ROWS - 1) / PF_ROWS, nchunk, p.B);
+        hipLaunchKernelGGL(indexer_prefill_kernel, g, dim3(512), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,73 @@
+// kernels.h — launch parameters of the gfx950 kernels and their host-side
+// launchers (one per kernel family).  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct IndexerParams {
+    const int32_t *cu_q;
+    const int64_t *cu_kv;
+    const int32_t *pos0;
+    int B;
+    int64_t total_kv;
+    int max_kv;
+    const uint8_t *q;       // [T, 64, 128] e4m3
+    const float *q_scale;   // [T, 64]
+    const float *w;         // [T, 64]
+    const uint8_t *k;       // [N, 128] e4m3
+    const float *k_scale;   // [N]
+    float *scores;          // [T, ld]
+    int64_t ld;
+    int key_chunk;          // keys per workgroup
+    int fill_masked;        // write -inf for s in [nvis, ctx)
+};
+
+struct TopkParams {
+    const int32_t *cu_q;
+    const int64_t *cu_kv;
+    const int32_t *pos0;
+    int B;
+    int64_t total_kv;
+    int max_kv;
+    const float *scores;    // [T, ld]
+    int64_t ld;
+    int k;
+    int32_t *idx;           // [T, k]
+    uint32_t *cand_key;     // [T, nchunk, k] workspace (rows longer than one chunk)
+    int32_t *cand_pos;      // [T, nchunk, k]
+    int nchunk;             // chunks per row = ceil(max_kv / TOPK_CHUNK)
+};
+
+struct MlaParams {
+    const int32_t *cu_q;
+    const int64_t *cu_kv;
+    const int32_t *pos0;
+    int B;
+    int64_t total_kv;
+    int max_kv;
+    const uint16_t *q;      // [T, 128, 576] bf16
+    const uint16_t *kv;     // [N, 576] bf16
+    const int32_t *idx;     // [T, k]
+    int k;
+    float scale_log2;       // softmax scale * log2(e)
+    uint16_t *out;          // [T, 128, 512] bf16
+    float *lse;             // [T, 128]
+    int splits;             // workgroups per query row (split-KV)
+    int blocks_per_split;   // 64-key blocks per split
+    float *o_part;          // [T, splits, 128, 512] (splits > 1)
+    float *lse_part;        // [T, splits, 128]
+};
+
+constexpr int TOPK_CHUNK = 32768;     // columns selected per workgroup in LDS
+constexpr int TOPK_MAX_CHUNKS = 8;    // merge capacity: 8 x 2048 candidates
+constexpr int MLA_BK = 32;            // keys per gathered block
+
+hipError_t launch_indexer(const IndexerParams &p, int T, int max_q, bool decode_variant,
+                          hipStream_t s);
+hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s);
+hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s);
+
+}  // namespace dsa

@@ -1,0 +1,111 @@
+"""Helpers shared by the GPU parity tests: device upload of synth inputs, the
+parity tolerances, and index-set comparison modulo near-ties.
+
+Tolerances (per the hot path's parity bar):
+  * index scores: |I_gpu - I_ref| <= 1e-3 * max(|I_ref|, A_ref), where A is the
+    sum of absolute head terms (signed head weights can make I cancel);
+  * top-k sets: identical, except at positions whose reference score lies within
+    1e-3 * max(|I_kth|, A_kth) of the k-th selected reference score;
+  * attention: |out_gpu - o_ref| <= 2e-2 + 1e-2 * |o_ref| (bf16 output) and
+    |lse_gpu - lse_ref| <= 1e-3.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+SCORE_RTOL = 1e-3
+TIE_RTOL = 1e-3
+OUT_ATOL, OUT_RTOL = 2e-2, 1e-2
+LSE_ATOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x: np.ndarray, device="cuda"):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+class DevInputs:
+    def __init__(self, inp, dsa, device="cuda"):
+        b = inp.batch
+        self.inp = inp
+        self.batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0, device)
+        self.qi = dev(inp.qi)
+        self.qs = dev(inp.qi_scale)
+        self.w = dev(inp.w)
+        self.ki = dev(inp.ki)
+        self.ks = dev(inp.ki_scale)
+        self.q = dev(inp.q)
+        self.kv = dev(inp.kv)
+
+
+def bf16_to_f32(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.bfloat16).float().cpu().numpy()
+
+
+def check_scores(gpu: np.ndarray, ref: np.ndarray, A: np.ndarray, nvis: np.ndarray, what=""):
+    """gpu/ref/A: [rows, ld]; columns < nvis compared with the score tolerance."""
+    worst = 0.0
+    for r in range(ref.shape[0]):
+        n = int(nvis[r])
+        g, e, a = gpu[r, :n].astype(np.float64), ref[r, :n].astype(np.float64), A[r, :n]
+        assert np.all(np.isfinite(g)), f"{what} row {r}: non-finite visible score"
+        scale = np.maximum(np.abs(e), a)
+        err = np.abs(g - e)
+        bad = err > SCORE_RTOL * scale + 1e-30
+        assert not np.any(bad), (f"{what} row {r}: {bad.sum()} scores out of tolerance, "
+                                 f"worst rel {np.max(err / np.maximum(scale, 1e-30)):.3g}")
+        if n:
+            worst = max(worst, float(np.max(err / np.maximum(scale, 1e-30))))
+    return worst
+
+
+def check_idx_sets(gpu_idx: np.ndarray, ref_idx: np.ndarray, ref_scores: np.ndarray,
+                   A: np.ndarray, nvis: np.ndarray, k: int, what=""):
+    """Sets equal except near-ties of the k-th reference score.  Returns the
+    list of rows whose sets differ (all differences excused)."""
+    differ = []
+    for r in range(ref_idx.shape[0]):
+        n = int(nvis[r])
+        m = min(n, k)
+        g = gpu_idx[r]
+        assert np.all(g[m:] == -1), f"{what} row {r}: padding"
+        gs = g[:m]
+        assert np.all((gs >= 0) & (gs < n)), f"{what} row {r}: index out of range"
+        assert np.all(np.diff(gs) > 0), f"{what} row {r}: not ascending / duplicate"
+        rs = ref_idx[r, :m]
+        if np.array_equal(gs, rs):
+            continue
+        sr = ref_scores[r]
+        kth = rs[np.argmin(sr[rs])]  # lowest selected reference score
+        band = TIE_RTOL * max(abs(float(sr[kth])), float(A[r, kth]))
+        diff = np.setxor1d(gs, rs)
+        far = diff[np.abs(sr[diff].astype(np.float64) - float(sr[kth])) > band]
+        assert far.size == 0, (f"{what} row {r}: {far.size} differing positions outside the "
+                               f"near-tie band, e.g. {far[:5]}")
+        differ.append(r)
+    return differ
+
+
+def check_attention(out_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray,
+                    lse_ref: np.ndarray, what=""):
+    """out_gpu [rows, H, Dv] float (from bf16), lse_gpu [rows, H]."""
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse_gpu), fin), f"{what}: empty-row mismatch"
+    dl = np.abs(lse_gpu[fin] - lse_ref[fin])
+    assert np.all(dl <= LSE_ATOL), f"{what}: lse error {dl.max():.3g}"
+    err = np.abs(out_gpu - o_ref)
+    bad = err > OUT_ATOL + OUT_RTOL * np.abs(o_ref)
+    assert not np.any(bad), f"{what}: {bad.sum()} outputs out of tolerance, worst {err.max():.3g}"
+    assert np.all(out_gpu[~fin] == 0), f"{what}: empty rows must be zero"
+    num = np.linalg.norm((out_gpu - o_ref).reshape(out_gpu.shape[0], -1), axis=1)
+    den = np.maximum(np.linalg.norm(o_ref.reshape(o_ref.shape[0], -1), axis=1), 1e-30)
+    return float(dl.max()) if dl.size else 0.0, float(np.max(num / den))

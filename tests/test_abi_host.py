@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (include/dsa.h): the library loads, exports
+every declared entry point, sizes workspaces, and rejects bad arguments with
+the documented status before launching anything.  No GPU is touched: every
+call here returns from host validation (fake, aligned pointer values are never
+dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "sparse_attention_16_amd", "libdsa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdsa.so not built")
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_16_amd as m
+    return m
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(dsa):
+    syms = _declared_symbols()
+    assert set(syms) == set(dsa.EXPORTS)
+    lib = dsa.raw_lib()
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings_and_version(dsa):
+    assert dsa.status_string(0) == "ok"
+    assert "unsupported" in dsa.status_string(2)
+    assert "workspace" in dsa.status_string(3)
+    assert "gfx950" in dsa.version()
+
+
+FAKE = 1 << 20  # aligned, never dereferenced
+
+
+def _batch(dsa, T=4096, N=4096, B=1, max_q=None, max_kv=None):
+    return dsa.dsa_batch(B, T, T if max_q is None else max_q, N if max_kv is None else max_kv, N,
+                         FAKE, FAKE, FAKE)
+
+
+def test_workspace_sizes(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa, 4096, 4096)
+    # one chunk of top-k: no workspace; 4096 rows: no split-KV
+    assert lib.dsa_workspace_size(dsa.WS_TOPK, ctypes.byref(b), 2048, 128, 512) == 0
+    assert lib.dsa_workspace_size(dsa.WS_SPARSE_MLA, ctypes.byref(b), 2048, 128, 512) == 0
+    pre = lib.dsa_workspace_size(dsa.WS_PREFILL, ctypes.byref(b), 2048, 128, 512)
+    assert pre >= 4096 * 4096 * 4 + 4096 * 2048 * 4
+    # decode-like: 64 rows over 131072-long rows -> chunked top-k and split-KV
+    d = _batch(dsa, 64, 64 * 131072, B=64, max_q=1, max_kv=131072)
+    assert lib.dsa_workspace_size(dsa.WS_TOPK, ctypes.byref(d), 2048, 128, 512) >= 64 * 4 * 2048 * 8
+    assert lib.dsa_workspace_size(dsa.WS_SPARSE_MLA, ctypes.byref(d), 2048, 128, 512) > 0
+    # invalid arguments -> 0
+    assert lib.dsa_workspace_size(dsa.WS_PREFILL, ctypes.byref(b), 0, 128, 512) == 0
+    assert lib.dsa_workspace_size(dsa.WS_PREFILL, ctypes.byref(b), 2048, 64, 512) == 0
+    assert lib.dsa_workspace_size(dsa.WS_PREFILL, None, 2048, 128, 512) == 0
+
+
+def test_indexer_validation(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa)
+    args = [FAKE] * 5
+    assert lib.dsa_indexer_scores(None, *args, 64, 128, FAKE, 4096, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_scores(ctypes.byref(b), *args, 32, 128, FAKE, 4096, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_indexer_scores(ctypes.byref(b), *args, 64, 64, FAKE, 4096, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_indexer_scores(ctypes.byref(b), None, *args[1:], 64, 128, FAKE, 4096, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_scores(ctypes.byref(b), *args, 64, 128, FAKE, 4095, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_scores(ctypes.byref(b), FAKE + 4, *args[1:], 64, 128, FAKE, 4096, None) == dsa.DSA_ERR_INVALID_ARG
+    bad = _batch(dsa, B=0)
+    assert lib.dsa_indexer_scores(ctypes.byref(bad), *args, 64, 128, FAKE, 4096, None) == dsa.DSA_ERR_INVALID_ARG
+    bad = dsa.dsa_batch(1, 10, 10, 10, 10, None, FAKE, FAKE)
+    assert lib.dsa_indexer_scores(ctypes.byref(bad), *args, 64, 128, FAKE, 4096, None) == dsa.DSA_ERR_INVALID_ARG
+    empty = _batch(dsa, T=0, max_q=0)
+    assert lib.dsa_indexer_scores(ctypes.byref(empty), *args, 64, 128, FAKE, 4096, None) == dsa.DSA_OK
+
+
+def test_topk_validation(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa)
+    assert lib.dsa_topk(ctypes.byref(b), FAKE, 4096, 0, FAKE, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk(ctypes.byref(b), FAKE, 4096, 2049, FAKE, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk(ctypes.byref(b), None, 4096, 2048, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(ctypes.byref(b), FAKE, 100, 2048, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    long = _batch(dsa, T=8, N=8 * 131072, B=8, max_q=1, max_kv=131072)
+    assert lib.dsa_topk(ctypes.byref(long), FAKE, 131072, 2048, FAKE, None, 0, None) == dsa.DSA_ERR_WORKSPACE
+    need = lib.dsa_workspace_size(dsa.WS_TOPK, ctypes.byref(long), 2048, 128, 512)
+    assert lib.dsa_topk(ctypes.byref(long), FAKE, 131072, 2048, FAKE, FAKE, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+    huge = _batch(dsa, T=1, N=300000, B=1, max_q=1, max_kv=300000)
+    assert lib.dsa_topk(ctypes.byref(huge), FAKE, 300000, 2048, FAKE, FAKE, 1 << 40, None) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_sparse_mla_validation(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa)
+    ok = dict(H=128, D=576, Dv=512)
+
+    def call(q=FAKE, kv=FAKE, idx=FAKE, k=2048, H=128, D=576, Dv=512, scale=0.04, out=FAKE,
+             lse=FAKE, ws=None, nbytes=0, batch=b):
+        return lib.dsa_sparse_mla_fwd(ctypes.byref(batch), q, kv, idx, k, H, D, Dv, scale, out,
+                                      lse, ws, nbytes, None)
+
+    assert call(H=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(D=512) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(Dv=576) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(q=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(out=FAKE + 2) == dsa.DSA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == dsa.DSA_ERR_INVALID_ARG
+    dec = _batch(dsa, T=64, N=64 * 20000, B=64, max_q=1, max_kv=20000)
+    assert call(batch=dec) == dsa.DSA_ERR_WORKSPACE
+    assert ok
+
+
+def test_fused_validation(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa)
+    a = dsa.dsa_fwd_args(b, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 128, 576, 512, 2048, 0.04)
+    for fn in (lib.dsa_prefill_fwd, lib.dsa_decode_fwd):
+        assert fn(None, FAKE, FAKE, None, FAKE, 1 << 40, None) == dsa.DSA_ERR_INVALID_ARG
+        assert fn(ctypes.byref(a), FAKE, FAKE, None, None, 0, None) == dsa.DSA_ERR_WORKSPACE
+        need = lib.dsa_workspace_size(dsa.WS_PREFILL, ctypes.byref(b), 2048, 128, 512)
+        assert fn(ctypes.byref(a), FAKE, FAKE, None, FAKE, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+        bad = dsa.dsa_fwd_args(b, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 64, 576, 512, 2048, 0.04)
+        assert fn(ctypes.byref(bad), FAKE, FAKE, None, FAKE, 1 << 40, None) == dsa.DSA_ERR_UNSUPPORTED
+        bad = dsa.dsa_fwd_args(b, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 128, 576, 512, 2048, 0.04)
+        assert fn(ctypes.byref(bad), FAKE, FAKE, None, FAKE, 1 << 40, None) == dsa.DSA_ERR_INVALID_ARG
+        assert fn(ctypes.byref(a), FAKE, FAKE, FAKE + 8, FAKE, 1 << 40, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_tiny_fp32_configuration_is_unsupported(dsa):
+    # the 4-head / 32-dim / 80-dim fp32 configuration is oracle-only
+    lib = dsa.raw_lib()
+    b = _batch(dsa, 256, 256)
+    a = dsa.dsa_fwd_args(b, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 8, 80, 64, 32, 80 ** -0.5)
+    assert lib.dsa_prefill_fwd(ctypes.byref(a), FAKE, FAKE, None, FAKE, 1 << 40, None) == dsa.DSA_ERR_UNSUPPORTED
