@@ -1,0 +1,250 @@
+"""DSA hot-path benchmark on one MI355X: indexer + top-2048 + sparse MQA MLA.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_32k]
+
+A step is one call of the fused C-ABI entry (dsa_prefill_fwd, or dsa_decode_fwd
+for the decode workload) over one batch of synthetic inputs already resident
+in HBM.  Prints one JSON line: tokens/s over the K timed steps, the roofline of
+the dominant kernel (timed with HIP events around its own launches, on the
+stream it runs on), and the CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+
+Workloads (synthetic, seeded; the shapes and distributions of the DSA
+configurations): prefill_32k (default), prefill_4k, decode_64k (64 sequences,
+contexts uniform in 16384..131072, one new token each), chunked_128k (4096 new
+tokens at the end of a 131072-entry context).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DSA tokens/s (indexer+top-2048+sparse MLA), 32K prefill & 64K-ctx decode"
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+HI, DI, H, D, DV = 64, 128, 128, 576, 512
+
+
+# ----------------------------------------------------------------- accounting
+
+def visible_counts(cu_q, cu_kv, pos0):
+    """Visible keys per query row: min(position + 1, context length)."""
+    cu_q, cu_kv, pos0 = np.asarray(cu_q), np.asarray(cu_kv), np.asarray(pos0)
+    out = []
+    for b in range(len(pos0)):
+        nq = int(cu_q[b + 1] - cu_q[b])
+        ctx = int(cu_kv[b + 1] - cu_kv[b])
+        pos = int(pos0[b]) + np.arange(nq, dtype=np.int64)
+        out.append(np.clip(np.minimum(pos + 1, ctx), 0, None))
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def indexer_flops(nvis):
+    """FP8 MFMA flops of the index score: 2*HI*DI per visible (query, key) pair."""
+    return 2.0 * HI * DI * float(np.sum(nvis))
+
+
+def mla_flops(nvis, k):
+    """bf16 MFMA flops of sparse MQA attention: per selected (query, key) pair,
+    H heads x (2*D for q.k + 2*Dv for p.v)."""
+    return float(np.sum(np.minimum(nvis, k))) * H * 2.0 * (D + DV)
+
+
+def dense_mla_flops(nvis):
+    return float(np.sum(nvis)) * H * 2.0 * (D + DV)
+
+
+def indexer_bytes(nvis, ctx_total, T):
+    """Algorithmic HBM bytes of the indexer: every cached key (128 code bytes +
+    4 scale bytes) and every query row (64x128 codes, 64 scales, 64 weights) read
+    once, one fp32 score written per visible pair."""
+    return ctx_total * (DI + 4) + T * (HI * DI + HI * 8) + 4.0 * float(np.sum(nvis))
+
+
+def mla_bytes(nvis, k, T):
+    """Algorithmic HBM bytes of sparse MLA if every selected 1152-byte latent row
+    came from HBM (the decode regime): gathered rows + q + out + idx + lse."""
+    return float(np.sum(np.minimum(nvis, k))) * D * 2 + T * (H * D * 2 + H * DV * 2 + k * 4 + H * 4)
+
+
+# ------------------------------------------------------------------ workloads
+
+def make_workload(name):
+    import synth
+    if name == "prefill_32k":
+        return synth.prefill(32768), "prefill"
+    if name == "prefill_4k":
+        return synth.prefill(4096), "prefill"
+    if name == "decode_64k":
+        return synth.decode(64), "decode"
+    if name == "chunked_128k":
+        return synth.chunked_prefill(4096, 131072), "prefill"
+    raise SystemExit(f"unknown workload {name}")
+
+
+def cpu_baseline(wl, target_s=15.0):
+    """Oracle (indexer -> top-k -> exact attention) on evenly spaced query rows,
+    sized to roughly `target_s` seconds of wall time on this host."""
+    import oracle
+    b = wl.batch
+    T = b.T
+
+    def run(rows):
+        inp = wl.sampled_host(rows)
+        t0 = time.perf_counter()
+        s = oracle.indexer(b.cu_q, b.cu_kv, b.pos0, inp.qi, inp.qi_scale, inp.w, inp.ki,
+                           inp.ki_scale, rows=rows)
+        idx = oracle.topk(b.cu_q, b.cu_kv, b.pos0, s, wl.k, rows=rows)
+        oracle.sparse_attn(b.cu_q, b.cu_kv, b.pos0, inp.q, inp.kv, idx, wl.Dv, wl.scale, rows=rows)
+        return time.perf_counter() - t0
+
+    threads = oracle.num_threads()
+    probe = np.unique(np.linspace(0, T - 1, min(T, max(threads, 8))).astype(np.int64))
+    dt = run(probe)
+    per_row = dt / len(probe)
+    n = int(min(T, max(len(probe), math.floor(target_s / max(per_row, 1e-6)))))
+    rows = np.unique(np.linspace(0, T - 1, n).astype(np.int64))
+    dt = run(rows)
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} query rows evenly spaced over all {T} rows of the same "
+                      f"workload (full indexer row, top-{wl.k}, exact attention per row), "
+                      f"{dt:.1f} s wall"}
+
+
+# ---------------------------------------------------------------------- bench
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_32k",
+                    choices=["prefill_32k", "prefill_4k", "decode_64k", "chunked_128k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--kernel-reps", type=int, default=5,
+                    help="timed launches of the dominant kernel")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(each MI355X box here has a single GPU).", file=sys.stderr)
+        return 2
+
+    import torch
+    import sparse_attention_16_amd as dsa
+
+    torch.cuda.set_device(0)
+    wl, entry = make_workload(args.workload)
+    b = wl.batch
+    say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+    say(f"[bench] workload {args.workload}: T={b.T} N={b.N} B={b.B} max_kv={b.max_kv}")
+    t0 = time.time()
+    dev = wl.device("cuda")
+    torch.cuda.synchronize()
+    say(f"[bench] inputs generated and resident in HBM ({time.time() - t0:.1f} s)")
+
+    batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0)
+    fargs = dsa.fwd_args(batch, dev["qi"], dev["qs"], dev["w"], dev["ki"], dev["ks"], dev["q"],
+                         dev["kv"], wl.k, wl.scale)
+    out = torch.empty((b.T, H, DV), dtype=torch.int16, device="cuda")
+    lse = torch.empty((b.T, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((b.T, wl.k), dtype=torch.int32, device="cuda")
+    ws_entry = dsa.WS_PREFILL if entry == "prefill" else dsa.WS_DECODE
+    ws = torch.empty(max(1, dsa.workspace_size(ws_entry, batch, wl.k)), dtype=torch.uint8,
+                     device="cuda")
+    fwd = dsa.prefill_fwd if entry == "prefill" else dsa.decode_fwd
+
+    def step():
+        fwd(fargs, batch, out, lse, idx, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = b.T * args.steps / elapsed
+    say(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, {tokens_per_s:,.0f} tokens/s")
+
+    # ---- dominant kernel, timed alone with HIP events on its stream
+    nvis = visible_counts(b.cu_q, b.cu_kv, b.pos0)
+    stream = torch.cuda.current_stream()
+    if entry == "prefill":
+        name = "sparse_mla_kernel"
+        flops = mla_flops(nvis, wl.k)
+        mws = torch.empty(max(1, dsa.workspace_size(dsa.WS_SPARSE_MLA, batch, wl.k)),
+                          dtype=torch.uint8, device="cuda")
+        out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+
+        def kernel():
+            dsa.sparse_mla_fwd(batch, dev["q"], dev["kv"], idx, wl.scale, out2, lse2, ws=mws)
+    else:
+        name = "indexer_decode_kernel"
+        ld = ((b.max_kv + 63) // 64) * 64
+        scores = torch.empty((b.T, ld), dtype=torch.float32, device="cuda")
+        nbytes = indexer_bytes(nvis, b.N, b.T)
+
+        def kernel():
+            dsa.indexer_scores(batch, dev["qi"], dev["qs"], dev["w"], dev["ki"], dev["ks"], scores)
+    kernel()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        kernel()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    if entry == "prefill":
+        achieved = flops / (kms * 1e-3) / 1e12
+        roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "avg_ms": round(kms, 4), "algorithmic_flops": flops}
+    else:
+        achieved = nbytes / (kms * 1e-3) / 1e9
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None, "avg_ms": round(kms, 4), "algorithmic_bytes": nbytes}
+    say(f"[bench] {name}: {kms:.3f} ms/launch, {roof['achieved']} {roof['unit']} "
+        f"({100 * roof['frac']:.1f}% of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        say("[bench] timing the CPU oracle on a sample of the workload ...")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        say(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
+
+    cfg = {"workload": args.workload, "batch": b.B, "query_tokens": b.T, "cache_rows": b.N,
+           "max_context": b.max_kv, "topk": wl.k, "indexer_heads": HI, "indexer_dim": DI,
+           "heads": H, "d_qk": D, "d_v": DV, "entry": f"dsa_{entry}_fwd"}
+    if args.workload == "decode_64k":
+        cfg["mean_context"] = round(float(np.mean(np.diff(b.cu_kv))), 1)
+    line = {"metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8+bf16", "data": "synthetic", "config": cfg, "roofline": roof,
+            "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

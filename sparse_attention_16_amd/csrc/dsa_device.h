@@ -52,6 +52,20 @@ __device__ __forceinline__ float xor16_f(float v) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
 }
 
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations (lgkmcnt 0) but not for outstanding global or direct-to-LDS loads
+// (vmcnt), so a gather in flight keeps flying across it.  The wavefront-scope
+// fences emit no wait; they only stop the compiler from moving LDS accesses
+// across the barrier.  (A workgroup-scope LDS fence would also wait for the
+// in-flight direct-to-LDS loads, and an asm memory clobber hides the LDS
+// buffers' alias scopes from the compiler's wait insertion.)
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // float -> bf16 bits, round to nearest even (inputs are finite here).
 __device__ __forceinline__ uint16_t f2bf(float f) {
     uint32_t u = __float_as_uint(f);

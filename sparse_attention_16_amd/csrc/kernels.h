@@ -56,7 +56,7 @@ struct MlaParams {
     uint16_t *out;          // [T, 128, 512] bf16
     float *lse;             // [T, 128]
     int splits;             // workgroups per query row (split-KV)
-    int blocks_per_split;   // 64-key blocks per split
+    int blocks_per_split;   // MLA_BK-key blocks per split
     float *o_part;          // [T, splits, 128, 512] (splits > 1)
     float *lse_part;        // [T, splits, 128]
 };

@@ -10,19 +10,29 @@
 //
 // One workgroup serves one query row (or one split of its selected set) for
 // all 128 heads, so every gathered 1152-byte latent row feeds 128 heads (the
-// MQA property that keeps the gather coalesced).  4 waves x 32 heads: each K
-// or V operand read from LDS feeds two 16-head MFMA tiles.
+// MQA property that keeps the gather coalesced).  4 waves x 32 heads, one
+// wave per SIMD: a wave's query operands (144 VGPRs) and O accumulators (256
+// AGPRs) stay in registers for the whole row, and every K or V operand read
+// from LDS feeds two 16-head MFMA tiles.
 //
-// Per 64-key block:
-//   gather  : 64 selected rows -> LDS with direct-to-LDS 16-byte loads
-//             (row pitch 1168 B), double-buffered so the next block's gather
-//             overlaps this block's math;
+// Per 32-key block:
+//   gather  : the 32 selected rows -> LDS with direct-to-LDS 16-byte loads
+//             into one of three buffers, two blocks ahead; dims 0..511 of a
+//             row are one 1 KB load (row index from a scalar load), the 64
+//             rope dims of 8 rows share one XOR-swizzled 1 KB slab;
 //   S^T     : z^T[key, head] = K Q^T on the 16x16x32 bf16 MFMA; A = K rows
-//             from LDS, B = this wave's 16 query heads (registers, loaded once);
-//   softmax : online (running max m and sum l per head), exp2 domain;
+//             from LDS, B = query heads (registers, loaded once);
+//   softmax : exp2 domain against a per-head reference max fixed at the
+//             first block with a usable key;
 //   PV      : O^T[c, head] += V^T P^T; B = P^T straight from the S^T
-//             accumulators (the C layout of S^T already puts one head per
-//             lane), A = V^T read with the LDS transpose load.
+//             accumulators (their C layout already puts one head per lane),
+//             A = V^T read with the LDS transpose load.
+// The loop never touches O except through MFMAs (no online rescale), which is
+// what lets O live in AGPRs.  Exactness: p = 2^(z - m_ref) is bounded by 2^64
+// as long as no later logit exceeds the reference by more than 64 (log2
+// units); a block that does sets a restart flag, and the row is recomputed
+// with the row's true maximum as the reference (tracked during the first
+// pass), which cannot overflow.
 // Split-KV (few query rows): each split writes a normalised partial and its
 // lse; mla_merge_kernel combines them.
 #include "dsa_device.h"
@@ -35,59 +45,82 @@ namespace {
 constexpr int H = 128;
 constexpr int D = 576;
 constexpr int DV = 512;
-constexpr int ROWB = D * 2;            // 1152 bytes per latent row
-constexpr int PITCH = ROWB + 16;       // LDS row pitch
-constexpr int BK = MLA_BK;             // 64 keys per block
-constexpr int BUF_BYTES = BK * PITCH;  // 74752
-constexpr int NWAVES = 8;
+constexpr int ROWB = D * 2;              // 1152 bytes per latent row
+constexpr int BK = MLA_BK;               // 32 keys per block
+constexpr int PA = 1056;                 // LDS pitch of the dims 0..511 part (1 KB + 32 B)
+constexpr int RB = BK * PA;              // start of the rope slabs (8 rows x 128 B each)
+constexpr int BUF_BYTES = RB + BK * 128; // 37888
+constexpr int NWAVES = 4;                // 4 head groups of 32 heads
 constexpr int NTHREADS = NWAVES * kWave;
-constexpr int HPW = H / NWAVES;        // heads per wave
-constexpr int NHT = HPW / 16;          // 16-head MFMA tiles per wave
-constexpr int LOADS_PER_BUF = (BUF_BYTES + 1023) / 1024;  // 1 KB per wave-wide load
-constexpr int KSTEPS = D / 32;         // 18
-constexpr int MT = BK / 16;            // 16-key tiles per block
-constexpr int KK = BK / 32;            // 32-key PV steps per block
-constexpr int CTILES = DV / 16;        // 32
+constexpr int NHT = 2;                   // 16-head MFMA tiles per wave
+constexpr int KSTEPS = D / 32;           // 18 k-steps (16 latent + 2 rope)
+constexpr int MT = BK / 16;              // 16-key tiles per block
+constexpr int CTILES = DV / 16;          // 32 value tiles
 constexpr float LN2 = 0.69314718055994530942f;
+constexpr float MAX_RISE = 64.f;         // log2 headroom above the reference max
+
+static_assert(BK == 32 && NWAVES * 8 == BK, "each wave loads 8 rows and one rope slab");
 
 typedef DSA_LDS uint8_t lds_u8;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
-// Issues the direct-to-LDS loads of one 64-key block.  Load slot j (16 B) of
-// the buffer maps to LDS byte 16*j = row*PITCH + col; columns >= 1152 are the
-// pitch padding and load a harmless in-bounds 16 bytes of the same row.
-__device__ __forceinline__ void gather_block(const MlaParams &p, const int32_t *sel, int nsel,
-                                             int blk, int64_t kv0, int ctx, lds_u8 *buf) {
-    const int wave = threadIdx.x >> 6, l = lane_id();
-    for (int li = wave; li < LOADS_PER_BUF; li += NWAVES) {
-        const int off = li * 1024 + l * 16;
-        int row = off / PITCH;
-        int col = off - row * PITCH;
-        if (row >= BK) {
-            row = BK - 1;
-            col = 0;
-        }
-        if (col >= ROWB) col = 0;
-        const int j = blk * BK + row;
-        int s = j < nsel ? sel[j] : -1;
-        if (s < 0 || s >= ctx) s = 0;   // masked later; any in-bounds row
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(p.kv) + (kv0 + s) * ROWB + col;
-        __builtin_amdgcn_global_load_lds(src, buf + li * 1024, 16, 0, 0);
+__device__ __forceinline__ int64_t clamp_row(int s, int ctx) {
+    return (s >= 0 && s < ctx) ? s : 0;   // unusable slots load row 0 (masked later)
+}
+
+// Issues the 9 direct-to-LDS loads of one block for this wave.  Wave w loads
+// rows 8w..8w+7 (dims 0..511: one 1 KB load per row) and their rope slab
+// (dims 512..575, 8 rows x 128 B): inside a slab, logical 16-byte chunk c of
+// row rr sits at chunk position c ^ rr, so that a column of 8 rows read
+// together lands on distinct banks.  Slot positions are read with scalar loads
+// (wave-uniform addresses), so they never wait behind the vector-memory
+// counter the direct-to-LDS loads use.
+__device__ __forceinline__ void gather_block(const uint16_t *kv, const int32_t *__restrict__ idx_row,
+                                             int nsel, int blk, int64_t kv0, int ctx, lds_u8 *buf,
+                                             int l) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int jw = blk * BK + 8 * wave;
+    int s8[8];
+    if (jw + 8 <= nsel) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s8[i] = idx_row[jw + i];
+    } else {   // last, partial block of the slice
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s8[i] = idx_row[jw + i < nsel ? jw + i : nsel - 1];
     }
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(kv) + kv0 * ROWB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 8 * wave + i;
+        const int64_t s = clamp_row(s8[i], ctx);
+        __builtin_amdgcn_global_load_lds(base + s * ROWB + 16 * l, buf + r * PA, 16, 0, 0);
+    }
+    const int rr = l >> 3;   // row inside the slab
+    int sr = s8[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) sr = rr == i ? s8[i] : sr;
+    const int64_t s = clamp_row(sr, ctx);
+    __builtin_amdgcn_global_load_lds(base + s * ROWB + 1024 + 16 * ((l & 7) ^ rr),
+                                     buf + RB + wave * 1024, 16, 0, 0);
 }
 
 }  // namespace
 
-// Grid: x = query row, y = split.  LDS: two gather buffers + the row's idx.
-__global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(MlaParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t buf0[LOADS_PER_BUF * 1024];
-    __shared__ __attribute__((aligned(1024))) uint8_t buf1[LOADS_PER_BUF * 1024];
-    __shared__ int32_t sel[2048];
+// Grid: x = query row, y = split.  LDS: three gather buffers + restart flags.
+// The index array and every output are separate restrict-qualified arguments
+// so the compiler can prove no store clobbers idx and read the slot positions
+// with scalar loads.
+__global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
+    MlaParams p, const int32_t *__restrict__ idx, uint16_t *__restrict__ out,
+    float *__restrict__ lse, float *__restrict__ o_part, float *__restrict__ lse_part) {
+    __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t buf2[BUF_BYTES];
+    __shared__ int restart_flag[NWAVES];
 
     const int t = blockIdx.x, split = blockIdx.y;
-    const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
+    const int wave = threadIdx.x >> 6, l = lane_id();
     const int row16 = l & 15, grp = l >> 4;
     const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
 
@@ -96,17 +129,11 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(MlaParams p) {
     int j1 = j0 + p.blocks_per_split * BK;
     j1 = j1 < p.k ? j1 : p.k;
     const int nsel = (j1 > j0 && ri.ctx > 0) ? j1 - j0 : 0;
-    const int32_t *idx_row = p.idx + (int64_t)t * p.k + j0;
-    for (int j = tid; j < nsel; j += NTHREADS) {
-        const int s = idx_row[j];
-        sel[j] = (s >= 0 && s < ri.ctx) ? s : -1;
-    }
-    __syncthreads();
+    const int32_t *__restrict__ idx_row = idx + (int64_t)t * p.k + j0;
     const int nblk = (nsel + BK - 1) / BK;
 
-    // query operands of this wave's 2 x 16 heads: lane holds head
-    // h0 + 16*ht + row16, dims 32*ks + 8*grp .. +7
-    const int h0 = wave * HPW;
+    // query operands: lane holds head h0 + 16*ht + row16, dims 32*ks + 8*grp .. +7
+    const int h0 = wave * 32;
     bf16x8 qb[NHT][KSTEPS];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
@@ -115,140 +142,188 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(MlaParams p) {
         for (int ks = 0; ks < KSTEPS; ++ks)
             qb[ht][ks] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query operands resident before the pipeline
 
-    f32x4 o[NHT][CTILES];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-        for (int c = 0; c < CTILES; ++c) o[ht][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[NHT], l_run[NHT];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-        m_run[ht] = -INFINITY;
-        l_run[ht] = 0.f;
+    // validity masks: lane b holds bit i = slot b*BK + i is a usable row
+    // (inside the slice, inside [0, ctx)); read per block with readlane
+    uint32_t maskv = 0;
+    for (int it = 0; it * kWave < nsel; ++it) {
+        const int j = it * kWave + l;
+        const bool ok = j < nsel && (uint32_t)idx_row[j < nsel ? j : 0] < (uint32_t)ri.ctx;
+        const uint64_t m = __ballot(ok);
+        maskv = l == 2 * it ? (uint32_t)m : (l == 2 * it + 1 ? (uint32_t)(m >> 32) : maskv);
     }
+
+    // per-lane LDS read offsets (buffer-relative)
+    const int rr16 = row16 & 7;
+    const int kA = row16 * PA + 16 * grp;                              // K rows, dims < 512
+    const int kB = RB + (row16 >> 3) * 1024 + rr16 * 128;              // rope slab row
+    const int kB16 = kB + 16 * (grp ^ rr16);                           // dims 512 + 8*grp
+    const int kB17 = kB + 16 * ((4 + grp) ^ rr16);                     // dims 544 + 8*grp
+    const int vA = (4 * grp + (row16 >> 2)) * PA + 8 * (row16 & 3);    // V^T transpose reads
 
     lds_u8 *lb0 = (lds_u8 *)buf0;
     lds_u8 *lb1 = (lds_u8 *)buf1;
-    if (nblk > 0) gather_block(p, sel, nsel, 0, ri.kv0, ri.ctx, lb0);
+    lds_u8 *lb2 = (lds_u8 *)buf2;
 
-    // One block step; `cur` and `nxt` are distinct LDS arrays at compile time
-    // (the loop is unrolled by two), so the compiler can see that reads of
-    // `cur` do not depend on the direct-to-LDS loads still landing in `nxt`.
-    auto step = [&](int blk, lds_u8 *cur, lds_u8 *nxt) {
-        // block blk has landed in `cur` for every wave, and every wave is done
-        // reading `nxt` (block blk-1)
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __syncthreads();
-        if (blk + 1 < nblk) gather_block(p, sel, nsel, blk + 1, ri.kv0, ri.ctx, nxt);
+    f32x4 o[NHT][CTILES];
+    float m_run[NHT], l_run[NHT], m_seen[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) m_seen[ht] = -INFINITY;
 
-        // ---- S^T = K Q^T : MT key tiles of 16, lane = (head row16, keys 4*grp+i).
-        // The next k-step's operand of key tile mt is loaded right after the
-        // current one is consumed; the scheduling barrier keeps the compiler
-        // from hoisting more LDS reads (query operands and accumulators fill
-        // most of the register file).
-        f32x4 sacc[NHT][MT];
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sacc[ht][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        {
-            const lds_u8 *kbase = cur + row16 * PITCH + 16 * grp;
-            bf16x8 abuf[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                abuf[mt] = *reinterpret_cast<const DSA_LDS bf16x8 *>(kbase + 16 * mt * PITCH);
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const bf16x8 a = abuf[mt];
-                    if (ks + 1 < KSTEPS)
-                        abuf[mt] = *reinterpret_cast<const DSA_LDS bf16x8 *>(
-                            kbase + 16 * mt * PITCH + 64 * (ks + 1));
-#pragma unroll
-                    for (int ht = 0; ht < NHT; ++ht)
-                        sacc[ht][mt] = mfma_bf16_16x16x32(a, qb[ht][ks], sacc[ht][mt]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-
-        // ---- online softmax (log2 domain), per head tile.  The running max
-        // only moves when a block raises it by more than 8 (p stays <= 2^8),
-        // so the O rescale is rare after the first block; the result is the
-        // same softmax because l and O always share the max used for p.
-        const int jv = blk * BK + (l & (BK - 1));
-        const uint32_t vmask = (uint32_t)__ballot(jv < nsel && sel[jv] >= 0);
-        bf16x8 pb[NHT][KK];
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
-            float bmax = -INFINITY;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const uint32_t nib = (vmask >> (16 * mt + 4 * grp)) & 0xFu;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float z = ((nib >> i) & 1u) ? sacc[ht][mt][i] * p.scale_log2 : -INFINITY;
-                    sacc[ht][mt][i] = z;
-                    bmax = fmaxf(bmax, z);
-                }
-            }
-            bmax = fmaxf(bmax, xor16_f(bmax));
-            bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
-            const bool raise = bmax > m_run[ht] + 8.f;
-            if (__ballot(raise)) {
-                const float alpha = raise ? exp2f(m_run[ht] - bmax) : 1.f;
-                if (raise) m_run[ht] = bmax;
-                l_run[ht] *= alpha;
-#pragma unroll
-                for (int c = 0; c < CTILES; ++c) o[ht][c] *= alpha;
-            }
-            const float m_use = m_run[ht] == -INFINITY ? 0.f : m_run[ht];
-            float psum = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                float pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pv[e] = exp2f(sacc[ht][2 * kk + (e >> 2)][e & 3] - m_use);
-                    psum += pv[e];
-                }
-                u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-                pb[ht][kk] = __builtin_bit_cast(bf16x8, pk);
-            }
-            l_run[ht] += psum;
+            for (int c = 0; c < CTILES; ++c) o[ht][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_run[ht] = pass == 0 ? -INFINITY : m_seen[ht];
+            l_run[ht] = 0.f;
         }
+        bool restart = false;
 
-        // ---- O^T += V^T P^T : A = V^T via transpose reads, one c-tile ahead.
-        // 16-lane group grp reads rows (keys) 32*kk + 4*grp + r (+16 for the
-        // second half); lane (row16) of the group addresses row row16/4,
-        // columns 16*ct + 4*(row16%4) .. +3.
-        const int tr_row = row16 >> 2, tr_col = 4 * (row16 & 3);
+        // Pipeline: at the top of step b, vmcnt(9) leaves only this wave's 9
+        // loads of block b+1 in flight, so block b has landed.
+        if (nblk > 0) gather_block(p.kv, idx_row, nsel, 0, ri.kv0, ri.ctx, lb0, l);
+        if (nblk > 1) gather_block(p.kv, idx_row, nsel, 1, ri.kv0, ri.ctx, lb1, l);
+
+        // One block step: cur = buffer of block blk, nxt2 = buffer for blk+2
+        // (the one block blk-1 used).  `cur` and `nxt2` are distinct LDS arrays
+        // at compile time (the loop is unrolled by three), which lets the
+        // compiler see that reads of `cur` do not wait for the loads landing
+        // elsewhere.
+        auto step = [&](int blk, lds_u8 *cur, lds_u8 *nxt2) {
+            if (blk + 1 < nblk)
+                __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+            else
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            // LDS-only barrier: every wave's part of block blk has landed and
+            // every wave is done reading block blk-1's buffer
+            lds_barrier();
+            // Lane-derived values are rebuilt inside the step from an opaque
+            // zero (blk >> 30 == 0 for every real block count): hoisted out of
+            // the loop they would cost registers the operands need.
+            const int z = blk >> 30;
+            const int lz = lane_id() + z;
+            if (blk + 2 < nblk) gather_block(p.kv, idx_row, nsel, blk + 2, ri.kv0, ri.ctx, nxt2, lz);
+            const uint32_t vmask = __builtin_amdgcn_readlane(maskv, blk);
+
+            // ---- S^T: MT key tiles x NHT head tiles, lane = (head row16, keys 4*grp+i)
+            f32x4 sacc[NHT][MT];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const lds_u8 *r0 = cur + (32 * kk + 4 * grp + tr_row) * PITCH + 2 * tr_col;
-            const lds_u8 *r1 = r0 + 16 * PITCH;
-            i16x4 vlo = lds_read_tr16(r0), vhi = lds_read_tr16(r1);
+            for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-            for (int ct = 0; ct < CTILES; ++ct) {
-                const i16x8 a8 = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
-                if (ct + 1 < CTILES) {
-                    vlo = lds_read_tr16(r0 + 32 * (ct + 1));
-                    vhi = lds_read_tr16(r1 + 32 * (ct + 1));
+                for (int mt = 0; mt < MT; ++mt) sacc[ht][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // K operands are loaded QK_AHEAD k-steps ahead of their MFMAs
+            // (software pipeline; one wave per SIMD hides nothing by itself).
+            constexpr int QK_AHEAD = 2;
+            const int kAz = kA + z, kB16z = kB16 + z, kB17z = kB17 + z;
+            auto k_off = [&](int ks, int mt) {
+                return ks < 16 ? kAz + 64 * ks + mt * 16 * PA
+                               : (ks == 16 ? kB16z : kB17z) + mt * 2048;
+            };
+            bf16x8 kbuf[QK_AHEAD + 1][MT];
+#pragma unroll
+            for (int ks = 0; ks < QK_AHEAD; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    kbuf[ks][mt] = *reinterpret_cast<const DSA_LDS bf16x8 *>(cur + k_off(ks, mt));
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                if (ks + QK_AHEAD < KSTEPS) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        kbuf[(ks + QK_AHEAD) % (QK_AHEAD + 1)][mt] = *reinterpret_cast<const DSA_LDS bf16x8 *>(
+                            cur + k_off(ks + QK_AHEAD, mt));
                 }
-                const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
 #pragma unroll
-                for (int ht = 0; ht < NHT; ++ht)
-                    o[ht][ct] = mfma_bf16_16x16x32(a, pb[ht][kk], o[ht][ct]);
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int ht = 0; ht < NHT; ++ht)
+                        sacc[ht][mt] = mfma_bf16_16x16x32(kbuf[ks % (QK_AHEAD + 1)][mt], qb[ht][ks],
+                                                          sacc[ht][mt]);
                 __builtin_amdgcn_sched_barrier(0);
             }
+
+            // ---- softmax numerators against the reference max
+            if (vmask != 0xFFFFFFFFu) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint32_t nib = (vmask >> (16 * mt + 4 * grp)) & 0xFu;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int ht = 0; ht < NHT; ++ht)
+                            if (!((nib >> i) & 1u)) sacc[ht][mt][i] = -INFINITY;
+                }
+            }
+            bf16x8 pb[NHT];
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht) {
+                float bmax = fmaxf(fmaxf(fmaxf(sacc[ht][0][0], sacc[ht][0][1]),
+                                         fmaxf(sacc[ht][0][2], sacc[ht][0][3])),
+                                   fmaxf(fmaxf(sacc[ht][1][0], sacc[ht][1][1]),
+                                         fmaxf(sacc[ht][1][2], sacc[ht][1][3])));
+                bmax = fmaxf(bmax, xor16_f(bmax));
+                bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
+                const float bz = bmax * p.scale_log2;
+                m_seen[ht] = fmaxf(m_seen[ht], bz);
+                if (m_run[ht] == -INFINITY)
+                    m_run[ht] = bz;              // first usable key: O and l are still zero
+                else if (bz > m_run[ht] + MAX_RISE)
+                    restart = true;
+                const float neg_m = m_run[ht] == -INFINITY ? 0.f : -m_run[ht];
+                float pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pv[e] = exp2f(fmaf(sacc[ht][e >> 2][e & 3], p.scale_log2, neg_m));
+                l_run[ht] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+                pb[ht] = bf16x8{(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3],
+                                (__bf16)pv[4], (__bf16)pv[5], (__bf16)pv[6], (__bf16)pv[7]};
+            }
+
+            // ---- O^T += V^T P^T.  A = V^T via transpose reads: 16-lane group
+            // grp reads rows (keys) 4*grp + r and 16 + 4*grp + r; lane row16 of
+            // the group addresses row row16/4, columns 16*ct + 4*(row16%4) .. +3.
+            // Each A operand feeds NHT MFMAs.
+            // V^T operands are loaded PV_AHEAD c-tiles ahead of their MFMAs.
+            constexpr int PV_AHEAD = 3;
+            const int vAz = vA + z;
+            i16x4 vbuf[PV_AHEAD + 1][2];
+#pragma unroll
+            for (int ct = 0; ct < PV_AHEAD; ++ct) {
+                vbuf[ct][0] = lds_read_tr16(cur + vAz + 32 * ct);
+                vbuf[ct][1] = lds_read_tr16(cur + vAz + 16 * PA + 32 * ct);
+            }
+#pragma unroll
+            for (int ct = 0; ct < CTILES; ++ct) {
+                if (ct + PV_AHEAD < CTILES) {
+                    vbuf[(ct + PV_AHEAD) % (PV_AHEAD + 1)][0] = lds_read_tr16(cur + vAz + 32 * (ct + PV_AHEAD));
+                    vbuf[(ct + PV_AHEAD) % (PV_AHEAD + 1)][1] =
+                        lds_read_tr16(cur + vAz + 16 * PA + 32 * (ct + PV_AHEAD));
+                }
+                const i16x4 lo = vbuf[ct % (PV_AHEAD + 1)][0], hi = vbuf[ct % (PV_AHEAD + 1)][1];
+                const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+                for (int ht = 0; ht < NHT; ++ht) o[ht][ct] = mfma_bf16_16x16x32(a, pb[ht], o[ht][ct]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        for (int blk = 0; blk < nblk; blk += 3) {
+            step(blk, lb0, lb2);
+            if (blk + 1 < nblk) step(blk + 1, lb1, lb0);
+            if (blk + 2 < nblk) step(blk + 2, lb2, lb1);
         }
-    };
-    for (int blk = 0; blk < nblk; blk += 2) {
-        step(blk, lb0, lb1);
-        if (blk + 1 < nblk) step(blk + 1, lb1, lb0);
+
+        // ---- did any head of any wave outgrow its reference max?
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of this pass left in flight
+        if (l == 0) restart_flag[wave] = __ballot(restart) != 0;
+        __syncthreads();
+        bool again = false;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) again |= restart_flag[w] != 0;
+        __syncthreads();
+        if (!again) break;
     }
 
     // ---- finish: full sum per head, normalise, write
@@ -260,62 +335,62 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(MlaParams p) {
         const bool empty = !(l_tot > 0.f);
         const float inv = empty ? 0.f : 1.f / l_tot;
         const float lse_v = empty ? -INFINITY : (m_run[ht] + log2f(l_tot)) * LN2;
+        const int c0 = 4 * grp;
         if (p.splits == 1) {
-            uint16_t *orow = p.out + ((int64_t)t * H + h) * DV + 4 * grp;
+            uint16_t *orow = out + ((int64_t)t * H + h) * DV + c0;
 #pragma unroll
             for (int ct = 0; ct < CTILES; ++ct) {
-                u32x2 v = {pack_bf16x2(o[ht][ct][0] * inv, o[ht][ct][1] * inv),
-                           pack_bf16x2(o[ht][ct][2] * inv, o[ht][ct][3] * inv)};
-                *reinterpret_cast<u32x2 *>(orow + 16 * ct) = v;
+                const bf16x4 v = {(__bf16)(o[ht][ct][0] * inv), (__bf16)(o[ht][ct][1] * inv),
+                                  (__bf16)(o[ht][ct][2] * inv), (__bf16)(o[ht][ct][3] * inv)};
+                *reinterpret_cast<bf16x4 *>(orow + 16 * ct) = v;
             }
-            if (grp == 0) p.lse[(int64_t)t * H + h] = lse_v;
+            if (grp == 0) lse[(int64_t)t * H + h] = lse_v;
         } else {
-            float *orow = p.o_part + (((int64_t)t * p.splits + split) * H + h) * DV + 4 * grp;
+            float *orow = o_part + (((int64_t)t * p.splits + split) * H + h) * DV + c0;
 #pragma unroll
             for (int ct = 0; ct < CTILES; ++ct)
                 *reinterpret_cast<f32x4 *>(orow + 16 * ct) = o[ht][ct] * inv;
-            if (grp == 0) p.lse_part[((int64_t)t * p.splits + split) * H + h] = lse_v;
+            if (grp == 0) lse_part[((int64_t)t * p.splits + split) * H + h] = lse_v;
         }
     }
 }
 
 // Combines split partials: lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) o_s.
-// Grid: x = query row; 128 threads x 4 columns each per head loop.
+// Grid: x = query row, y = pair of heads; 128 threads x 4 value columns per head.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
     const int t = blockIdx.x;
+    const int h = 2 * blockIdx.y + (threadIdx.x >> 7);
+    const int c = 4 * (threadIdx.x & 127);
     const int S = p.splits;
-    for (int h = threadIdx.x >> 7 ? 1 : 0; h < H; h += 2) {
-        const float *lp = p.lse_part + ((int64_t)t * S) * H + h;
-        float mx = -INFINITY;
-        for (int s = 0; s < S; ++s) mx = fmaxf(mx, lp[(int64_t)s * H]);
+    const float *lp = p.lse_part + (int64_t)t * S * H + h;
+    float mx = -INFINITY;
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, lp[(int64_t)s * H]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float L = -INFINITY;
+    if (mx != -INFINITY) {
         float den = 0.f;
-        if (mx != -INFINITY)
-            for (int s = 0; s < S; ++s) den += expf(lp[(int64_t)s * H] - mx);
-        const float L = mx == -INFINITY ? -INFINITY : mx + logf(den);
-        const int c = 4 * (threadIdx.x & 127);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (mx != -INFINITY) {
-            for (int s = 0; s < S; ++s) {
-                const float ls = lp[(int64_t)s * H];
-                if (ls == -INFINITY) continue;
-                const float wgt = expf(ls - L);
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(
-                    p.o_part + (((int64_t)t * S + s) * H + h) * DV + c);
-                acc += v * wgt;
-            }
+        for (int s = 0; s < S; ++s) den += expf(lp[(int64_t)s * H] - mx);
+        L = mx + logf(den);
+        for (int s = 0; s < S; ++s) {
+            const float ls = lp[(int64_t)s * H];
+            if (ls == -INFINITY) continue;
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(
+                p.o_part + (((int64_t)t * S + s) * H + h) * DV + c);
+            acc += v * expf(ls - L);
         }
-        u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-        *reinterpret_cast<u32x2 *>(p.out + ((int64_t)t * H + h) * DV + c) = v;
-        if ((threadIdx.x & 127) == 0) p.lse[(int64_t)t * H + h] = L;
     }
+    const bf16x4 v = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+    *reinterpret_cast<bf16x4 *>(p.out + ((int64_t)t * H + h) * DV + c) = v;
+    if ((threadIdx.x & 127) == 0) p.lse[(int64_t)t * H + h] = L;
 }
 
 hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(sparse_mla_kernel, dim3(T, p.splits), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL(sparse_mla_kernel, dim3(T, p.splits), dim3(NTHREADS), 0, s, p, p.idx, p.out,
+                       p.lse, p.o_part, p.lse_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    hipLaunchKernelGGL(mla_merge_kernel, dim3(T), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(mla_merge_kernel, dim3(T, H / 2), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -157,53 +157,143 @@ class Inputs:
     seed: int
 
 
-def _seq_rows(batch: Batch, seed, tid, which: str, elems: int, scale: float, per_seq: bool):
-    """Generate query-side (which='q') or cache-side (which='kv') rows; with
-    per_seq each sequence has its own stream (rows restart at 0 per sequence)."""
-    cu = batch.cu_q if which == "q" else batch.cu_kv
-    total = int(cu[-1])
-    out = np.empty((total, elems), dtype=np.float32)
-    if not per_seq:
-        normal_rows(seed, tid, 0, total, elems, scale, out=out)
+class Workload:
+    """Row-addressable description of one forward's inputs.  Every row of every
+    tensor is a pure function of (seed, tensor id, [sequence,] row), so the same
+    values can be produced in full (small cases), streamed to the GPU in chunks
+    (large cases), or regenerated for a few sampled rows (the oracle side).
+
+    q_I, k_I ~ N(0,1) as FP8 E4M3FN with a per-token absmax scale (when fp8);
+    w ~ N(0,1) * w_scale (default 1/sqrt(HI)); q, kv ~ N(0,1) rounded to bf16
+    (float32 when fp8=False); softmax scale 1/sqrt(D) unless given.  With
+    per_seq each sequence draws from its own streams (rows restart per sequence).
+    """
+
+    def __init__(self, batch: Batch, *, seed: int, HI=64, DI=128, H=128, D=576, Dv=512, k=2048,
+                 scale: float | None = None, w_scale: float | None = None, fp8: bool = True,
+                 per_seq: bool = False):
+        self.batch, self.seed = batch, int(seed)
+        self.HI, self.DI, self.H, self.D, self.Dv, self.k = HI, DI, H, D, Dv, k
+        self.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
+        self.w_scale = float(1.0 / math.sqrt(HI) if w_scale is None else w_scale)
+        self.fp8, self.per_seq = fp8, per_seq
+
+    # -- row generation ------------------------------------------------------
+    def _rows(self, tid, side, r0, r1, elems, scale):
+        """Rows [r0, r1) (global numbering) of a query-side ('q') or cache-side
+        ('kv') tensor."""
+        out = np.empty((r1 - r0, elems), dtype=np.float32)
+        if not self.per_seq:
+            return normal_rows(self.seed, tid, r0, r1, elems, scale, out=out)
+        cu = self.batch.cu_q if side == "q" else self.batch.cu_kv
+        b = int(np.searchsorted(cu, r0, side="right") - 1)
+        r = r0
+        while r < r1:
+            while int(cu[b + 1]) <= r:
+                b += 1
+            hi = min(r1, int(cu[b + 1]))
+            lo = int(cu[b])
+            normal_rows(self.seed, tid, r - lo, hi - lo, elems, scale, sub=b,
+                        out=out[r - r0:hi - r0])
+            r = hi
         return out
-    for b in range(batch.B):
-        lo, hi = int(cu[b]), int(cu[b + 1])
-        if hi > lo:
-            normal_rows(seed, tid, 0, hi - lo, elems, scale, sub=b, out=out[lo:hi])
-    return out
+
+    def qi_rows(self, r0, r1):
+        x = self._rows(T_QI, "q", r0, r1, self.HI * self.DI, 1.0)
+        if not self.fp8:
+            return x.reshape(-1, self.HI, self.DI), np.ones((r1 - r0, self.HI), np.float32)
+        codes, sc = quant_e4m3_rows(x)  # one scale per token
+        return (codes.reshape(-1, self.HI, self.DI),
+                np.repeat(sc[:, None], self.HI, axis=1).astype(np.float32))
+
+    def w_rows(self, r0, r1):
+        return self._rows(T_W, "q", r0, r1, self.HI, self.w_scale)
+
+    def q_rows(self, r0, r1):
+        x = self._rows(T_Q, "q", r0, r1, self.H * self.D, 1.0)
+        return (to_bf16_bits(x) if self.fp8 else x).reshape(-1, self.H, self.D)
+
+    def ki_rows(self, r0, r1):
+        x = self._rows(T_KI, "kv", r0, r1, self.DI, 1.0)
+        if not self.fp8:
+            return x, np.ones(r1 - r0, np.float32)
+        return quant_e4m3_rows(x)
+
+    def kv_rows(self, r0, r1):
+        x = self._rows(T_KV, "kv", r0, r1, self.D, 1.0)
+        return to_bf16_bits(x) if self.fp8 else x
+
+    # -- assembled forms -----------------------------------------------------
+    def host(self) -> "Inputs":
+        T, N = self.batch.T, self.batch.N
+        qi, qs = self.qi_rows(0, T)
+        ki, ks = self.ki_rows(0, N)
+        return Inputs(self.batch, qi, qs, self.w_rows(0, T), ki, ks, self.q_rows(0, T),
+                      self.kv_rows(0, N), self.HI, self.DI, self.H, self.D, self.Dv, self.k,
+                      self.scale, self.seed)
+
+    def sampled_host(self, rows) -> "Inputs":
+        """Full caches plus the query-side tensors of the given rows only: the
+        other query rows stay zero in arrays allocated with np.zeros (pages
+        never touched are never made resident), so the oracle can check a few
+        rows of a large forward with its usual global row numbering."""
+        T, N = self.batch.T, self.batch.N
+        qi = np.zeros((T, self.HI, self.DI), np.uint8 if self.fp8 else np.float32)
+        qs = np.zeros((T, self.HI), np.float32)
+        w = np.zeros((T, self.HI), np.float32)
+        q = np.zeros((T, self.H, self.D), np.uint16 if self.fp8 else np.float32)
+        for t in sorted(set(int(r) for r in rows)):
+            a, sc = self.qi_rows(t, t + 1)
+            qi[t], qs[t] = a[0], sc[0]
+            w[t] = self.w_rows(t, t + 1)[0]
+            q[t] = self.q_rows(t, t + 1)[0]
+        ki, ks = self.ki_rows(0, N)
+        return Inputs(self.batch, qi, qs, w, ki, ks, q, self.kv_rows(0, N), self.HI, self.DI,
+                      self.H, self.D, self.Dv, self.k, self.scale, self.seed)
+
+    def device(self, device="cuda", chunk_elems: int = 1 << 26) -> dict:
+        """All inputs as torch tensors on `device`, generated in row chunks."""
+        T, N = self.batch.T, self.batch.N
+        out = {
+            "qi": torch.empty((T, self.HI, self.DI), dtype=torch.uint8, device=device),
+            "qs": torch.empty((T, self.HI), dtype=torch.float32, device=device),
+            "w": torch.empty((T, self.HI), dtype=torch.float32, device=device),
+            "q": torch.empty((T, self.H, self.D), dtype=torch.int16, device=device),
+            "ki": torch.empty((N, self.DI), dtype=torch.uint8, device=device),
+            "ks": torch.empty((N,), dtype=torch.float32, device=device),
+            "kv": torch.empty((N, self.D), dtype=torch.int16, device=device),
+        }
+
+        def put(name, r0, arr):
+            a = np.ascontiguousarray(arr)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            out[name][r0:r0 + a.shape[0]].copy_(torch.from_numpy(a))
+
+        step_q = max(1, chunk_elems // (self.H * self.D))
+        for r0 in range(0, T, step_q):
+            r1 = min(T, r0 + step_q)
+            qi, qs = self.qi_rows(r0, r1)
+            put("qi", r0, qi)
+            put("qs", r0, qs)
+            put("w", r0, self.w_rows(r0, r1))
+            put("q", r0, self.q_rows(r0, r1))
+        step_k = max(1, chunk_elems // self.D)
+        for r0 in range(0, N, step_k):
+            r1 = min(N, r0 + step_k)
+            ki, ks = self.ki_rows(r0, r1)
+            put("ki", r0, ki)
+            put("ks", r0, ks)
+            put("kv", r0, self.kv_rows(r0, r1))
+        return out
 
 
 def make_inputs(batch: Batch, *, seed: int, HI=64, DI=128, H=128, D=576, Dv=512, k=2048,
                 scale: float | None = None, w_scale: float | None = None, fp8: bool = True,
                 per_seq: bool = False) -> Inputs:
-    """Inputs for one forward: q_I, k_I ~ N(0,1) (FP8 E4M3FN with per-token
-    absmax scale when fp8), w ~ N(0,1)*w_scale (default 1/sqrt(HI), i.e. 1/8 at
-    64 heads), q and kv ~ N(0,1) rounded to bf16 (float32 when fp8=False),
-    softmax scale 1/sqrt(D) unless given."""
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if w_scale is None:
-        w_scale = 1.0 / math.sqrt(HI)
-    T, N = batch.T, batch.N
-    qi = _seq_rows(batch, seed, T_QI, "q", HI * DI, 1.0, per_seq)
-    ki = _seq_rows(batch, seed, T_KI, "kv", DI, 1.0, per_seq)
-    w = _seq_rows(batch, seed, T_W, "q", HI, w_scale, per_seq)
-    q = _seq_rows(batch, seed, T_Q, "q", H * D, 1.0, per_seq)
-    kv = _seq_rows(batch, seed, T_KV, "kv", D, 1.0, per_seq)
-    if fp8:
-        qi_codes, qs = quant_e4m3_rows(qi)          # one scale per token
-        qi = qi_codes.reshape(T, HI, DI)
-        qi_scale = np.repeat(qs[:, None], HI, axis=1).astype(np.float32)
-        ki, ki_scale = quant_e4m3_rows(ki)
-        q = to_bf16_bits(q).reshape(T, H, D)
-        kv = to_bf16_bits(kv)
-    else:
-        qi = qi.reshape(T, HI, DI)
-        qi_scale = np.ones((T, HI), np.float32)
-        ki_scale = np.ones(N, np.float32)
-        q = q.reshape(T, H, D)
-    return Inputs(batch, qi, qi_scale, w.reshape(T, HI), ki, ki_scale, q, kv,
-                  HI, DI, H, D, Dv, k, float(scale), seed)
+    """Full host arrays of Workload(...) (small cases)."""
+    return Workload(batch, seed=seed, HI=HI, DI=DI, H=H, D=D, Dv=Dv, k=k, scale=scale,
+                    w_scale=w_scale, fp8=fp8, per_seq=per_seq).host()
 
 
 def decode_contexts(seed: int, B: int, lo: int = 16384, hi: int = 131072) -> np.ndarray:
@@ -224,21 +314,21 @@ def tiny_prefill(k: int = 32) -> Inputs:
                        D=80, Dv=64, k=k, fp8=False)
 
 
-def prefill(L: int, seed: int = SEED_BASE + 2, k: int = 2048) -> Inputs:
+def prefill(L: int, seed: int = SEED_BASE + 2, k: int = 2048) -> Workload:
     """Batch 1, L causal tokens: FP8 indexer (64 heads x 128), 128-head MQA-mode
     MLA over 576-d bf16 latent rows (value = first 512)."""
-    return make_inputs(Batch.prefill(L, L, 0), seed=seed, k=k)
+    return Workload(Batch.prefill(L, L, 0), seed=seed, k=k)
 
 
 def decode(B: int = 64, seed: int = SEED_BASE + 4, lo: int = 16384, hi: int = 131072,
-           k: int = 2048) -> Inputs:
+           k: int = 2048) -> Workload:
     """B sequences, one new token each at the end of a context drawn from
     U{lo..hi}; per-sequence streams."""
     ctx = decode_contexts(seed, B, lo, hi)
-    return make_inputs(Batch.decode(ctx), seed=seed, k=k, per_seq=True)
+    return Workload(Batch.decode(ctx), seed=seed, k=k, per_seq=True)
 
 
 def chunked_prefill(n_new: int = 4096, ctx: int = 131072, seed: int = SEED_BASE + 5,
-                    k: int = 2048) -> Inputs:
+                    k: int = 2048) -> Workload:
     """n_new query tokens at positions ctx-n_new .. ctx-1 over a ctx-entry cache."""
-    return make_inputs(Batch.prefill(n_new, ctx, ctx - n_new), seed=seed, k=k)
+    return Workload(Batch.prefill(n_new, ctx, ctx - n_new), seed=seed, k=k)
