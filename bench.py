@@ -138,16 +138,29 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=5,
                     help="timed launches of the dominant kernel")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(each MI355X box here has a single GPU).", file=sys.stderr)
+        print(f"bench.py: the DSA path runs on a single GPU; --gpus {args.gpus} is not "
+              "supported (no multi-GPU sharding is implemented).", file=sys.stderr)
         return 2
 
     import torch
-    import sparse_attention_16_amd as dsa
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
+        return 0
+    import sparse_attention_16_amd as dsa
+
     wl, entry = make_workload(args.workload)
     b = wl.batch
     say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
