@@ -38,6 +38,40 @@ PEAK_HBM_GBS = 8000.0
 
 HI, DI, H, D, DV = 64, 128, 128, 576, 512
 
+# HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch, one run each).  The raw
+# counters are scaled by what the same counters read for a plain 1 GiB
+# device-to-device copy (bench.py --copy-calibration): FETCH_SIZE reads
+# 524300 KiB for the 1 GiB read (x2.0), WRITE_SIZE 1048576 KiB (x1.0).  Each
+# entry holds a hash of the sources the kernel was built from when the
+# counters were taken; once those sources change the figure no longer describes
+# the kernel and the traffic is reported as null.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+COUNTERS = {
+    ("prefill_32k", "sparse_mla_kernel"): {
+        "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h", "api.hip"),
+        "sha256_16": "9f9b481a6919852e", "fetch_kib": 11637631, "write_kib": 4214704},
+    ("decode_64k", "indexer_decode_kernel"): {
+        "sources": ("indexer.hip", "dsa_device.h", "kernels.h", "api.hip"),
+        "sha256_16": "c8aa8d564659d080", "fetch_kib": 289436, "write_kib": 17469},
+}
+
+
+def measured_traffic(workload, kernel):
+    """Scaled FETCH+WRITE bytes per launch, or None when no counters were taken
+    for this kernel and workload or its sources have changed since."""
+    import hashlib
+    c = COUNTERS.get((workload, kernel))
+    if c is None:
+        return None
+    h = hashlib.sha256()
+    for f in c["sources"]:
+        with open(os.path.join(ROOT, "sparse_attention_16_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != c["sha256_16"]:
+        return None
+    return {"fetch": c["fetch_kib"] * 1024 * FETCH_SCALE, "write": c["write_kib"] * 1024 * WRITE_SCALE}
+
 
 # ----------------------------------------------------------------- accounting
 
@@ -75,10 +109,13 @@ def indexer_bytes(nvis, ctx_total, T):
     return ctx_total * (DI + 4) + T * (HI * DI + HI * 8) + 4.0 * float(np.sum(nvis))
 
 
-def mla_bytes(nvis, k, T):
-    """Algorithmic HBM bytes of sparse MLA if every selected 1152-byte latent row
-    came from HBM (the decode regime): gathered rows + q + out + idx + lse."""
-    return float(np.sum(np.minimum(nvis, k))) * D * 2 + T * (H * D * 2 + H * DV * 2 + k * 4 + H * 4)
+def mla_bytes(nvis, k, T, N=None):
+    """Algorithmic HBM bytes of sparse MLA: q + out + idx + lse, plus the latent
+    rows.  Without N every selected 1152-byte row is counted (the decode regime,
+    where rows are not shared between queries); with N each of the N cached rows
+    is counted once (the least any prefill schedule can read)."""
+    rows = float(np.sum(np.minimum(nvis, k))) if N is None else min(float(N), float(np.sum(np.minimum(nvis, k))))
+    return rows * D * 2 + T * (H * D * 2 + H * DV * 2 + k * 4 + H * 4)
 
 
 # ------------------------------------------------------------------ workloads
@@ -226,16 +263,23 @@ def main(argv=None):
         e1.record(stream)
     torch.cuda.synchronize()
     kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    traffic = measured_traffic(args.workload, name)
     if entry == "prefill":
         achieved = flops / (kms * 1e-3) / 1e12
         roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "avg_ms": round(kms, 4), "algorithmic_flops": flops}
+                "traffic": None, "avg_ms": round(kms, 4), "algorithmic_flops": flops,
+                "algorithmic_bytes": mla_bytes(nvis, wl.k, b.T, b.N)}
     else:
         achieved = nbytes / (kms * 1e-3) / 1e9
         roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": None, "avg_ms": round(kms, 4), "algorithmic_bytes": nbytes}
+    if traffic is not None:
+        roof["traffic"] = round(traffic["fetch"] + traffic["write"])
+        roof["traffic_unit"] = "bytes/launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
+        roof["traffic_fetch"] = round(traffic["fetch"])
+        roof["traffic_write"] = round(traffic["write"])
     say(f"[bench] {name}: {kms:.3f} ms/launch, {roof['achieved']} {roof['unit']} "
         f"({100 * roof['frac']:.1f}% of peak)")
 

@@ -2,7 +2,9 @@
 bench.py times (dsa_prefill_fwd for prefill workloads, dsa_decode_fwd for the
 decode batch), checked on sampled query rows that the oracle recomputes one by
 one: index scores (through dsa_indexer_scores on the same inputs), the top-k
-set modulo near-ties, and the attention output and lse.
+set modulo near-ties, and the attention output and lse, which the oracle
+recomputes over the GPU's own index set (several sets are correct at near-ties,
+and attention must be right for whichever one was chosen).
 
 Sampled rows always include the first and last rows and the rows around the
 point where the visible count crosses k."""
@@ -76,8 +78,7 @@ def test_fullsize_sampled_rows(dsa, name):
     differ = check_idx_sets(g_idx, ref_idx, ref_s, A, nvis[rows], wl.k, name)
     say(f"  {name}: {len(differ)} rows differ only at near-ties")
     assert len(differ) <= max(2, len(rows) // 10)
-    same = np.setdiff1d(np.arange(len(rows)), differ)
-    o_ref, l_ref = oracle.sparse_attn(b.cu_q, b.cu_kv, b.pos0, inp.q, inp.kv, ref_idx[same],
-                                      wl.Dv, wl.scale, rows=rows[same])
-    dl, rel = check_attention(g_out[same], g_lse[same], o_ref, l_ref, name)
+    o_ref, l_ref = oracle.sparse_attn(b.cu_q, b.cu_kv, b.pos0, inp.q, inp.kv, g_idx, wl.Dv,
+                                      wl.scale, rows=rows)
+    dl, rel = check_attention(g_out, g_lse, o_ref, l_ref, name)
     say(f"  {name}: attention max |dlse| {dl:.3g}, max row ||do||/||o|| {rel:.3g}")
