@@ -97,9 +97,11 @@ __device__ __forceinline__ void gather_block(const uint16_t *kv, const int32_t *
         __builtin_amdgcn_global_load_lds(base + s * ROWB + 16 * l, buf + r * PA, 16, 0, 0);
     }
     const int rr = l >> 3;   // row inside the slab
-    int sr = s8[0];
+    // lane i < 8 holds s8[i]; every lane then fetches the entry of its slab row
+    int v8 = s8[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) sr = rr == i ? s8[i] : sr;
+    for (int i = 1; i < 8; ++i) asm("v_writelane_b32 %0, %1, %2" : "+v"(v8) : "s"(s8[i]), "i"(i));
+    const int sr = __builtin_amdgcn_ds_bpermute(rr << 2, v8);
     const int64_t s = clamp_row(sr, ctx);
     __builtin_amdgcn_global_load_lds(base + s * ROWB + 1024 + 16 * ((l & 7) ^ rr),
                                      buf + RB + wave * 1024, 16, 0, 0);
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
                 float pv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    pv[e] = exp2f(fmaf(sacc[ht][e >> 2][e & 3], p.scale_log2, neg_m));
+                    pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[ht][e >> 2][e & 3], p.scale_log2, neg_m));
                 l_run[ht] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
                 pb[ht] = bf16x8{(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3],
                                 (__bf16)pv[4], (__bf16)pv[5], (__bf16)pv[6], (__bf16)pv[7]};
