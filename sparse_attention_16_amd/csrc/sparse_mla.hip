@@ -58,6 +58,7 @@ constexpr int MT = BK / 16;              // 16-key tiles per block
 constexpr int CTILES = DV / 16;          // 32 value tiles
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float MAX_RISE = 64.f;         // log2 headroom above the reference max
+constexpr int MAX_SEL = 2048;            // largest k (slots staged in LDS)
 
 static_assert(BK == 32 && NWAVES * 8 == BK, "each wave loads 8 rows and one rope slab");
 
@@ -73,22 +74,19 @@ __device__ __forceinline__ int64_t clamp_row(int s, int ctx) {
 // rows 8w..8w+7 (dims 0..511: one 1 KB load per row) and their rope slab
 // (dims 512..575, 8 rows x 128 B): inside a slab, logical 16-byte chunk c of
 // row rr sits at chunk position c ^ rr, so that a column of 8 rows read
-// together lands on distinct banks.  Slot positions are read with scalar loads
-// (wave-uniform addresses), so they never wait behind the vector-memory
-// counter the direct-to-LDS loads use.
-__device__ __forceinline__ void gather_block(const uint16_t *kv, const int32_t *__restrict__ idx_row,
-                                             int nsel, int blk, int64_t kv0, int ctx, lds_u8 *buf,
-                                             int l) {
+// together lands on distinct banks.  Slot positions come from the row's index
+// slice staged in LDS (sel, padded with -1 up to a whole block): a wave-
+// uniform LDS read is a short wait, where a scalar load of fresh index data
+// would wait on L2 every block.
+__device__ __forceinline__ void gather_block(const uint16_t *kv, const DSA_LDS int32_t *sel, int blk,
+                                             int64_t kv0, int ctx, lds_u8 *buf, int l) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int jw = blk * BK + 8 * wave;
-    int s8[8];
-    if (jw + 8 <= nsel) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s8[i] = idx_row[jw + i];
-    } else {   // last, partial block of the slice
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s8[i] = idx_row[jw + i < nsel ? jw + i : nsel - 1];
-    }
+    const DSA_LDS int32_t *s8p = sel + blk * BK + 8 * wave;
+    const i32x4 a = *reinterpret_cast<const DSA_LDS i32x4 *>(s8p);
+    const i32x4 b = *reinterpret_cast<const DSA_LDS i32x4 *>(s8p + 4);
+    const int rr = l >> 3;   // row inside the slab
+    const int sr = s8p[rr];
+    const int s8[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     const uint8_t *base = reinterpret_cast<const uint8_t *>(kv) + kv0 * ROWB;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -96,12 +94,6 @@ __device__ __forceinline__ void gather_block(const uint16_t *kv, const int32_t *
         const int64_t s = clamp_row(s8[i], ctx);
         __builtin_amdgcn_global_load_lds(base + s * ROWB + 16 * l, buf + r * PA, 16, 0, 0);
     }
-    const int rr = l >> 3;   // row inside the slab
-    // lane i < 8 holds s8[i]; every lane then fetches the entry of its slab row
-    int v8 = s8[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) asm("v_writelane_b32 %0, %1, %2" : "+v"(v8) : "s"(s8[i]), "i"(i));
-    const int sr = __builtin_amdgcn_ds_bpermute(rr << 2, v8);
     const int64_t s = clamp_row(sr, ctx);
     __builtin_amdgcn_global_load_lds(base + s * ROWB + 1024 + 16 * ((l & 7) ^ rr),
                                      buf + RB + wave * 1024, 16, 0, 0);
@@ -109,16 +101,36 @@ __device__ __forceinline__ void gather_block(const uint16_t *kv, const int32_t *
 
 }  // namespace
 
+// S^T accumulators live in VGPRs: the QK MFMAs are written as inline asm with
+// VGPR operands, because the compiler would otherwise place them in AGPRs,
+// which the 256 O accumulators already fill (it then moves O registers out and
+// back around every block).  The compiler does not know these are MFMAs, so
+// the wait states an MFMA result needs before a VALU instruction reads it are
+// inserted explicitly (qk_drain: 24, more than any 16x16 MFMA requires), and
+// the first k-step takes an inline zero accumulator instead of a VALU-written
+// one.  Accumulation is in place (dst == srcC), which back-to-back MFMAs of
+// the same opcode support without wait states.
+__device__ __forceinline__ void qk_first(f32x4 &d, const bf16x8 &a, const bf16x8 &b) {
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_next(f32x4 &d, const bf16x8 &a, const bf16x8 &b) {
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_drain(f32x4 (&s)[NHT][MT]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
+}
+
 // Grid: x = query row, y = split.  LDS: three gather buffers + restart flags.
 // The index array and every output are separate restrict-qualified arguments
-// so the compiler can prove no store clobbers idx and read the slot positions
-// with scalar loads.
+// (no store of the kernel can clobber idx).
 __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     MlaParams p, const int32_t *__restrict__ idx, uint16_t *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t buf2[BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
     __shared__ int restart_flag[NWAVES];
 
     const int t = blockIdx.x, split = blockIdx.y;
@@ -144,14 +156,17 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
         for (int ks = 0; ks < KSTEPS; ++ks)
             qb[ht][ks] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
     }
+    // the slice's slot positions, padded with -1 (row 0, masked) to whole blocks
+    for (int j = threadIdx.x; j < nblk * BK; j += NTHREADS) sel[j] = j < nsel ? idx_row[j] : -1;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query operands resident before the pipeline
+    __syncthreads();
 
     // validity masks: lane b holds bit i = slot b*BK + i is a usable row
     // (inside the slice, inside [0, ctx)); read per block with readlane
     uint32_t maskv = 0;
     for (int it = 0; it * kWave < nsel; ++it) {
         const int j = it * kWave + l;
-        const bool ok = j < nsel && (uint32_t)idx_row[j < nsel ? j : 0] < (uint32_t)ri.ctx;
+        const bool ok = j < nsel && (uint32_t)sel[j < nsel ? j : 0] < (uint32_t)ri.ctx;
         const uint64_t m = __ballot(ok);
         maskv = l == 2 * it ? (uint32_t)m : (l == 2 * it + 1 ? (uint32_t)(m >> 32) : maskv);
     }
@@ -164,6 +179,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     const int kB17 = kB + 16 * ((4 + grp) ^ rr16);                     // dims 544 + 8*grp
     const int vA = (4 * grp + (row16 >> 2)) * PA + 8 * (row16 & 3);    // V^T transpose reads
 
+    const DSA_LDS int32_t *lsel = (const DSA_LDS int32_t *)sel;
     lds_u8 *lb0 = (lds_u8 *)buf0;
     lds_u8 *lb1 = (lds_u8 *)buf1;
     lds_u8 *lb2 = (lds_u8 *)buf2;
@@ -185,8 +201,8 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
 
         // Pipeline: at the top of step b, vmcnt(9) leaves only this wave's 9
         // loads of block b+1 in flight, so block b has landed.
-        if (nblk > 0) gather_block(p.kv, idx_row, nsel, 0, ri.kv0, ri.ctx, lb0, l);
-        if (nblk > 1) gather_block(p.kv, idx_row, nsel, 1, ri.kv0, ri.ctx, lb1, l);
+        if (nblk > 0) gather_block(p.kv, lsel, 0, ri.kv0, ri.ctx, lb0, l);
+        if (nblk > 1) gather_block(p.kv, lsel, 1, ri.kv0, ri.ctx, lb1, l);
 
         // One block step: cur = buffer of block blk, nxt2 = buffer for blk+2
         // (the one block blk-1 used).  `cur` and `nxt2` are distinct LDS arrays
@@ -206,15 +222,11 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
             // the loop they would cost registers the operands need.
             const int z = blk >> 30;
             const int lz = lane_id() + z;
-            if (blk + 2 < nblk) gather_block(p.kv, idx_row, nsel, blk + 2, ri.kv0, ri.ctx, nxt2, lz);
+            if (blk + 2 < nblk) gather_block(p.kv, lsel, blk + 2, ri.kv0, ri.ctx, nxt2, lz);
             const uint32_t vmask = __builtin_amdgcn_readlane(maskv, blk);
 
             // ---- S^T: MT key tiles x NHT head tiles, lane = (head row16, keys 4*grp+i)
             f32x4 sacc[NHT][MT];
-#pragma unroll
-            for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) sacc[ht][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
             // K operands are loaded QK_AHEAD k-steps ahead of their MFMAs
             // (software pipeline; one wave per SIMD hides nothing by itself).
             constexpr int QK_AHEAD = 2;
@@ -241,11 +253,14 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int ht = 0; ht < NHT; ++ht)
-                        sacc[ht][mt] = mfma_bf16_16x16x32(kbuf[ks % (QK_AHEAD + 1)][mt], qb[ht][ks],
-                                                          sacc[ht][mt]);
+                        if (ks == 0)
+                            qk_first(sacc[ht][mt], kbuf[0][mt], qb[ht][0]);
+                        else
+                            qk_next(sacc[ht][mt], kbuf[ks % (QK_AHEAD + 1)][mt], qb[ht][ks]);
                 __builtin_amdgcn_sched_barrier(0);
             }
 
+            qk_drain(sacc);
             // ---- softmax numerators against the reference max
             if (vmask != 0xFFFFFFFFu) {
 #pragma unroll
