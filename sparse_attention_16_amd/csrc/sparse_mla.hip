@@ -276,18 +276,23 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
             bf16x8 pb[NHT];
 #pragma unroll
             for (int ht = 0; ht < NHT; ++ht) {
+                // this lane's 8 logits of the head; the restart test and the
+                // running maximum work per lane (the head's 4 lane groups are
+                // combined once per pass), only the first usable block needs
+                // the head's block maximum across the groups
                 float bmax = fmaxf(fmaxf(fmaxf(sacc[ht][0][0], sacc[ht][0][1]),
                                          fmaxf(sacc[ht][0][2], sacc[ht][0][3])),
                                    fmaxf(fmaxf(sacc[ht][1][0], sacc[ht][1][1]),
                                          fmaxf(sacc[ht][1][2], sacc[ht][1][3])));
-                bmax = fmaxf(bmax, xor16_f(bmax));
-                bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
                 const float bz = bmax * p.scale_log2;
                 m_seen[ht] = fmaxf(m_seen[ht], bz);
-                if (m_run[ht] == -INFINITY)
-                    m_run[ht] = bz;              // first usable key: O and l are still zero
-                else if (bz > m_run[ht] + MAX_RISE)
+                if (m_run[ht] == -INFINITY) {    // first usable key: O and l are still zero
+                    bmax = fmaxf(bmax, xor16_f(bmax));
+                    bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
+                    m_run[ht] = bmax * p.scale_log2;
+                } else if (bz > m_run[ht] + MAX_RISE) {
                     restart = true;
+                }
                 const float neg_m = m_run[ht] == -INFINITY ? 0.f : -m_run[ht];
                 float pv[8];
 #pragma unroll
@@ -332,6 +337,13 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
             if (blk + 2 < nblk) step(blk + 2, lb2, lb1);
         }
 
+        // ---- the head's maximum over its 4 lane groups (the reference of a
+        // second pass)
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+            m_seen[ht] = fmaxf(m_seen[ht], xor16_f(m_seen[ht]));
+            m_seen[ht] = fmaxf(m_seen[ht], shfl_xor_f(m_seen[ht], 32));
+        }
         // ---- did any head of any wave outgrow its reference max?
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of this pass left in flight
         if (l == 0) restart_flag[wave] = __ballot(restart) != 0;

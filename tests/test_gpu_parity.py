@@ -202,6 +202,45 @@ def test_sparse_mla_holes_and_empty_rows(dsa):
     assert np.all(np.isneginf(lse.cpu().numpy()[3]))
 
 
+@pytest.mark.parametrize("T,amp", [(512, 0x43C8), (512, 0x4416), (40, 0x4416)])
+def test_sparse_mla_reference_restart(dsa, T, amp):
+    """A selected key whose logit exceeds the first block's maximum by more
+    than the kernel's headroom (64 in log2 units) must trigger the exact
+    second pass.  Every query head gets a strong component along dim 0 and one
+    cache row a large dim-0 value: its logit is about 50 (natural units) while
+    the others stay near N(0, 1) (amp = bf16 400: about 62..78 log2 units
+    above the first block, around the headroom; bf16 600: far above).  The
+    row's position in the selected set
+    varies: first block (no restart), middle, last.  T=512 runs one split per
+    row; T=40 splits the selected set (the merge sees very different lse)."""
+    say(f"[sparse_mla restart] T={T} amp={amp:#x}")
+    N = 3000
+    inp = synth.make_inputs(synth.Batch.prefill(T, N, N - T), seed=115, k=256)
+    b = inp.batch
+    big = 1500
+    q = inp.q.copy()
+    q[:, :, 0] = np.uint16(0x4040)           # 3.0 in bf16
+    kv = inp.kv.copy()
+    kv[big, 0] = np.uint16(amp)
+    rng = np.random.default_rng(9)
+    idx = np.empty((T, 256), np.int32)
+    for t in range(T):
+        cand = rng.choice(np.setdiff1d(np.arange(N - T + t + 1), [big]), size=255, replace=False)
+        row = np.sort(np.append(cand, big)).astype(np.int32)
+        pos = [3, 130, 250][t % 3]           # where the big row lands in the selected set
+        row = np.delete(row, np.searchsorted(row, big))
+        idx[t] = np.insert(row, pos, big)
+    o_ref, lse_ref = oracle.sparse_attn(b.cu_q, b.cu_kv, b.pos0, q, kv, idx, inp.Dv, inp.scale)
+    assert float(np.max(lse_ref)) > 40.0      # the jump is really there
+    batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0)
+    out = torch.empty((T, 128, 512), dtype=torch.int16, device="cuda")
+    lse = torch.empty((T, 128), device="cuda")
+    dsa.sparse_mla_fwd(batch, dev(q), dev(kv), dev(idx), inp.scale, out, lse)
+    torch.cuda.synchronize()
+    dl, rel = check_attention(bf16_to_f32(out), lse.cpu().numpy(), o_ref, lse_ref, f"restart T={T} amp={amp:#x}")
+    say(f"  max |dlse| {dl:.3g}, max row ||do||/||o|| {rel:.3g}")
+
+
 # ------------------------------------------------------------ fused entries
 
 def _check_fused(dsa, inp, entry, rows=None, what=""):
