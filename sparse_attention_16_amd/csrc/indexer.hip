@@ -12,8 +12,10 @@
 // instruction; A = 16 indexer heads of one query row (held in registers for
 // the whole kernel), B = 16 keys.  The C tile holds 4 heads per lane for one
 // key column, so the ReLU and the weighted head sum run in registers (16
-// terms per lane per row) followed by a two-step cross-lane add over the four
-// 16-lane groups.  Only the final fp32 score leaves the registers.
+// terms per lane per row).  The sum over the four 16-lane groups is done for
+// four 16-key blocks at once with two rounds of VALU lane swaps (a reduce-
+// scatter that leaves key l of the 64 in lane l).  Only the final fp32 score
+// leaves the registers.
 #include "dsa_device.h"
 #include "kernels.h"
 
@@ -26,24 +28,22 @@ constexpr int DI = 128;
 constexpr int ROW_BYTES = HI * DI;  // one query row of FP8 indexer queries
 
 // Loads the A operands (4 head groups) and folded weights of one query row.
+// Branch-free: an invalid row reads row t anyway (the caller passes a valid
+// row index) and gets zero weights, so its scores are zero.
 __device__ __forceinline__ void load_query(const IndexerParams &p, int64_t t, bool valid,
                                            i32x8 (&qa)[4], float (&wq)[4][4]) {
     const int l = lane_id();
     const int row = l & 15, grp = l >> 4;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        if (valid) {
-            const uint8_t *src = p.q + t * ROW_BYTES + (16 * m + row) * DI + 32 * grp;
-            const i32x4 *s4 = reinterpret_cast<const i32x4 *>(src);
-            i32x4 lo = s4[0], hi = s4[1];
-            qa[m] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        } else {
-            qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+        const uint8_t *src = p.q + t * ROW_BYTES + (16 * m + row) * DI + 32 * grp;
+        const i32x4 *s4 = reinterpret_cast<const i32x4 *>(src);
+        const i32x4 lo = s4[0], hi = s4[1];
+        qa[m] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int j = 16 * m + 4 * grp + i;
-            wq[m][i] = valid ? p.w[t * HI + j] * p.q_scale[t * HI + j] : 0.0f;
+            wq[m][i] = (valid ? 1.0f : 0.0f) * (p.w[t * HI + j] * p.q_scale[t * HI + j]);
         }
     }
 }
@@ -63,6 +63,38 @@ __device__ __forceinline__ float score_block(const i32x8 (&qa)[4], const float (
     part += shfl_xor_f(part, 16);
     part += shfl_xor_f(part, 32);
     return part;
+}
+
+// The 16 head partials of one lane for one 16-key block: 4 MFMAs (one per
+// group of 16 heads), kept in separate accumulators so that they can be in
+// flight while the previous block's epilogue runs.
+__device__ __forceinline__ void block_mfma(const i32x8 (&qa)[4], const i32x8 &kb, f32x4 (&c)[4]) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) c[m] = mfma_f8_16x16x128(qa[m], kb, zero);
+}
+
+// ReLU + weighted sum over this lane's 16 heads (4 per MFMA tile).
+__device__ __forceinline__ float block_epilogue(const f32x4 (&c)[4], const float (&wq)[4][4]) {
+    float part = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = fmaf(wq[m][i], fmaxf(c[m][i], 0.f), part);
+    return part;
+}
+
+// Sum over the four 16-lane groups of four 16-key blocks at once: p[b] holds,
+// in lane l, the partial (over the heads of group l/16) of key 16*b + l%16.
+// Returns, in lane l, the total of key l of the 64-key group.  Two exchanges
+// of the lane halves, then of the 16-lane rows (VALU lane swaps, no LDS).
+__device__ __forceinline__ float reduce_scatter4(const float (&p)[4]) {
+    const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+    const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+    const float a = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);   // blocks 0 | 2, halves summed
+    const float b = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);   // blocks 1 | 3
+    const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(y[0]) + __uint_as_float(y[1]);
 }
 
 }  // namespace
@@ -115,7 +147,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
         const int tl = tb + 2 * wave + r;
         valid[r] = tl < nq;
         pos[r] = p.pos0[b] + tl;
-        load_query(p, (int64_t)(q0 + tl), valid[r], qa[r], wq[r]);
+        load_query(p, (int64_t)(q0 + (valid[r] ? tl : tb)), valid[r], qa[r], wq[r]);
     }
 
     // register staging of the next key tile: 1024 16-byte chunks over 512 threads
@@ -126,10 +158,9 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
         for (int r = 0; r < 2; ++r) {
             const int c = tid + 512 * r;
             const int key = c >> 3, byte = (c & 7) * 16;
-            if (kbase + key < comp_end)
-                stage[r] = *reinterpret_cast<const i32x4 *>(p.k + (kv0 + kbase + key) * DI + byte);
-            else
-                stage[r] = i32x4{0, 0, 0, 0};
+            const bool in = kbase + key < comp_end;
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(p.k + (kv0 + (in ? kbase + key : c0)) * DI + byte);
+            stage[r] = in ? v : i32x4{0, 0, 0, 0};
         }
         if (tid < PF_KT) sstage = (kbase + tid < comp_end) ? p.k_scale[kv0 + kbase + tid] : 0.f;
     };
@@ -146,36 +177,56 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
         __syncthreads();
         if (kbase + PF_KT < comp_end) fetch(kbase + PF_KT);
 
-        const int nsub = (comp_end - kbase + 15) >> 4;  // 16-key column blocks with work
-        float keep[2] = {0.f, 0.f};
-        for (int st = 0; st < PF_KT / 16; ++st) {
-            if (st < nsub) {
-                const uint8_t *src = &ktile[(16 * st + (l & 15)) * PF_PITCH + 32 * (l >> 4)];
-                const i32x4 lo = *reinterpret_cast<const i32x4 *>(src);
-                const i32x4 hi = *reinterpret_cast<const i32x4 *>(src + 16);
-                const i32x8 kb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        // 8 blocks of 16 keys, software-pipelined: the MFMAs of block st+1
+        // are issued before the epilogue of block st.  Rows past the end of
+        // the sequence run with zero operands (no branches); their scores are
+        // not stored.
+        auto kload = [&](int st) {
+            const uint8_t *src = &ktile[(16 * st + (l & 15)) * PF_PITCH + 32 * (l >> 4)];
+            const i32x4 lo = *reinterpret_cast<const i32x4 *>(src);
+            const i32x4 hi = *reinterpret_cast<const i32x4 *>(src + 16);
+            return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        // Software pipeline over the 8 blocks of 16 keys: each stage issues
+        // the MFMAs of block st+1 (both rows) and then runs the epilogue of
+        // block st, whose MFMAs the previous stage issued, so matrix-core and
+        // VALU work overlap.  (The empty asm pins each epilogue to its stage:
+        // otherwise it is sunk to where the sums are reduced, and every
+        // block's MFMA results stay live until then.)
+        f32x4 ca[2][2][4];   // [pipeline slot][row][head group]
+        float part[2][4];
+        {
+            const i32x8 kb = kload(0);
+            block_mfma(qa[0], kb, ca[0][0]);
+            block_mfma(qa[1], kb, ca[0][1]);
+        }
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    if (valid[r]) {
-                        const float v = score_block(qa[r], wq[r], kb);
-                        if ((st & 3) == (l >> 4)) keep[r] = v;
-                    }
-                }
+        for (int st = 0; st < PF_KT / 16; ++st) {
+            if (st + 1 < PF_KT / 16) {
+                const i32x8 kb = kload(st + 1);
+                block_mfma(qa[0], kb, ca[(st + 1) & 1][0]);
+                block_mfma(qa[1], kb, ca[(st + 1) & 1][1]);
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                part[r][st & 3] = block_epilogue(ca[st & 1][r], wq[r]);
+                asm volatile("" : "+v"(part[r][st & 3]));
             }
             if ((st & 3) == 3) {
-                // lane l now holds the score of key kbase + 16*(st-3) + l
+                // lane l: key kbase + 16*(st-3) + l
                 const int key = kbase + 16 * (st - 3) + l;
-                if (key < fill_end) {
-                    const float ks = key < comp_end ? kscale[16 * (st - 3) + l] : 0.f;
+                const float ks = key < comp_end ? kscale[16 * (st - 3) + l] : 0.f;
 #pragma unroll
-                    for (int r = 0; r < 2; ++r) {
-                        if (valid[r]) {
-                            const float v = key <= pos[r] && key < comp_end ? keep[r] * ks : -INFINITY;
-                            p.scores[(int64_t)(q0 + tb + 2 * wave + r) * p.ld + key] = v;
-                        }
-                    }
+                for (int r = 0; r < 2; ++r) {
+                    const float v = reduce_scatter4(part[r]);
+                    if (valid[r] && key < fill_end)
+                        p.scores[(int64_t)(q0 + tb + 2 * wave + r) * p.ld + key] =
+                            key <= pos[r] && key < comp_end ? v * ks : -INFINITY;
                 }
             }
+            // one pipeline stage per region: left free, the scheduler hoists
+            // every block's MFMAs to the front and runs out of registers
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
