@@ -48,23 +48,6 @@ __device__ __forceinline__ void load_query(const IndexerParams &p, int64_t t, bo
     }
 }
 
-// ReLU + weighted head sum of one 16-key column block, reduced over the four
-// lane groups; every lane returns the sum for key column (lane % 16).
-__device__ __forceinline__ float score_block(const i32x8 (&qa)[4], const float (&wq)[4][4],
-                                             const i32x8 &kb) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    float part = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        f32x4 c = mfma_f8_16x16x128(qa[m], kb, zero);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part = fmaf(wq[m][i], fmaxf(c[i], 0.f), part);
-    }
-    part += shfl_xor_f(part, 16);
-    part += shfl_xor_f(part, 32);
-    return part;
-}
-
 // The 16 head partials of one lane for one 16-key block: 4 MFMAs (one per
 // group of 16 heads), kept in separate accumulators so that they can be in
 // flight while the previous block's epilogue runs.
@@ -245,8 +228,9 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
 // ---------------------------------------------------------------------------
 // Decode variant: one workgroup = one query row x one chunk of keys; the 4
 // waves split the chunk and stream their keys straight from HBM into the B
-// operand registers (a key is used by a single query row, so staging it in
-// LDS would buy nothing).  Grid: x = query row, y = key chunk.
+// operand registers, one 64-key group ahead (a key is used by a single query
+// row, so staging it in LDS would buy nothing).  Grid: x = query row, y = key
+// chunk.
 // ---------------------------------------------------------------------------
 constexpr int DC_WAVES = 4;
 
@@ -265,33 +249,47 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
     float wq[4][4];
     load_query(p, t, true, qa, wq);
 
-    // each wave owns 64-key groups wave, wave + 4, ... of the chunk
+    // Wave w takes the 64-key groups w, w+4, ... of the chunk; the keys of
+    // the next group are loaded (straight from HBM into B operands) before
+    // the current group is computed.
     const int row = l & 15, grp = l >> 4;
-    for (int g0 = c0 + 64 * wave; g0 < fill_end; g0 += 64 * DC_WAVES) {
-        i32x8 kb[4];
+    auto kload = [&](int g0, i32x8 (&kb)[4], float &ks) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int key = g0 + 16 * st + row;
-            if (key < comp_end) {
-                const i32x4 *s4 = reinterpret_cast<const i32x4 *>(p.k + (ri.kv0 + key) * DI + 32 * grp);
-                const i32x4 lo = s4[0], hi = s4[1];
-                kb[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            } else {
-                kb[st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
+            const bool in = key < comp_end;
+            const i32x4 *s4 = reinterpret_cast<const i32x4 *>(p.k + (ri.kv0 + (in ? key : c0)) * DI + 32 * grp);
+            const i32x4 lo = s4[0], hi = s4[1];
+            kb[st] = in ? i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}
+                        : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
         const int key = g0 + l;
-        const float ks = key < comp_end ? p.k_scale[ri.kv0 + key] : 0.f;
-        float keep = 0.f;
-        if (g0 < comp_end) {
+        ks = key < comp_end ? p.k_scale[ri.kv0 + key] : 0.f;
+    };
+    auto compute = [&](int g0, const i32x8 (&kb)[4], float ks) {
+        float part[4];
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const float v = score_block(qa, wq, kb[st]);
-                if (st == grp) keep = v;
-            }
+        for (int st = 0; st < 4; ++st) {
+            f32x4 c[4];
+            block_mfma(qa, kb[st], c);
+            part[st] = block_epilogue(c, wq);
         }
-        if (key < fill_end)
-            p.scores[(int64_t)t * p.ld + key] = key < comp_end ? keep * ks : -INFINITY;
+        const float v = reduce_scatter4(part);
+        const int key = g0 + l;
+        if (key < fill_end) p.scores[(int64_t)t * p.ld + key] = key < comp_end ? v * ks : -INFINITY;
+    };
+    constexpr int STRIDE = 64 * DC_WAVES;
+    i32x8 kA[4], kB[4];
+    float sA = 0.f, sB = 0.f;
+    int g0 = c0 + 64 * wave;
+    if (g0 < fill_end) kload(g0, kA, sA);
+    // unrolled by two so that both key buffers stay in registers
+    for (; g0 < fill_end; g0 += 2 * STRIDE) {
+        if (g0 + STRIDE < fill_end) kload(g0 + STRIDE, kB, sB);
+        compute(g0, kA, sA);
+        if (g0 + STRIDE >= fill_end) break;
+        if (g0 + 2 * STRIDE < fill_end) kload(g0 + 2 * STRIDE, kA, sA);
+        compute(g0 + STRIDE, kB, sB);
     }
 }
 
