@@ -66,37 +66,28 @@ typedef DSA_LDS uint8_t lds_u8;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
-__device__ __forceinline__ int64_t clamp_row(int s, int ctx) {
-    return (s >= 0 && s < ctx) ? s : 0;   // unusable slots load row 0 (masked later)
-}
-
 // Issues the 9 direct-to-LDS loads of one block for this wave.  Wave w loads
 // rows 8w..8w+7 (dims 0..511: one 1 KB load per row) and their rope slab
 // (dims 512..575, 8 rows x 128 B): inside a slab, logical 16-byte chunk c of
 // row rr sits at chunk position c ^ rr, so that a column of 8 rows read
-// together lands on distinct banks.  Slot positions come from the row's index
-// slice staged in LDS (sel, padded with -1 up to a whole block): a wave-
-// uniform LDS read is a short wait, where a scalar load of fresh index data
-// would wait on L2 every block.
-__device__ __forceinline__ void gather_block(const uint16_t *kv, const DSA_LDS int32_t *sel, int blk,
-                                             int64_t kv0, int ctx, lds_u8 *buf, int l) {
+// together lands on distinct banks.  Row positions come from the row's index
+// slice staged in LDS, already clamped to [0, ctx) (unusable slots hold row 0
+// and are masked later): a wave-uniform LDS read is a short wait, where a
+// scalar load of fresh index data would wait on L2 every block, and each load
+// address is then a single multiply-add on the lane's base pointer.
+__device__ __forceinline__ void gather_block(const uint8_t *lane_row, const uint8_t *lane_slab,
+                                             const DSA_LDS int32_t *sel, int blk, lds_u8 *buf, int l) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const DSA_LDS int32_t *s8p = sel + blk * BK + 8 * wave;
     const i32x4 a = *reinterpret_cast<const DSA_LDS i32x4 *>(s8p);
     const i32x4 b = *reinterpret_cast<const DSA_LDS i32x4 *>(s8p + 4);
-    const int rr = l >> 3;   // row inside the slab
-    const int sr = s8p[rr];
-    const int s8[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    const uint8_t *base = reinterpret_cast<const uint8_t *>(kv) + kv0 * ROWB;
+    const uint32_t sr = (uint32_t)s8p[l >> 3];
+    const uint32_t s8[8] = {(uint32_t)a[0], (uint32_t)a[1], (uint32_t)a[2], (uint32_t)a[3],
+                            (uint32_t)b[0], (uint32_t)b[1], (uint32_t)b[2], (uint32_t)b[3]};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 8 * wave + i;
-        const int64_t s = clamp_row(s8[i], ctx);
-        __builtin_amdgcn_global_load_lds(base + s * ROWB + 16 * l, buf + r * PA, 16, 0, 0);
-    }
-    const int64_t s = clamp_row(sr, ctx);
-    __builtin_amdgcn_global_load_lds(base + s * ROWB + 1024 + 16 * ((l & 7) ^ rr),
-                                     buf + RB + wave * 1024, 16, 0, 0);
+    for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_global_load_lds(lane_row + (uint64_t)s8[i] * ROWB, buf + (8 * wave + i) * PA, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(lane_slab + (uint64_t)sr * ROWB, buf + RB + wave * 1024, 16, 0, 0);
 }
 
 }  // namespace
@@ -156,8 +147,12 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
         for (int ks = 0; ks < KSTEPS; ++ks)
             qb[ht][ks] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
     }
-    // the slice's slot positions, padded with -1 (row 0, masked) to whole blocks
-    for (int j = threadIdx.x; j < nblk * BK; j += NTHREADS) sel[j] = j < nsel ? idx_row[j] : -1;
+    // the slice's slot positions, clamped to [0, ctx) and padded to whole
+    // blocks (unusable slots load row 0; the masks below exclude them)
+    for (int j = threadIdx.x; j < nblk * BK; j += NTHREADS) {
+        const int v = j < nsel ? idx_row[j] : -1;
+        sel[j] = (v >= 0 && v < ri.ctx) ? v : 0;
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query operands resident before the pipeline
     __syncthreads();
 
@@ -166,7 +161,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     uint32_t maskv = 0;
     for (int it = 0; it * kWave < nsel; ++it) {
         const int j = it * kWave + l;
-        const bool ok = j < nsel && (uint32_t)sel[j < nsel ? j : 0] < (uint32_t)ri.ctx;
+        const bool ok = j < nsel && (uint32_t)idx_row[j < nsel ? j : 0] < (uint32_t)ri.ctx;
         const uint64_t m = __ballot(ok);
         maskv = l == 2 * it ? (uint32_t)m : (l == 2 * it + 1 ? (uint32_t)(m >> 32) : maskv);
     }
@@ -180,6 +175,11 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     const int vA = (4 * grp + (row16 >> 2)) * PA + 8 * (row16 & 3);    // V^T transpose reads
 
     const DSA_LDS int32_t *lsel = (const DSA_LDS int32_t *)sel;
+    // per-lane source bases of the gather: dims 0..511 (16 bytes per lane)
+    // and the lane's rope chunk of its slab row
+    const uint8_t *kvb = reinterpret_cast<const uint8_t *>(p.kv) + ri.kv0 * ROWB;
+    const uint8_t *lane_row = kvb + 16 * l;
+    const uint8_t *lane_slab = kvb + 1024 + 16 * ((l & 7) ^ (l >> 3));
     lds_u8 *lb0 = (lds_u8 *)buf0;
     lds_u8 *lb1 = (lds_u8 *)buf1;
     lds_u8 *lb2 = (lds_u8 *)buf2;
@@ -201,8 +201,8 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
 
         // Pipeline: at the top of step b, vmcnt(9) leaves only this wave's 9
         // loads of block b+1 in flight, so block b has landed.
-        if (nblk > 0) gather_block(p.kv, lsel, 0, ri.kv0, ri.ctx, lb0, l);
-        if (nblk > 1) gather_block(p.kv, lsel, 1, ri.kv0, ri.ctx, lb1, l);
+        if (nblk > 0) gather_block(lane_row, lane_slab, lsel, 0, lb0, l);
+        if (nblk > 1) gather_block(lane_row, lane_slab, lsel, 1, lb1, l);
 
         // One block step: cur = buffer of block blk, nxt2 = buffer for blk+2
         // (the one block blk-1 used).  `cur` and `nxt2` are distinct LDS arrays
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
             // the loop they would cost registers the operands need.
             const int z = blk >> 30;
             const int lz = lane_id() + z;
-            if (blk + 2 < nblk) gather_block(p.kv, lsel, blk + 2, ri.kv0, ri.ctx, nxt2, lz);
+            if (blk + 2 < nblk) gather_block(lane_row, lane_slab, lsel, blk + 2, nxt2, lz);
             const uint32_t vmask = __builtin_amdgcn_readlane(maskv, blk);
 
             // ---- S^T: MT key tiles x NHT head tiles, lane = (head row16, keys 4*grp+i)
