@@ -10,29 +10,33 @@
 //
 // One workgroup serves one query row (or one split of its selected set) for
 // all 128 heads, so every gathered 1152-byte latent row feeds 128 heads (the
-// MQA property that keeps the gather coalesced).  4 waves x 32 heads, one
-// wave per SIMD: a wave's query operands (144 VGPRs) and O accumulators (256
-// AGPRs) stay in registers for the whole row, and every K or V operand read
-// from LDS feeds two 16-head MFMA tiles.
+// MQA property that keeps the gather coalesced).  8 waves, two per SIMD, so
+// that the hardware overlaps one wave's softmax, gather issue and barrier
+// waits with the other wave's matrix-core work.  For QK and the softmax a wave
+// owns 16 heads (its query operands, 72 VGPRs, stay in registers for the whole
+// row).  For PV a wave owns 64 of the 512 value columns of all 128 heads (128
+// accumulator registers): the probabilities go through LDS, and every V
+// operand read from LDS feeds eight head tiles.
 //
 // Per 32-key block:
 //   gather  : the 32 selected rows -> LDS with direct-to-LDS 16-byte loads
 //             into one of three buffers, two blocks ahead; dims 0..511 of a
-//             row are one 1 KB load (row index from a scalar load), the 64
-//             rope dims of 8 rows share one XOR-swizzled 1 KB slab;
+//             row are one 1 KB load, the 64 rope dims of 8 rows share one
+//             XOR-swizzled 1 KB slab;
 //   S^T     : z^T[key, head] = K Q^T on the 16x16x32 bf16 MFMA; A = K rows
 //             from LDS, B = query heads (registers, loaded once);
 //   softmax : exp2 domain against a per-head reference max fixed at the
 //             first block with a usable key;
-//   PV      : O^T[c, head] += V^T P^T; B = P^T straight from the S^T
-//             accumulators (their C layout already puts one head per lane),
-//             A = V^T read with the LDS transpose load.
-// The loop never touches O except through MFMAs (no online rescale), which is
-// what lets O live in AGPRs.  Exactness: p = 2^(z - m_ref) is bounded by 2^64
-// as long as no later logit exceeds the reference by more than 64 (log2
-// units); a block that does sets a restart flag, and the row is recomputed
-// with the row's true maximum as the reference (tracked during the first
-// pass), which cannot overflow.
+//   P       : each wave writes its heads' probabilities (bf16) to LDS in the
+//             B-operand layout of the PV MFMA (the S^T accumulator layout
+//             already puts one head per lane), then every wave reads all 128;
+//   PV      : O^T[c, head] += V^T P^T for the wave's value columns; A = V^T
+//             read with the LDS transpose load.
+// The loop never touches O except through MFMAs (no online rescale).
+// Exactness: p = 2^(z - m_ref) is bounded by 2^64 as long as no later logit
+// exceeds the reference by more than 64 (log2 units); a block that does sets
+// a restart flag, and the row is recomputed with the row's true maximum as the
+// reference (tracked during the first pass), which cannot overflow.
 // Split-KV (few query rows): each split writes a normalised partial and its
 // lse; mla_merge_kernel combines them.
 #include "dsa_device.h"
@@ -50,52 +54,66 @@ constexpr int BK = MLA_BK;               // 32 keys per block
 constexpr int PA = 1056;                 // LDS pitch of the dims 0..511 part (1 KB + 32 B)
 constexpr int RB = BK * PA;              // start of the rope slabs (8 rows x 128 B each)
 constexpr int BUF_BYTES = RB + BK * 128; // 37888
-constexpr int NWAVES = 4;                // 4 head groups of 32 heads
+constexpr int NWAVES = 8;                // 8 head groups of 16 heads
 constexpr int NTHREADS = NWAVES * kWave;
-constexpr int NHT = 2;                   // 16-head MFMA tiles per wave
+constexpr int NHT = 1;                   // 16-head MFMA tiles per wave
 constexpr int KSTEPS = D / 32;           // 18 k-steps (16 latent + 2 rope)
 constexpr int MT = BK / 16;              // 16-key tiles per block
 constexpr int CTILES = DV / 16;          // 32 value tiles
+constexpr int CT_W = CTILES / NWAVES;    // 4 value tiles per wave in PV
+constexpr int HT_ALL = H / 16;           // 8 head tiles
+constexpr int PP = 80;                   // LDS pitch of one head's 32 probabilities (64 B + 16)
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float MAX_RISE = 64.f;         // log2 headroom above the reference max
 constexpr int MAX_SEL = 2048;            // largest k (slots staged in LDS)
 
-static_assert(BK == 32 && NWAVES * 8 == BK, "each wave loads 8 rows and one rope slab");
+static_assert(BK == 32 && NWAVES * 4 == BK, "each wave loads 4 rows; waves 0..3 load the rope slabs");
 
 typedef DSA_LDS uint8_t lds_u8;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
-// Issues the 9 direct-to-LDS loads of one block for this wave.  Wave w loads
-// rows 8w..8w+7 (dims 0..511: one 1 KB load per row) and their rope slab
-// (dims 512..575, 8 rows x 128 B): inside a slab, logical 16-byte chunk c of
-// row rr sits at chunk position c ^ rr, so that a column of 8 rows read
-// together lands on distinct banks.  Row positions come from the row's index
-// slice staged in LDS, already clamped to [0, ctx) (unusable slots hold row 0
-// and are masked later): a wave-uniform LDS read is a short wait, where a
-// scalar load of fresh index data would wait on L2 every block, and each load
-// address is then a single multiply-add on the lane's base pointer.
+// One 16-byte-per-lane direct-to-LDS load: LDS destination lds + 16 * lane.
+// Issued from asm, so the compiler's wait insertion does not track it (it
+// cannot tell which LDS buffer the load writes and would fence later LDS reads
+// of unrelated buffers with a wait for it); the kernel waits for these loads
+// explicitly with vmcnt at the top of each step (no other vector-memory load
+// is issued inside the block loop).  M0 must be written one instruction ahead
+// of the load.
+__device__ __forceinline__ void dma16(const void *src, const DSA_LDS void *lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+                 : "m0");
+}
+
+// The direct-to-LDS loads of one block for this wave: wave w loads rows
+// 4w..4w+3 (dims 0..511: one 1 KB load per row); waves 0..3 also load rope
+// slab w (dims 512..575 of rows 8w..8w+7, 8 x 128 B), in which logical
+// 16-byte chunk c of row rr sits at chunk position c ^ rr, so that a column of
+// 8 rows read together lands on distinct banks.  Row positions come from the
+// row's index slice staged in LDS, already clamped to [0, ctx) (unusable slots
+// hold row 0 and are masked later): a wave-uniform LDS read is a short wait,
+// where a scalar load of fresh index data would wait on L2 every block, and
+// each load address is then a single multiply-add on the lane's base pointer.
 __device__ __forceinline__ void gather_block(const uint8_t *lane_row, const uint8_t *lane_slab,
                                              const DSA_LDS int32_t *sel, int blk, lds_u8 *buf, int l) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const DSA_LDS int32_t *s8p = sel + blk * BK + 8 * wave;
-    const i32x4 a = *reinterpret_cast<const DSA_LDS i32x4 *>(s8p);
-    const i32x4 b = *reinterpret_cast<const DSA_LDS i32x4 *>(s8p + 4);
-    const uint32_t sr = (uint32_t)s8p[l >> 3];
-    const uint32_t s8[8] = {(uint32_t)a[0], (uint32_t)a[1], (uint32_t)a[2], (uint32_t)a[3],
-                            (uint32_t)b[0], (uint32_t)b[1], (uint32_t)b[2], (uint32_t)b[3]};
+    const DSA_LDS int32_t *s4p = sel + blk * BK + 4 * wave;
+    const i32x4 a = *reinterpret_cast<const DSA_LDS i32x4 *>(s4p);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        __builtin_amdgcn_global_load_lds(lane_row + (uint64_t)s8[i] * ROWB, buf + (8 * wave + i) * PA, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(lane_slab + (uint64_t)sr * ROWB, buf + RB + wave * 1024, 16, 0, 0);
+    for (int i = 0; i < 4; ++i) dma16(lane_row + (uint64_t)(uint32_t)a[i] * ROWB, buf + (4 * wave + i) * PA);
+    if (wave < 4) {
+        const uint32_t sr = (uint32_t)sel[blk * BK + 8 * wave + (l >> 3)];
+        dma16(lane_slab + (uint64_t)sr * ROWB, buf + RB + wave * 1024);
+    }
 }
 
 }  // namespace
 
 // S^T accumulators live in VGPRs: the QK MFMAs are written as inline asm with
-// VGPR operands, because the compiler would otherwise place them in AGPRs,
-// which the 256 O accumulators already fill (it then moves O registers out and
-// back around every block).  The compiler does not know these are MFMAs, so
+// VGPR operands, which keeps the compiler from placing them in the accumulator
+// registers the O tiles use (it then moves O registers out and back around
+// every block).  The compiler does not know these are MFMAs, so
 // the wait states an MFMA result needs before a VALU instruction reads it are
 // inserted explicitly (qk_drain: 24, more than any 16x16 MFMA requires), and
 // the first k-step takes an inline zero accumulator instead of a VALU-written
@@ -108,11 +126,11 @@ __device__ __forceinline__ void qk_next(f32x4 &d, const bf16x8 &a, const bf16x8 
     asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void qk_drain(f32x4 (&s)[NHT][MT]) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0][0]), "+v"(s[0][1]));
 }
 
-// Grid: x = query row, y = split.  LDS: three gather buffers + restart flags.
+// Grid: x = query row, y = split.  LDS: three gather buffers, the index slice,
+// the probabilities of one block, per-head sums and restart flags.
 // The index array and every output are separate restrict-qualified arguments
 // (no store of the kernel can clobber idx).
 __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
@@ -122,6 +140,8 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t buf2[BUF_BYTES];
     __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
+    __shared__ __attribute__((aligned(16))) uint8_t plds[H * PP];
+    __shared__ float lsh[H];
     __shared__ int restart_flag[NWAVES];
 
     const int t = blockIdx.x, split = blockIdx.y;
@@ -138,7 +158,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     const int nblk = (nsel + BK - 1) / BK;
 
     // query operands: lane holds head h0 + 16*ht + row16, dims 32*ks + 8*grp .. +7
-    const int h0 = wave * 32;
+    const int h0 = wave * 16;
     bf16x8 qb[NHT][KSTEPS];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
@@ -184,7 +204,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     lds_u8 *lb1 = (lds_u8 *)buf1;
     lds_u8 *lb2 = (lds_u8 *)buf2;
 
-    f32x4 o[NHT][CTILES];
+    f32x4 o[HT_ALL][CT_W];   // O^T tiles: all heads x this wave's value columns
     float m_run[NHT], l_run[NHT], m_seen[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) m_seen[ht] = -INFINITY;
@@ -192,11 +212,13 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
-#pragma unroll
-            for (int c = 0; c < CTILES; ++c) o[ht][c] = f32x4{0.f, 0.f, 0.f, 0.f};
             m_run[ht] = pass == 0 ? -INFINITY : m_seen[ht];
             l_run[ht] = 0.f;
         }
+#pragma unroll
+        for (int ht = 0; ht < HT_ALL; ++ht)
+#pragma unroll
+            for (int c = 0; c < CT_W; ++c) o[ht][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         bool restart = false;
 
         // Pipeline: at the top of step b, vmcnt(9) leaves only this wave's 9
@@ -210,10 +232,14 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
         // compiler see that reads of `cur` do not wait for the loads landing
         // elsewhere.
         auto step = [&](int blk, lds_u8 *cur, lds_u8 *nxt2) {
-            if (blk + 1 < nblk)
-                __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
-            else
+            if (blk + 1 < nblk) {
+                if (wave < 4)
+                    __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+                else
+                    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+            } else {
                 __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            }
             // LDS-only barrier: every wave's part of block blk has landed and
             // every wave is done reading block blk-1's buffer
             lds_barrier();
@@ -303,31 +329,38 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
                                 (__bf16)pv[4], (__bf16)pv[5], (__bf16)pv[6], (__bf16)pv[7]};
             }
 
-            // ---- O^T += V^T P^T.  A = V^T via transpose reads: 16-lane group
-            // grp reads rows (keys) 4*grp + r and 16 + 4*grp + r; lane row16 of
-            // the group addresses row row16/4, columns 16*ct + 4*(row16%4) .. +3.
-            // Each A operand feeds NHT MFMAs.
-            // V^T operands are loaded PV_AHEAD c-tiles ahead of their MFMAs.
-            constexpr int PV_AHEAD = 3;
-            const int vAz = vA + z;
-            i16x4 vbuf[PV_AHEAD + 1][2];
+            // ---- P to LDS: head h0 + 16*ht + row16, probabilities of the
+            // permuted key order 8*grp .. 8*grp+7 (keys 4*grp+i and 16+4*grp+i)
+            lds_u8 *pl = (lds_u8 *)plds;
 #pragma unroll
-            for (int ct = 0; ct < PV_AHEAD; ++ct) {
-                vbuf[ct][0] = lds_read_tr16(cur + vAz + 32 * ct);
-                vbuf[ct][1] = lds_read_tr16(cur + vAz + 16 * PA + 32 * ct);
-            }
+            for (int ht = 0; ht < NHT; ++ht)
+                *reinterpret_cast<DSA_LDS bf16x8 *>(pl + (h0 + 16 * ht + row16) * PP + 16 * grp) = pb[ht];
+            lds_barrier();   // every wave's probabilities are in place
+            // ---- O^T += V^T P^T over this wave's value columns.  A = V^T via
+            // transpose reads (all CT_W tiles, read once): 16-lane group grp
+            // reads rows (keys) 4*grp + r and 16 + 4*grp + r; lane row16 of the
+            // group addresses row row16/4, columns 16*ct + 4*(row16%4) .. +3.
+            // B = P^T of head tile T, read from LDS one tile ahead; each B
+            // operand feeds CT_W MFMAs.
+            const int vAz = vA + z + 32 * CT_W * wave;
+            bf16x8 va[CT_W];
 #pragma unroll
-            for (int ct = 0; ct < CTILES; ++ct) {
-                if (ct + PV_AHEAD < CTILES) {
-                    vbuf[(ct + PV_AHEAD) % (PV_AHEAD + 1)][0] = lds_read_tr16(cur + vAz + 32 * (ct + PV_AHEAD));
-                    vbuf[(ct + PV_AHEAD) % (PV_AHEAD + 1)][1] =
-                        lds_read_tr16(cur + vAz + 16 * PA + 32 * (ct + PV_AHEAD));
-                }
-                const i16x4 lo = vbuf[ct % (PV_AHEAD + 1)][0], hi = vbuf[ct % (PV_AHEAD + 1)][1];
+            for (int ct = 0; ct < CT_W; ++ct) {
+                const i16x4 lo = lds_read_tr16(cur + vAz + 32 * ct);
+                const i16x4 hi = lds_read_tr16(cur + vAz + 16 * PA + 32 * ct);
                 const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+                va[ct] = __builtin_bit_cast(bf16x8, a8);
+            }
+            auto p_op = [&](int T) {
+                return *reinterpret_cast<const DSA_LDS bf16x8 *>(pl + (16 * T + row16) * PP + 16 * grp);
+            };
+            bf16x8 pt[2];
+            pt[0] = p_op(0);
 #pragma unroll
-                for (int ht = 0; ht < NHT; ++ht) o[ht][ct] = mfma_bf16_16x16x32(a, pb[ht], o[ht][ct]);
+            for (int T = 0; T < HT_ALL; ++T) {
+                if (T + 1 < HT_ALL) pt[(T + 1) & 1] = p_op(T + 1);
+#pragma unroll
+                for (int ct = 0; ct < CT_W; ++ct) o[T][ct] = mfma_bf16_16x16x32(va[ct], pt[T & 1], o[T][ct]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -355,31 +388,42 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
         if (!again) break;
     }
 
-    // ---- finish: full sum per head, normalise, write
+    // ---- finish: the owner of each head reduces its sum and writes its lse;
+    // every wave then normalises its value columns of all heads
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
         float l_tot = l_run[ht] + xor16_f(l_run[ht]);
         l_tot += shfl_xor_f(l_tot, 32);
         const int h = h0 + 16 * ht + row16;
         const bool empty = !(l_tot > 0.f);
-        const float inv = empty ? 0.f : 1.f / l_tot;
         const float lse_v = empty ? -INFINITY : (m_run[ht] + log2f(l_tot)) * LN2;
-        const int c0 = 4 * grp;
+        if (grp == 0) {
+            lsh[h] = l_tot;
+            if (p.splits == 1)
+                lse[(int64_t)t * H + h] = lse_v;
+            else
+                lse_part[((int64_t)t * p.splits + split) * H + h] = lse_v;
+        }
+    }
+    __syncthreads();
+    const int c0 = CT_W * 16 * wave + 4 * grp;
+#pragma unroll
+    for (int T = 0; T < HT_ALL; ++T) {
+        const int h = 16 * T + row16;
+        const float l_tot = lsh[h];
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         if (p.splits == 1) {
             uint16_t *orow = out + ((int64_t)t * H + h) * DV + c0;
 #pragma unroll
-            for (int ct = 0; ct < CTILES; ++ct) {
-                const bf16x4 v = {(__bf16)(o[ht][ct][0] * inv), (__bf16)(o[ht][ct][1] * inv),
-                                  (__bf16)(o[ht][ct][2] * inv), (__bf16)(o[ht][ct][3] * inv)};
+            for (int ct = 0; ct < CT_W; ++ct) {
+                const bf16x4 v = {(__bf16)(o[T][ct][0] * inv), (__bf16)(o[T][ct][1] * inv),
+                                  (__bf16)(o[T][ct][2] * inv), (__bf16)(o[T][ct][3] * inv)};
                 *reinterpret_cast<bf16x4 *>(orow + 16 * ct) = v;
             }
-            if (grp == 0) lse[(int64_t)t * H + h] = lse_v;
         } else {
             float *orow = o_part + (((int64_t)t * p.splits + split) * H + h) * DV + c0;
 #pragma unroll
-            for (int ct = 0; ct < CTILES; ++ct)
-                *reinterpret_cast<f32x4 *>(orow + 16 * ct) = o[ht][ct] * inv;
-            if (grp == 0) lse_part[((int64_t)t * p.splits + split) * H + h] = lse_v;
+            for (int ct = 0; ct < CT_W; ++ct) *reinterpret_cast<f32x4 *>(orow + 16 * ct) = o[T][ct] * inv;
         }
     }
 }
