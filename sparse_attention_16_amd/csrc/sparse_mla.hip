@@ -140,7 +140,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t buf2[BUF_BYTES];
     __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
-    __shared__ __attribute__((aligned(16))) uint8_t plds[H * PP];
+    __shared__ __attribute__((aligned(16))) uint8_t plds[2][H * PP];   // by block parity
     __shared__ float lsh[H];
     __shared__ int restart_flag[NWAVES];
 
@@ -221,18 +221,12 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
             for (int c = 0; c < CT_W; ++c) o[ht][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         bool restart = false;
 
-        // Pipeline: at the top of step b, vmcnt(9) leaves only this wave's 9
-        // loads of block b+1 in flight, so block b has landed.
+        // Pipeline: blocks 0 and 1 are loaded here; block b+2 is loaded during
+        // step b, after the step's barrier.
         if (nblk > 0) gather_block(lane_row, lane_slab, lsel, 0, lb0, l);
         if (nblk > 1) gather_block(lane_row, lane_slab, lsel, 1, lb1, l);
-
-        // One block step: cur = buffer of block blk, nxt2 = buffer for blk+2
-        // (the one block blk-1 used).  `cur` and `nxt2` are distinct LDS arrays
-        // at compile time (the loop is unrolled by three), which lets the
-        // compiler see that reads of `cur` do not wait for the loads landing
-        // elsewhere.
-        auto step = [&](int blk, lds_u8 *cur, lds_u8 *nxt2) {
-            if (blk + 1 < nblk) {
+        if (nblk > 0) {   // block 0 landed and visible to every wave
+            if (nblk > 1) {
                 if (wave < 4)
                     __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
                 else
@@ -240,15 +234,27 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
             } else {
                 __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             }
-            // LDS-only barrier: every wave's part of block blk has landed and
-            // every wave is done reading block blk-1's buffer
             lds_barrier();
+        }
+
+        // One block step: cur = buffer of block blk, nxt2 = buffer for blk+2
+        // (the one block blk-1 used).  `cur` and `nxt2` are distinct LDS arrays
+        // at compile time (the loop is unrolled by three), which lets the
+        // compiler see that reads of `cur` do not wait for the loads landing
+        // elsewhere.
+        // One barrier per block, between the probability write and the PV:
+        // before it each wave waits for its own loads of block blk+1 (issued
+        // a step earlier), so after it block blk+1 is visible to every wave,
+        // every wave's probabilities of block blk are in place and every wave
+        // is done with block blk-1's buffer, which then receives block blk+2.
+        // The probabilities are double-buffered by block parity: a wave may
+        // write block blk+1's while another still reads block blk's.
+        auto step = [&](int blk, lds_u8 *cur, lds_u8 *nxt2) {
             // Lane-derived values are rebuilt inside the step from an opaque
             // zero (blk >> 30 == 0 for every real block count): hoisted out of
             // the loop they would cost registers the operands need.
             const int z = blk >> 30;
             const int lz = lane_id() + z;
-            if (blk + 2 < nblk) gather_block(lane_row, lane_slab, lsel, blk + 2, nxt2, lz);
             const uint32_t vmask = __builtin_amdgcn_readlane(maskv, blk);
 
             // ---- S^T: MT key tiles x NHT head tiles, lane = (head row16, keys 4*grp+i)
@@ -331,11 +337,13 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
 
             // ---- P to LDS: head h0 + 16*ht + row16, probabilities of the
             // permuted key order 8*grp .. 8*grp+7 (keys 4*grp+i and 16+4*grp+i)
-            lds_u8 *pl = (lds_u8 *)plds;
+            lds_u8 *pl = (lds_u8 *)plds[blk & 1];
 #pragma unroll
             for (int ht = 0; ht < NHT; ++ht)
                 *reinterpret_cast<DSA_LDS bf16x8 *>(pl + (h0 + 16 * ht + row16) * PP + 16 * grp) = pb[ht];
-            lds_barrier();   // every wave's probabilities are in place
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block blk+1
+            lds_barrier();
+            if (blk + 2 < nblk) gather_block(lane_row, lane_slab, lsel, blk + 2, nxt2, lz);
             // ---- O^T += V^T P^T over this wave's value columns.  A = V^T via
             // transpose reads (all CT_W tiles, read once): 16-lane group grp
             // reads rows (keys) 4*grp + r and 16 + 4*grp + r; lane row16 of the
