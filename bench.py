@@ -50,10 +50,10 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     ("prefill_32k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "9f9b481a6919852e", "fetch_kib": 11637631, "write_kib": 4214704},
+        "sha256_16": "43ea6b7d2d7e0de9", "fetch_kib": 11415301, "write_kib": 4220696},
     ("decode_64k", "indexer_decode_kernel"): {
         "sources": ("indexer.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "c8aa8d564659d080", "fetch_kib": 289436, "write_kib": 17469},
+        "sha256_16": "824953ea7f23f2f0", "fetch_kib": 289457, "write_kib": 17469},
 }
 
 
