@@ -11,12 +11,13 @@
 // One workgroup serves one query row (or one split of its selected set) for
 // all 128 heads, so every gathered 1152-byte latent row feeds 128 heads (the
 // MQA property that keeps the gather coalesced).  8 waves, two per SIMD, so
-// that the hardware overlaps one wave's softmax, gather issue and barrier
-// waits with the other wave's matrix-core work.  For QK and the softmax a wave
-// owns 16 heads (its query operands, 72 VGPRs, stay in registers for the whole
-// row).  For PV a wave owns 64 of the 512 value columns of all 128 heads (128
-// accumulator registers): the probabilities go through LDS, and every V
-// operand read from LDS feeds eight head tiles.
+// that the hardware overlaps one wave's stalls with the other wave's
+// matrix-core work.  For QK and the softmax a wave owns 16 heads (the query
+// operands of the 512 latent dims, 64 VGPRs, stay in registers for the whole
+// row; those of the 64 rope dims sit in LDS).  For PV a wave owns 64 of the
+// 512 value columns of all 128 heads (128 accumulator registers): the
+// probabilities go through LDS, and every V operand read from LDS feeds eight
+// head tiles.
 //
 // Per 32-key block:
 //   gather  : the 32 selected rows -> LDS with direct-to-LDS 16-byte loads
@@ -24,7 +25,7 @@
 //             row are one 1 KB load, the 64 rope dims of 8 rows share one
 //             XOR-swizzled 1 KB slab;
 //   S^T     : z^T[key, head] = K Q^T on the 16x16x32 bf16 MFMA; A = K rows
-//             from LDS, B = query heads (registers, loaded once);
+//             from LDS, B = query heads;
 //   softmax : exp2 domain against a per-head reference max fixed at the
 //             first block with a usable key;
 //   P       : each wave writes its heads' probabilities (bf16) to LDS in the
@@ -32,11 +33,16 @@
 //             already puts one head per lane), then every wave reads all 128;
 //   PV      : O^T[c, head] += V^T P^T for the wave's value columns; A = V^T
 //             read with the LDS transpose load.
+// Between two barriers a wave runs S^T of block b+1 (with the loads of block
+// b+2 spread over its k-steps, so that the 36 KB of loads of all waves do not
+// queue up at once), then the PV of block b with block b+1's softmax stages
+// placed between its MFMAs (the matrix cores and the VALU run side by side).
 // The loop never touches O except through MFMAs (no online rescale).
 // Exactness: p = 2^(z - m_ref) is bounded by 2^64 as long as no later logit
-// exceeds the reference by more than 64 (log2 units); a block that does sets
-// a restart flag, and the row is recomputed with the row's true maximum as the
-// reference (tracked during the first pass), which cannot overflow.
+// exceeds the reference by more than 64 (log2 units).  Each lane tracks its
+// largest rise above the reference; if any exceeds 64 at the end of the pass,
+// the row is recomputed with the row's true maximum as the reference (tracked
+// during the first pass), which cannot overflow.
 // Split-KV (few query rows): each split writes a normalised partial and its
 // lse; mla_merge_kernel combines them.
 #include "dsa_device.h"
@@ -73,39 +79,55 @@ typedef DSA_LDS uint8_t lds_u8;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
-// One 16-byte-per-lane direct-to-LDS load: LDS destination lds + 16 * lane.
-// Issued from asm, so the compiler's wait insertion does not track it (it
-// cannot tell which LDS buffer the load writes and would fence later LDS reads
-// of unrelated buffers with a wait for it); the kernel waits for these loads
-// explicitly with vmcnt at the top of each step (no other vector-memory load
-// is issued inside the block loop).  M0 must be written one instruction ahead
-// of the load.
-__device__ __forceinline__ void dma16(const void *src, const DSA_LDS void *lds) {
+// One 16-byte-per-lane direct-to-LDS load from sbase + voff (a scalar base
+// and a 32-bit per-lane offset) to LDS lds + 16 * lane.  Issued from asm, so
+// the compiler's wait insertion does not track it (it cannot tell which LDS
+// buffer the load writes and would fence later LDS reads of unrelated buffers
+// with a wait for it); the kernel waits for these loads explicitly with vmcnt
+// before each barrier (no other vector-memory load is issued inside the block
+// loop).  M0 must be written one instruction ahead of the load.
+__device__ __forceinline__ void dma16s(uint64_t sbase, uint32_t voff, const DSA_LDS void *lds) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                  : "m0");
 }
 
-// The direct-to-LDS loads of one block for this wave: wave w loads rows
-// 4w..4w+3 (dims 0..511: one 1 KB load per row); waves 0..3 also load rope
-// slab w (dims 512..575 of rows 8w..8w+7, 8 x 128 B), in which logical
-// 16-byte chunk c of row rr sits at chunk position c ^ rr, so that a column of
-// 8 rows read together lands on distinct banks.  Row positions come from the
-// row's index slice staged in LDS, already clamped to [0, ctx) (unusable slots
-// hold row 0 and are masked later): a wave-uniform LDS read is a short wait,
-// where a scalar load of fresh index data would wait on L2 every block, and
-// each load address is then a single multiply-add on the lane's base pointer.
-__device__ __forceinline__ void gather_block(const uint8_t *lane_row, const uint8_t *lane_slab,
-                                             const DSA_LDS int32_t *sel, int blk, lds_u8 *buf, int l) {
+// Maximum over the four 16-lane groups (lanes l, l^16, l^32, l^48) with two
+// VALU lane swaps: no LDS traffic and no exec-mask change.
+__device__ __forceinline__ float group4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// The loads of one block, split for interleaving with the MFMAs.
+// gather_slots reads the wave's four row positions (made scalar: each row is
+// one 1 KB load from a scalar base, the lane adding 16 * lane) and, for waves
+// 0..3, the lane's slab row; gather_issue(i) issues load i (rows 0..3, then
+// the slab).  kvb is the sequence's first latent row (wave-uniform).
+struct GatherSlots {
+    uint64_t base[4];   // row bases (scalar registers)
+    uint64_t kvb;
+    uint32_t soff;      // slab: this lane's byte offset from kvb
+};
+__device__ __forceinline__ GatherSlots gather_slots(const DSA_LDS int32_t *sel, int blk, int l, uint64_t kvb) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const DSA_LDS int32_t *s4p = sel + blk * BK + 4 * wave;
-    const i32x4 a = *reinterpret_cast<const DSA_LDS i32x4 *>(s4p);
+    GatherSlots g;
+    const i32x4 a = *reinterpret_cast<const DSA_LDS i32x4 *>(sel + blk * BK + 4 * wave);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(lane_row + (uint64_t)(uint32_t)a[i] * ROWB, buf + (4 * wave + i) * PA);
-    if (wave < 4) {
-        const uint32_t sr = (uint32_t)sel[blk * BK + 8 * wave + (l >> 3)];
-        dma16(lane_slab + (uint64_t)sr * ROWB, buf + RB + wave * 1024);
-    }
+    for (int i = 0; i < 4; ++i) g.base[i] = kvb + (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(a[i]) * ROWB;
+    const uint32_t sr = (uint32_t)sel[blk * BK + 8 * (wave & 3) + (l >> 3)];
+    g.soff = sr * ROWB + 1024 + 16 * ((l & 7) ^ (l >> 3));
+    g.kvb = kvb;
+    return g;
+}
+__device__ __forceinline__ void gather_issue(const GatherSlots &g, int i, int l, lds_u8 *buf) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (i < 4)
+        dma16s(g.base[i], 16 * l, buf + (4 * wave + i) * PA);
+    else if (wave < 4)
+        dma16s(g.kvb, g.soff, buf + RB + wave * 1024);
 }
 
 }  // namespace
@@ -129,8 +151,9 @@ __device__ __forceinline__ void qk_drain(f32x4 (&s)[NHT][MT]) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0][0]), "+v"(s[0][1]));
 }
 
-// Grid: x = query row, y = split.  LDS: three gather buffers, the index slice,
-// the probabilities of one block, per-head sums and restart flags.
+// Grid: x = query row, y = split.  LDS (156 KB): three gather buffers, the
+// index slice, the probabilities of two blocks, the rope query operands,
+// per-head sums and restart flags.
 // The index array and every output are separate restrict-qualified arguments
 // (no store of the kernel can clobber idx).
 __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
@@ -141,6 +164,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t buf2[BUF_BYTES];
     __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
     __shared__ __attribute__((aligned(16))) uint8_t plds[2][H * PP];   // by block parity
+    __shared__ __attribute__((aligned(16))) uint8_t qrope[NWAVES * 2 * 1024];  // rope operands, per wave
     __shared__ float lsh[H];
     __shared__ int restart_flag[NWAVES];
 
@@ -159,14 +183,20 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
 
     // query operands: lane holds head h0 + 16*ht + row16, dims 32*ks + 8*grp .. +7
     const int h0 = wave * 16;
-    bf16x8 qb[NHT][KSTEPS];
+    // (the two rope k-steps are kept in LDS, each wave reading back its own)
+    bf16x8 qb[NHT][16];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
         const uint16_t *qrow = p.q + ((int64_t)t * H + h0 + 16 * ht + row16) * D + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
+        for (int ks = 0; ks < 16; ++ks)
             qb[ht][ks] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
+#pragma unroll
+        for (int ks = 16; ks < KSTEPS; ++ks)
+            *reinterpret_cast<bf16x8 *>(qrope + (wave * 2 + ks - 16) * 1024 + 16 * l) =
+                *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
     }
+    const DSA_LDS uint8_t *lqr = (const DSA_LDS uint8_t *)qrope + wave * 2048 + 16 * l;
     // the slice's slot positions, clamped to [0, ctx) and padded to whole
     // blocks (unusable slots load row 0; the masks below exclude them)
     for (int j = threadIdx.x; j < nblk * BK; j += NTHREADS) {
@@ -197,15 +227,16 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     const DSA_LDS int32_t *lsel = (const DSA_LDS int32_t *)sel;
     // per-lane source bases of the gather: dims 0..511 (16 bytes per lane)
     // and the lane's rope chunk of its slab row
-    const uint8_t *kvb = reinterpret_cast<const uint8_t *>(p.kv) + ri.kv0 * ROWB;
-    const uint8_t *lane_row = kvb + 16 * l;
-    const uint8_t *lane_slab = kvb + 1024 + 16 * ((l & 7) ^ (l >> 3));
+    uint64_t kvb = (uint64_t)(uintptr_t)p.kv + (uint64_t)ri.kv0 * ROWB;
+    // (readfirstlane returns int: widen through uint32_t, or the low word is sign-extended)
+    kvb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(kvb >> 32)) << 32) |
+          (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)kvb);
     lds_u8 *lb0 = (lds_u8 *)buf0;
     lds_u8 *lb1 = (lds_u8 *)buf1;
     lds_u8 *lb2 = (lds_u8 *)buf2;
 
     f32x4 o[HT_ALL][CT_W];   // O^T tiles: all heads x this wave's value columns
-    float m_run[NHT], l_run[NHT], m_seen[NHT];
+    float m_run[NHT], l_run[NHT], m_seen[NHT], rise[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) m_seen[ht] = -INFINITY;
 
@@ -214,53 +245,21 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
         for (int ht = 0; ht < NHT; ++ht) {
             m_run[ht] = pass == 0 ? -INFINITY : m_seen[ht];
             l_run[ht] = 0.f;
+            rise[ht] = -INFINITY;
         }
 #pragma unroll
         for (int ht = 0; ht < HT_ALL; ++ht)
 #pragma unroll
             for (int c = 0; c < CT_W; ++c) o[ht][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bool restart = false;
 
-        // Pipeline: blocks 0 and 1 are loaded here; block b+2 is loaded during
-        // step b, after the step's barrier.
-        if (nblk > 0) gather_block(lane_row, lane_slab, lsel, 0, lb0, l);
-        if (nblk > 1) gather_block(lane_row, lane_slab, lsel, 1, lb1, l);
-        if (nblk > 0) {   // block 0 landed and visible to every wave
-            if (nblk > 1) {
-                if (wave < 4)
-                    __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
-                else
-                    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-            } else {
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-            }
-            lds_barrier();
-        }
-
-        // One block step: cur = buffer of block blk, nxt2 = buffer for blk+2
-        // (the one block blk-1 used).  `cur` and `nxt2` are distinct LDS arrays
-        // at compile time (the loop is unrolled by three), which lets the
-        // compiler see that reads of `cur` do not wait for the loads landing
-        // elsewhere.
-        // One barrier per block, between the probability write and the PV:
-        // before it each wave waits for its own loads of block blk+1 (issued
-        // a step earlier), so after it block blk+1 is visible to every wave,
-        // every wave's probabilities of block blk are in place and every wave
-        // is done with block blk-1's buffer, which then receives block blk+2.
-        // The probabilities are double-buffered by block parity: a wave may
-        // write block blk+1's while another still reads block blk's.
-        auto step = [&](int blk, lds_u8 *cur, lds_u8 *nxt2) {
-            // Lane-derived values are rebuilt inside the step from an opaque
-            // zero (blk >> 30 == 0 for every real block count): hoisted out of
-            // the loop they would cost registers the operands need.
+        // ---- S^T of block blk from buffer cur (lane = head row16, keys 4*grp+i)
+        // (gl: the loads of another block, issued one per DMA_EVERY k-steps
+        // so that they do not queue up behind each other)
+        constexpr int DMA_EVERY = 3;
+        auto qk_block = [&](int blk, const lds_u8 *cur, f32x4 (&sacc)[NHT][MT],
+                            const GatherSlots &gl, bool gon, lds_u8 *gbuf, int glz) {
             const int z = blk >> 30;
-            const int lz = lane_id() + z;
-            const uint32_t vmask = __builtin_amdgcn_readlane(maskv, blk);
-
-            // ---- S^T: MT key tiles x NHT head tiles, lane = (head row16, keys 4*grp+i)
-            f32x4 sacc[NHT][MT];
             // K operands are loaded QK_AHEAD k-steps ahead of their MFMAs
-            // (software pipeline; one wave per SIMD hides nothing by itself).
             constexpr int QK_AHEAD = 2;
             const int kAz = kA + z, kB16z = kB16 + z, kB17z = kB17 + z;
             auto k_off = [&](int ks, int mt) {
@@ -268,6 +267,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
                                : (ks == 16 ? kB16z : kB17z) + mt * 2048;
             };
             bf16x8 kbuf[QK_AHEAD + 1][MT];
+            bf16x8 qr[2];
 #pragma unroll
             for (int ks = 0; ks < QK_AHEAD; ++ks)
 #pragma unroll
@@ -275,11 +275,15 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
                     kbuf[ks][mt] = *reinterpret_cast<const DSA_LDS bf16x8 *>(cur + k_off(ks, mt));
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
+                if (ks % DMA_EVERY == 0 && ks / DMA_EVERY < 5 && gon) gather_issue(gl, ks / DMA_EVERY, glz, gbuf);
                 if (ks + QK_AHEAD < KSTEPS) {
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
                         kbuf[(ks + QK_AHEAD) % (QK_AHEAD + 1)][mt] = *reinterpret_cast<const DSA_LDS bf16x8 *>(
                             cur + k_off(ks + QK_AHEAD, mt));
+                    if (ks + QK_AHEAD >= 16)
+                        qr[ks + QK_AHEAD - 16] = *reinterpret_cast<const DSA_LDS bf16x8 *>(
+                            lqr + 1024 * (ks + QK_AHEAD - 16) + z);
                 }
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
@@ -288,13 +292,16 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
                         if (ks == 0)
                             qk_first(sacc[ht][mt], kbuf[0][mt], qb[ht][0]);
                         else
-                            qk_next(sacc[ht][mt], kbuf[ks % (QK_AHEAD + 1)][mt], qb[ht][ks]);
+                            qk_next(sacc[ht][mt], kbuf[ks % (QK_AHEAD + 1)][mt], ks < 16 ? qb[ht][ks] : qr[ks - 16]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-
             qk_drain(sacc);
-            // ---- softmax numerators against the reference max
-            if (vmask != 0xFFFFFFFFu) {
+        };
+
+        // ---- unusable slots of a block: logit -inf.  Only the last block of a
+        // row and rows with fewer usable slots than k take this branch.
+        auto mask_block = [&](uint32_t vmask, f32x4 (&sacc)[NHT][MT]) {
+            if (__builtin_expect(vmask != 0xFFFFFFFFu, 0)) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const uint32_t nib = (vmask >> (16 * mt + 4 * grp)) & 0xFu;
@@ -305,51 +312,117 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
                             if (!((nib >> i) & 1u)) sacc[ht][mt][i] = -INFINITY;
                 }
             }
-            bf16x8 pb[NHT];
+        };
+
+        // ---- softmax of one block in stages (so that each stage can sit
+        // between the MFMAs of another block's PV).  The head's reference is
+        // the maximum of its first usable block (all 4 lane groups); until
+        // then m_run is -inf and O, l are zero.  The running maximum and the
+        // rise above the reference are tracked per lane, checked once per pass.
+        float bz[NHT], neg_m[NHT], pv[NHT][8];
+        bf16x8 pb[NHT];
+        auto soft_stage = [&](int st, const f32x4 (&sacc)[NHT][MT], lds_u8 *pl) {
 #pragma unroll
             for (int ht = 0; ht < NHT; ++ht) {
-                // this lane's 8 logits of the head; the restart test and the
-                // running maximum work per lane (the head's 4 lane groups are
-                // combined once per pass), only the first usable block needs
-                // the head's block maximum across the groups
-                float bmax = fmaxf(fmaxf(fmaxf(sacc[ht][0][0], sacc[ht][0][1]),
-                                         fmaxf(sacc[ht][0][2], sacc[ht][0][3])),
-                                   fmaxf(fmaxf(sacc[ht][1][0], sacc[ht][1][1]),
-                                         fmaxf(sacc[ht][1][2], sacc[ht][1][3])));
-                const float bz = bmax * p.scale_log2;
-                m_seen[ht] = fmaxf(m_seen[ht], bz);
-                if (m_run[ht] == -INFINITY) {    // first usable key: O and l are still zero
-                    bmax = fmaxf(bmax, xor16_f(bmax));
-                    bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
-                    m_run[ht] = bmax * p.scale_log2;
-                } else if (bz > m_run[ht] + MAX_RISE) {
-                    restart = true;
+                if (st == 0) {
+                    const float bmax = fmaxf(fmaxf(fmaxf(sacc[ht][0][0], sacc[ht][0][1]),
+                                                   fmaxf(sacc[ht][0][2], sacc[ht][0][3])),
+                                             fmaxf(fmaxf(sacc[ht][1][0], sacc[ht][1][1]),
+                                                   fmaxf(sacc[ht][1][2], sacc[ht][1][3])));
+                    bz[ht] = bmax * p.scale_log2;
+                    m_seen[ht] = fmaxf(m_seen[ht], bz[ht]);
+                    asm volatile("" : "+v"(bz[ht]));
+                } else if (st == 1) {
+                    const float ball = group4_max(bz[ht]);
+                    m_run[ht] = m_run[ht] == -INFINITY ? ball : m_run[ht];
+                    neg_m[ht] = m_run[ht] == -INFINITY ? 0.f : -m_run[ht];
+                    rise[ht] = fmaxf(rise[ht], bz[ht] + neg_m[ht]);
+                    asm volatile("" : "+v"(neg_m[ht]));
+                } else if (st == 2 || st == 3) {
+#pragma unroll
+                    for (int e = 4 * (st - 2); e < 4 * (st - 1); ++e) {
+                        pv[ht][e] = __builtin_amdgcn_exp2f(fmaf(sacc[ht][e >> 2][e & 3], p.scale_log2, neg_m[ht]));
+                        asm volatile("" : "+v"(pv[ht][e]));
+                    }
+                } else if (st == 4) {
+                    l_run[ht] += ((pv[ht][0] + pv[ht][1]) + (pv[ht][2] + pv[ht][3])) +
+                                 ((pv[ht][4] + pv[ht][5]) + (pv[ht][6] + pv[ht][7]));
+                    pb[ht] = bf16x8{(__bf16)pv[ht][0], (__bf16)pv[ht][1], (__bf16)pv[ht][2], (__bf16)pv[ht][3],
+                                    (__bf16)pv[ht][4], (__bf16)pv[ht][5], (__bf16)pv[ht][6], (__bf16)pv[ht][7]};
+                } else if (st == 5) {
+                    // P to LDS: head h0 + 16*ht + row16, probabilities of the
+                    // permuted key order 8*grp .. 8*grp+7 (keys 4*grp+i and 16+4*grp+i)
+                    *reinterpret_cast<DSA_LDS bf16x8 *>(pl + (h0 + 16 * ht + row16) * PP + 16 * grp) = pb[ht];
                 }
-                const float neg_m = m_run[ht] == -INFINITY ? 0.f : -m_run[ht];
-                float pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[ht][e >> 2][e & 3], p.scale_log2, neg_m));
-                l_run[ht] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-                pb[ht] = bf16x8{(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3],
-                                (__bf16)pv[4], (__bf16)pv[5], (__bf16)pv[6], (__bf16)pv[7]};
             }
+        };
 
-            // ---- P to LDS: head h0 + 16*ht + row16, probabilities of the
-            // permuted key order 8*grp .. 8*grp+7 (keys 4*grp+i and 16+4*grp+i)
-            lds_u8 *pl = (lds_u8 *)plds[blk & 1];
+        // Pipeline.  Blocks 0 and 1 are loaded and block 0's probabilities
+        // computed before the loop.  Step blk (between two barriers): load
+        // block blk+2; S^T of block blk+1; PV of block blk with block blk+1's
+        // softmax stages between its MFMAs.  The barrier at the end of the
+        // step publishes block blk+1's probabilities and block blk+2's rows,
+        // and frees block blk's buffer (which receives block blk+3) and its
+        // probabilities (plds by block parity).  The last step runs the
+        // softmax stages on an empty block (every slot masked: no effect).
+        if (nblk > 0) {
+            {
+                const GatherSlots g0 = gather_slots(lsel, 0, l, kvb);
 #pragma unroll
-            for (int ht = 0; ht < NHT; ++ht)
-                *reinterpret_cast<DSA_LDS bf16x8 *>(pl + (h0 + 16 * ht + row16) * PP + 16 * grp) = pb[ht];
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block blk+1
+                for (int i = 0; i < 5; ++i) gather_issue(g0, i, l, lb0);
+            }
+            if (nblk > 1) {
+                const GatherSlots g1 = gather_slots(lsel, 1, l, kvb);
+#pragma unroll
+                for (int i = 0; i < 5; ++i) gather_issue(g1, i, l, lb1);
+            }
+            if (nblk > 1) {
+                if (wave < 4)
+                    __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+                else
+                    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            }
+            lds_barrier();   // block 0 landed and visible to every wave
+            f32x4 sacc[NHT][MT];
+            {
+                const GatherSlots gnone = gather_slots(lsel, 0, l, kvb);
+                qk_block(0, lb0, sacc, gnone, false, lb2, l);
+            }
+            mask_block(__builtin_amdgcn_readlane(maskv, 0), sacc);
+#pragma unroll
+            for (int st = 0; st < 6; ++st) soft_stage(st, sacc, (lds_u8 *)plds[0]);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block 1
             lds_barrier();
-            if (blk + 2 < nblk) gather_block(lane_row, lane_slab, lsel, blk + 2, nxt2, lz);
+        }
+        auto step = [&](int blk, lds_u8 *cur, lds_u8 *nx1, lds_u8 *nx2) {
+            const int z = blk >> 30;
+            const int lz = lane_id() + z;
+            const bool ld2 = blk + 2 < nblk;
+            const bool more = blk + 1 < nblk;
+            f32x4 sacc[NHT][MT];
+            // block blk+2's loads spread over block blk+1's S^T
+            const GatherSlots g = gather_slots(lsel, ld2 ? blk + 2 : blk, lz, kvb);
+            if (more) {
+                qk_block(blk + 1, nx1, sacc, g, ld2, nx2, lz);
+            } else {
+#pragma unroll
+                for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) sacc[ht][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            mask_block(more ? __builtin_amdgcn_readlane(maskv, blk + 1) : 0u, sacc);
+            lds_u8 *pl_next = (lds_u8 *)plds[(blk + 1) & 1];
+
             // ---- O^T += V^T P^T over this wave's value columns.  A = V^T via
             // transpose reads (all CT_W tiles, read once): 16-lane group grp
             // reads rows (keys) 4*grp + r and 16 + 4*grp + r; lane row16 of the
             // group addresses row row16/4, columns 16*ct + 4*(row16%4) .. +3.
             // B = P^T of head tile T, read from LDS one tile ahead; each B
-            // operand feeds CT_W MFMAs.
+            // operand feeds CT_W MFMAs.  Softmax stage T of block blk+1 runs
+            // after head tile T's MFMAs.
+            const lds_u8 *pl = (const lds_u8 *)plds[blk & 1];
             const int vAz = vA + z + 32 * CT_W * wave;
             bf16x8 va[CT_W];
 #pragma unroll
@@ -369,13 +442,16 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
                 if (T + 1 < HT_ALL) pt[(T + 1) & 1] = p_op(T + 1);
 #pragma unroll
                 for (int ct = 0; ct < CT_W; ++ct) o[T][ct] = mfma_bf16_16x16x32(va[ct], pt[T & 1], o[T][ct]);
+                if (T < 6) soft_stage(T, sacc, pl_next);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block blk+2
+            lds_barrier();
         };
         for (int blk = 0; blk < nblk; blk += 3) {
-            step(blk, lb0, lb2);
-            if (blk + 1 < nblk) step(blk + 1, lb1, lb0);
-            if (blk + 2 < nblk) step(blk + 2, lb2, lb1);
+            step(blk, lb0, lb1, lb2);
+            if (blk + 1 < nblk) step(blk + 1, lb1, lb2, lb0);
+            if (blk + 2 < nblk) step(blk + 2, lb2, lb0, lb1);
         }
 
         // ---- the head's maximum over its 4 lane groups (the reference of a
@@ -387,6 +463,9 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
         }
         // ---- did any head of any wave outgrow its reference max?
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of this pass left in flight
+        bool restart = false;
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) restart |= rise[ht] > MAX_RISE;
         if (l == 0) restart_flag[wave] = __ballot(restart) != 0;
         __syncthreads();
         bool again = false;
