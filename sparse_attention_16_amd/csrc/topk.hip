@@ -7,28 +7,28 @@
 // column; all visible columns when there are at most k.  Output: the selected
 // columns in ascending order, -1 padded.
 //
-// Method (one workgroup per row chunk, keys staged in LDS):
-//   1. stage   : scores -> order-preserving uint32 keys in LDS (16-byte
-//                loads issued one chunk ahead), building a histogram of the
-//                top 11 key bits on the way; its scan names the bin b1 that
-//                holds the k-th largest key.
-//   2. extract : each wave walks its own contiguous column segment, counts
-//                the keys above bin b1 and copies the keys of bin b1 (a few
-//                percent of the row) into its own candidate region.  Wave-
-//                local running offsets come from ballots: no atomics.
-//   3. refine  : two histogram passes of 11 and 10 bits over the candidates
-//                give the exact k-th largest key kappa and how many keys equal
-//                to kappa are taken.  (If bin b1 overflows the candidate
-//                regions - e.g. a row of equal scores - these passes run over
-//                the whole row instead.)
-//   4. emit    : per wave, the number of keys > kappa and == kappa in its
-//                segment gives (through one block prefix) its first output
-//                slot; the wave then walks its segment in column order and
-//                writes every key > kappa and the lowest-column keys ==
-//                kappa.  The output is ascending with no sort.
-// Rows longer than one 32768-column chunk: each chunk selects its exact local
-// top-k candidates (key, column) into workspace; a merge workgroup runs the
-// same select over the candidates.  The union of the chunk-local top-k sets
+// Method (one 512-thread workgroup per row chunk of up to 32768 columns; the
+// chunk's scores stay in registers, 64 per thread, as order-preserving uint32
+// keys):
+//   1. range   : block minimum and maximum of the chunk's scores.
+//   2. bin     : a 2048-bin histogram of the scores, binned by value over
+//                [min, max] (a non-decreasing map, so bins keep the order);
+//                a scan from the top names the bin b1 holding the k-th
+//                largest key and how many of its keys are taken.
+//   3. kappa   : the keys of bin b1 (a handful on spread-out scores) are
+//                collected in LDS and each is ranked against the others: the
+//                k-th largest key kappa and the number of keys equal to kappa
+//                to take follow directly.  If the bins cannot be formed or bin
+//                b1 is too full (e.g. many equal scores), three exact radix
+//                passes (11, 11, 10 key bits) over the register keys give
+//                kappa instead.
+//   4. emit    : each thread counts, per 4-column group, its keys > kappa and
+//                == kappa; one block prefix over the groups in column order
+//                gives every selected key its output slot.  The output is
+//                ascending with no sort.
+// Rows longer than one chunk: each chunk selects its exact local top-k
+// candidates (key, column) into workspace; a merge workgroup runs the same
+// select over the candidates.  The union of the chunk-local top-k sets
 // contains the global top-k under the same total order, so the merge is exact.
 #include "dsa_device.h"
 #include "kernels.h"
@@ -37,40 +37,70 @@ namespace dsa {
 
 namespace {
 
-constexpr int TPB = 512;            // threads per workgroup
-constexpr int NWAVE = TPB / kWave;
-constexpr int NBIN = 2048;          // 11-bit digits
-constexpr int BPT = NBIN / TPB;     // histogram bins scanned per thread
-constexpr int CAP_W = 512;          // candidate keys per wave
-constexpr int CAND_CAP = CAP_W * NWAVE;
-constexpr int SEG_ALIGN = 4 * kWave;  // a wave step covers 256 columns
-static_assert(NBIN % TPB == 0, "bins per thread");
+constexpr int TPB = 512;                                   // threads per workgroup
+constexpr int NWAVE = TPB / kWave;                         // 8
+constexpr int NBIN = 2048;                                 // histogram bins
+constexpr int BPT = NBIN / TPB;                            // bins scanned per thread
+constexpr int CCAP = TPB;                                  // candidates ranked directly (one per thread)
+constexpr int CH_V4 = TOPK_CHUNK / (4 * TPB);              // 4-key groups per thread, chunk kernel
+constexpr int MG_V4 = TOPK_MAX_CHUNKS * 2048 / (4 * TPB);  // 4-key groups per thread, merge kernel
+constexpr int MAX_V4 = CH_V4 > MG_V4 ? CH_V4 : MG_V4;
+static_assert(NBIN % TPB == 0 && CH_V4 * 4 * TPB == TOPK_CHUNK && MG_V4 * 4 * TPB == TOPK_MAX_CHUNKS * 2048,
+              "register layout");
+static_assert(NWAVE * MAX_V4 <= 2 * kWave, "one wave scans the group totals, two per lane");
 
 struct SelectShared {
-    uint32_t hist[NBIN];
-    uint32_t wtot[NWAVE];     // scan scratch
-    uint32_t wnc[NWAVE];      // candidates found by each wave
-    uint32_t wabove[NWAVE];   // keys above bin b1 in each wave's segment
-    uint32_t wgt[NWAVE];      // keys > kappa in each wave's segment
-    uint32_t weq[NWAVE];      // keys == kappa in each wave's segment
-    uint32_t prefix;          // key bits fixed so far
-    uint32_t rem;             // keys still needed inside the current prefix
+    // each array has one spare entry per lane after its end: writes that
+    // must not count go there (a spare per lane, so that they do not collide)
+    uint32_t hist[NBIN + kWave];
+    uint32_t ckey[CCAP + kWave];
+    int32_t ocol[2048 + kWave];      // selected columns by slot
+    uint32_t okey[2048 + kWave];     // their keys
+    uint32_t gsum[MAX_V4 * NWAVE];   // per (group, wave) packed counts, then their prefix
+    uint32_t wtot[NWAVE];            // scan and reduction scratch
+    uint32_t wmin[NWAVE], wmax[NWAVE];
+    uint32_t ncand;
+    uint32_t prefix;                 // bin b1, or radix key bits fixed so far
+    uint32_t rem;                    // keys still needed inside the prefix
+    uint32_t kappa, need_eq;
 };
 
-__device__ __forceinline__ uint64_t lanes_below() {
-    const int l = lane_id();
-    return l == 0 ? 0ull : (~0ull >> (64 - l));
+// Marks the register keys as changed (no instruction): values derived from
+// them in an earlier phase (validity masks, bins) are recomputed instead of
+// being kept live across the phases, which would not fit in the registers.
+template <int N>
+__device__ __forceinline__ void launder(uint32_t (&kr)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(kr[i]));
 }
 
-// Block-wide exclusive scan of one value per thread.
+// Score of a key (inverse of score_key; key != 0).
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Inclusive scan over the 64 lanes of a wave with DPP lane moves (VALU only,
+// no LDS round trip): row shifts by 1, 2, 4, 8 scan each 16-lane row, then
+// the last lane of row 0 is added to row 1 and 3 and that of rows 0-1 to
+// rows 2-3.  Lanes a move has no source for take the identity `id`.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t id, Op op) {
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t x) {
+    return wave_scan(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Block-wide exclusive scan of one value per thread (in thread order).
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wtot) {
     const int l = lane_id(), w = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(x, d, 64);
-        if (l >= d) x += y;
-    }
+    const uint32_t x = wave_scan_add(v);
     if (l == 63) wtot[w] = x;
     lds_barrier();
     uint32_t off = 0;
@@ -80,20 +110,11 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wtot) 
     return off + x - v;
 }
 
-__device__ __forceinline__ void init_select(SelectShared &sh, int k) {
-    for (int i = threadIdx.x; i < NBIN; i += TPB) sh.hist[i] = 0;
-    if (threadIdx.x == 0) {
-        sh.prefix = 0;
-        sh.rem = (uint32_t)k;
-    }
-}
-
-// From the histogram in sh.hist (digit of `width` bits below sh.prefix), picks
-// the bin holding the rem-th largest key; appends it to prefix, updates rem.
-__device__ void pick_bin(int width, SelectShared &sh) {
-    const int tid = threadIdx.x;
-    // thread i owns the BPT bins top, top-1, ... counted from the top
-    const int top = NBIN - 1 - BPT * tid;
+// From the counts in sh.hist (bin i = digit i, larger digits = larger keys),
+// picks the bin holding the sh.rem-th largest key: sh.prefix = (prefix <<
+// width) | bin, sh.rem = rank inside that bin.
+__device__ __forceinline__ void pick_bin(int width, SelectShared &sh) {
+    const int top = NBIN - 1 - BPT * (int)threadIdx.x;   // this thread's bins: top, top-1, ...
     uint32_t c[BPT], sum = 0;
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
@@ -115,180 +136,213 @@ __device__ void pick_bin(int width, SelectShared &sh) {
     lds_barrier();
 }
 
-// Histogram pass over the keys accepted by `get(i, key)` for i in [0, n):
-// bits [shift, shift+width) of the keys whose bits above equal sh.prefix.
-template <class Get>
-__device__ void radix_pass(int n, int shift, int width, SelectShared &sh, Get get) {
-    const int tid = threadIdx.x;
-    for (int i = tid; i < NBIN; i += TPB) sh.hist[i] = 0;
-    lds_barrier();
-    const uint32_t prefix = sh.prefix;
-    const int hi_shift = shift + width;
-    const uint32_t mask = (1u << width) - 1u;
-    for (int i = tid; i < n; i += TPB) {
-        uint32_t key;
-        if (get(i, key) && (key >> hi_shift) == prefix)
-            atomicAdd(&sh.hist[(key >> shift) & mask], 1u);
-    }
-    lds_barrier();
-    pick_bin(width, sh);
+__device__ __forceinline__ void clear_hist(SelectShared &sh) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) sh.hist[threadIdx.x + i * TPB] = 0u;
 }
 
-// Column segment of wave w: [s0, s1), a multiple of 256 columns long.
-__device__ __forceinline__ void wave_segment(int n, int w, int &s0, int &s1) {
-    const int per = (n + NWAVE - 1) / NWAVE;
-    const int seg = (per + SEG_ALIGN - 1) / SEG_ALIGN * SEG_ALIGN;
-    s0 = w * seg < n ? w * seg : n;
-    s1 = s0 + seg < n ? s0 + seg : n;
-}
-
-// Loads the 4 keys at columns i0..i0+3 (i0 a multiple of 4; zeros when i0 is
-// past the segment).  Callers mask columns >= s1 themselves.
-__device__ __forceinline__ uint4 load4(const uint32_t *keys, int i0, int s1) {
-    return i0 < s1 ? *reinterpret_cast<const uint4 *>(&keys[i0]) : uint4{0u, 0u, 0u, 0u};
-}
-
-// Steps 2-4 for keys[0..n), n > k, whose top-11-bit histogram is in sh.hist
-// (the caller's last LDS writes need not be fenced yet).  keys must be 16-byte
-// aligned and readable up to the next multiple of 4 past n.  Calls
-// emit(slot, i) for the k selected positions i, slot = rank in column order.
-template <class Emit>
-__device__ void select_emit(const uint32_t *keys, int n, int k, SelectShared &sh,
-                            uint32_t *cand, Emit emit) {
-    const int l = lane_id(), w = threadIdx.x >> 6;
-    const uint64_t lt = lanes_below();
-    lds_barrier();
-    pick_bin(11, sh);
-    const uint32_t b1 = sh.prefix;
-    int s0, s1;
-    wave_segment(n, w, s0, s1);
-
-    // 2. extract: candidates of bin b1 into this wave's region, keys above b1 counted
-    uint32_t *mine = cand + w * CAP_W;
-    uint32_t run = 0, above = 0;
-    for (int b = s0; b < s1; b += SEG_ALIGN) {
-        const int i0 = b + 4 * l;
-        const uint4 kk = load4(keys, i0, s1);
-        const uint32_t kv[4] = {kk.x, kk.y, kk.z, kk.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bool ok = i0 + u < s1;
-            const uint32_t bin = kv[u] >> 21;
-            const bool m = ok && bin == b1;
-            const uint64_t bm = __ballot(m);
-            above += (uint32_t)__popcll(__ballot(ok && bin > b1));
-            const uint32_t pos = run + (uint32_t)__popcll(bm & lt);
-            if (m && pos < CAP_W) mine[pos] = kv[u];
-            run += (uint32_t)__popcll(bm);
-        }
+// Exact kappa by three radix passes over the register keys (key 0 = no key).
+template <int NV4>
+__device__ __forceinline__ void radix_kappa(uint32_t (&kr)[4 * NV4], int ngroups, int k, SelectShared &sh) {
+    if (threadIdx.x == 0) {
+        sh.prefix = 0;
+        sh.rem = (uint32_t)k;
     }
-    if (l == 0) {
-        sh.wnc[w] = run;
-        sh.wabove[w] = above;
-    }
-    lds_barrier();
-    bool overflow = false;
+    constexpr int SHIFT[3] = {21, 10, 0}, WIDTH[3] = {11, 11, 10};
 #pragma unroll
-    for (int x = 0; x < NWAVE; ++x) overflow |= sh.wnc[x] > CAP_W;
-
-    // 3. refine: exact kappa
-    uint32_t kappa, need_eq;
-    if (!overflow) {
-        auto get = [&](int i, uint32_t &key) {
-            const int r = i / CAP_W, j = i - r * CAP_W;
-            key = cand[i];
-            return (uint32_t)j < sh.wnc[r];
-        };
-        radix_pass(CAND_CAP, 10, 11, sh, get);
-        radix_pass(CAND_CAP, 0, 10, sh, get);
-    } else {
-        auto get = [&](int i, uint32_t &key) {
-            key = keys[i];
-            return true;
-        };
-        radix_pass(n, 10, 11, sh, get);
-        radix_pass(n, 0, 10, sh, get);
-    }
-    kappa = sh.prefix;
-    need_eq = sh.rem;
-
-    // 4. emit: per-wave counts -> first slots -> ordered walk of the segment
-    uint32_t gt = 0, eq = 0;
-    if (!overflow) {
-        gt = sh.wabove[w];  // every key above bin b1 is > kappa
-        const uint32_t nc = sh.wnc[w];
-        for (uint32_t j = l; j < ((nc + 63u) & ~63u); j += 64) {
-            const uint32_t key = j < nc ? mine[j] : 0u;
-            gt += (uint32_t)__popcll(__ballot(j < nc && key > kappa));
-            eq += (uint32_t)__popcll(__ballot(j < nc && key == kappa));
-        }
-    } else {
-        for (int b = s0; b < s1; b += SEG_ALIGN) {
-            const int i0 = b + 4 * l;
-            const uint4 kk = load4(keys, i0, s1);
-            const uint32_t kv[4] = {kk.x, kk.y, kk.z, kk.w};
+    for (int ps = 0; ps < 3; ++ps) {
+        clear_hist(sh);
+        lds_barrier();
+        const uint32_t prefix = sh.prefix;
+        const int hi = SHIFT[ps] + WIDTH[ps];
+        launder(kr);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool ok = i0 + u < s1;
-                gt += (uint32_t)__popcll(__ballot(ok && kv[u] > kappa));
-                eq += (uint32_t)__popcll(__ballot(ok && kv[u] == kappa));
+        for (int i = 0; i < 4 * NV4; ++i) {
+            if (i / 4 < ngroups) {
+                const uint32_t key = kr[i];
+                const bool match = key != 0u && (hi == 32 || (key >> (hi & 31)) == prefix);
+                atomicAdd(&sh.hist[match ? (key >> SHIFT[ps]) & ((1u << WIDTH[ps]) - 1u) : NBIN + lane_id()], 1u);
             }
+            if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // one 4-key group at a time
         }
+        lds_barrier();
+        pick_bin(WIDTH[ps], sh);
     }
-    if (l == 0) {
-        sh.wgt[w] = gt;
-        sh.weq[w] = eq;
+    if (threadIdx.x == 0) {
+        sh.kappa = sh.prefix;
+        sh.need_eq = sh.rem;
     }
     lds_barrier();
-    uint32_t g_run = 0, e_run = 0;
+}
+
+// Steps 1-4 over the register keys kr (key 0 = no key; key i of group u sits
+// at column 4 * (u * TPB + tid) + i), at least k + 1 of them real, groups >=
+// ngroups empty.  tz is the thread index, passed in so that a caller's loop
+// can keep the per-key column arithmetic from being hoisted out of it and
+// held in registers.  On return (after a barrier) sh.ocol[slot], slot < k,
+// holds the columns of the k selected keys, slot = rank in column order, and
+// sh.okey[slot] their keys when want_keys.
+template <int NV4>
+__device__ __forceinline__ void select_regs(uint32_t (&kr)[4 * NV4], int ngroups, int k, SelectShared &sh, int tz,
+                                            bool want_keys) {
+    const int tid = threadIdx.x, l = lane_id(), w = tid >> 6;
+    launder(kr);
+
+    // 1. range (keys order like scores: min/max over keys)
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < 4 * NV4; ++i) {
+        const uint32_t key = kr[i];
+        kmin = key != 0u && key < kmin ? key : kmin;
+        kmax = key > kmax ? key : kmax;
+    }
+    kmin = wave_scan(kmin, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+    kmax = wave_scan(kmax, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+    if (l == 63) {   // the inclusive scan's last lane holds the wave's result
+        sh.wmin[w] = kmin;
+        sh.wmax[w] = kmax;
+    }
+    clear_hist(sh);
+    if (tid == 0) {
+        sh.ncand = 0;
+        sh.prefix = 0;
+        sh.rem = (uint32_t)k;
+    }
+    lds_barrier();
 #pragma unroll
     for (int x = 0; x < NWAVE; ++x) {
-        g_run += (x < w) ? sh.wgt[x] : 0u;
-        e_run += (x < w) ? sh.weq[x] : 0u;
+        kmin = sh.wmin[x] < kmin ? sh.wmin[x] : kmin;
+        kmax = sh.wmax[x] > kmax ? sh.wmax[x] : kmax;
     }
-    for (int b = s0; b < s1; b += SEG_ALIGN) {
-        const int i0 = b + 4 * l;
-        const uint4 kk = load4(keys, i0, s1);
-        const uint32_t kv[4] = {kk.x, kk.y, kk.z, kk.w};
-        bool fg[4], fe[4];
-        uint32_t gb = 0, eb = 0, gtot = 0, etot = 0;
+    const float vmin = key_value(kmin), vmax = key_value(kmax);
+    const float range = vmax - vmin;
+    const float inv = (float)NBIN / range;
+    // value bins need a finite, positive range with a finite scale
+    const bool binned = range > 0.f && range < INFINITY && inv < INFINITY;
+
+    bool exact_done = false;
+    if (binned) {
+        // 2. value histogram, bin b1
+        auto bin_of = [&](uint32_t key) {
+            const float t = (key_value(key) - vmin) * inv;
+            return (uint32_t)fminf(t, (float)(NBIN - 1));
+        };
+        launder(kr);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bool ok = i0 + u < s1;
-            fg[u] = ok && kv[u] > kappa;
-            fe[u] = ok && kv[u] == kappa;
-            const uint64_t bg = __ballot(fg[u]), be = __ballot(fe[u]);
-            gb += (uint32_t)__popcll(bg & lt);
-            eb += (uint32_t)__popcll(be & lt);
-            gtot += (uint32_t)__popcll(bg);
-            etot += (uint32_t)__popcll(be);
+        for (int i = 0; i < 4 * NV4; ++i) {
+            if (i / 4 < ngroups) atomicAdd(&sh.hist[kr[i] != 0u ? bin_of(kr[i]) : NBIN + l], 1u);
+            if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // one 4-key group at a time
         }
-        uint32_t g = g_run + gb, e = e_run + eb;
+        lds_barrier();
+        pick_bin(0, sh);   // prefix = b1, rem = rank inside b1
+        const uint32_t b1 = sh.prefix, rem = sh.rem;
+        // the bins are recomputed below, not kept from the histogram pass
+        // (64 live bin values would not fit in the registers)
+        launder(kr);
+        float vmin2 = vmin, inv2 = inv;
+        asm volatile("" : "+v"(vmin2), "+v"(inv2));
+        auto bin2_of = [&](uint32_t key) {
+            const float t = (key_value(key) - vmin2) * inv2;
+            return (uint32_t)fminf(t, (float)(NBIN - 1));
+        };
+        // 3. candidates of bin b1, ranked
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (fg[u] || (fe[u] && e < need_eq)) {
-                const uint32_t slot = g + (e < need_eq ? e : need_eq);
-                if (slot < (uint32_t)k) emit(slot, i0 + u);
+        for (int i = 0; i < 4 * NV4; ++i) {
+            if (i / 4 >= ngroups) continue;
+            const bool m = kr[i] != 0u && bin2_of(kr[i]) == b1;
+            const uint64_t bal = __ballot(m);
+            if (bal != 0ull) {   // wave-uniform; rare
+                uint32_t base = 0;
+                if (l == 0) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(bal));
+                base = __builtin_amdgcn_readlane(base, 0);
+                const uint32_t pos = base + (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                sh.ckey[m && pos < CCAP ? pos : CCAP + l] = kr[i];
             }
-            g += fg[u] ? 1u : 0u;
-            e += fe[u] ? 1u : 0u;
+            if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
-        g_run += gtot;
-        e_run += etot;
+        lds_barrier();
+        const uint32_t nc = sh.ncand;
+        if (nc <= CCAP) {
+            if ((uint32_t)tid < nc) {
+                const uint32_t key = sh.ckey[tid];
+                uint32_t gt = 0, eq = 0;
+                for (uint32_t j = 0; j < nc; ++j) {
+                    const uint32_t o = sh.ckey[j];
+                    gt += o > key ? 1u : 0u;
+                    eq += o == key ? 1u : 0u;
+                }
+                // every thread holding kappa writes the same two values
+                if (gt < rem && rem <= gt + eq) {
+                    sh.kappa = key;
+                    sh.need_eq = rem - gt;
+                }
+            }
+            lds_barrier();
+            exact_done = true;
+        }
     }
-    lds_barrier();  // LDS (keys, candidates, counters) free for the next select
+    if (!exact_done) radix_kappa<NV4>(kr, ngroups, k, sh);
+    const uint32_t kappa = sh.kappa, need_eq = sh.need_eq;
+
+    launder(kr);
+    // 4. emit: packed counts (keys > kappa in the low half, == kappa in the
+    // high half; each at most 32768) per 4-key group, prefix in column order
+    uint32_t incl[NV4];
+#pragma unroll
+    for (int u = 0; u < NV4; ++u) {
+        if (u < ngroups) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t key = kr[4 * u + i];
+                c += key > kappa ? 1u : (key == kappa ? 0x10000u : 0u);
+            }
+            const uint32_t x = wave_scan_add(c);
+            incl[u] = x - c;   // exclusive within the wave
+            if (l == 63) sh.gsum[u * NWAVE + w] = x;
+        }
+    }
+    lds_barrier();
+    if (w == 0) {   // exclusive prefix over (group, wave) in column order
+        const int n2 = ngroups * NWAVE;
+        const uint32_t a = 2 * l < n2 ? sh.gsum[2 * l] : 0u;
+        const uint32_t b = 2 * l + 1 < n2 ? sh.gsum[2 * l + 1] : 0u;
+        const uint32_t s = a + b;
+        const uint32_t x = wave_scan_add(s);
+        if (2 * l < n2) sh.gsum[2 * l] = x - s;
+        if (2 * l + 1 < n2) sh.gsum[2 * l + 1] = x - s + a;
+    }
+    lds_barrier();
+    launder(kr);
+#pragma unroll
+    for (int u = 0; u < NV4; ++u) {
+        if (u < ngroups) {
+            const uint32_t base = sh.gsum[u * NWAVE + w] + incl[u];
+            uint32_t g = base & 0xFFFFu, e = base >> 16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t key = kr[4 * u + i];
+                const bool fg = key > kappa, fe = key == kappa;
+                const uint32_t slot = g + (e < need_eq ? e : need_eq);
+                const bool take = (fg || (fe && e < need_eq)) && slot < (uint32_t)k;
+                const uint32_t at = take ? slot : 2048u + (uint32_t)l;   // this lane's spare slot
+                sh.ocol[at] = 4 * (u * TPB + tz) + i;
+                if (want_keys) sh.okey[at] = key;
+                g += fg ? 1u : 0u;
+                e += fe ? 1u : 0u;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();   // selection in sh.ocol / sh.okey
 }
 
-// Keys are staged through registers: a workgroup issues the 16-byte loads of
-// its next chunk before it selects the current one, so HBM latency overlaps
-// the LDS work.  PF float4 per thread cover one 32768-column chunk.
-constexpr int PF = TOPK_CHUNK / (4 * TPB);
-
+// One row chunk: row t, chunk c, visible columns n of the row; the chunk is
+// columns [c0, c0 + len) of the row (len 0: nothing to stage).
 struct ChunkItem {
-    int t, c;          // query row, chunk of the row
-    int n;             // visible columns of the row
-    int c0, len;       // first column and length of the chunk (len 0: nothing to stage)
-    int n4;            // float4 loads (0 when the row is not 16-byte aligned)
+    int t, c, n, c0, len;
+    bool vec;          // 16-byte aligned chunk: float4 loads
     const float *row;  // scores of the chunk
 };
 
@@ -301,41 +355,43 @@ __device__ __forceinline__ ChunkItem chunk_item(const TopkParams &p, int item) {
     it.c0 = it.c * TOPK_CHUNK;
     it.len = (it.n > p.k && it.c0 < it.n) ? ((it.n - it.c0) < TOPK_CHUNK ? it.n - it.c0 : TOPK_CHUNK) : 0;
     it.row = p.scores + (int64_t)it.t * p.ld + it.c0;
-    it.n4 = (reinterpret_cast<uintptr_t>(it.row) & 15) == 0 ? it.len >> 2 : 0;
+    // 16-byte loads when rows are 16-byte aligned and ld is a multiple of 4:
+    // then the load of a group with any column < len ends inside the row
+    it.vec = (reinterpret_cast<uintptr_t>(it.row) & 15) == 0 && (p.ld & 3) == 0;
     return it;
 }
 
-__device__ __forceinline__ void prefetch(const ChunkItem &it, float4 (&v)[PF]) {
-    const float4 *r4 = reinterpret_cast<const float4 *>(it.row);
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-        const int j = u * TPB + threadIdx.x;
-        v[u] = j < it.n4 ? r4[j] : float4{0.f, 0.f, 0.f, 0.f};
-    }
+// One 16-byte-per-lane direct-to-LDS load from sbase + voff (a scalar base
+// and a 32-bit per-lane offset) to LDS lds + 16 * lane.  Issued from asm, so
+// the compiler's wait insertion does not track it; the kernel waits with an
+// explicit vmcnt(0) before it reads the staged chunk.  M0 must be written one
+// instruction ahead of the load.
+__device__ __forceinline__ void dma16s(uint64_t sbase, uint32_t voff, const DSA_LDS void *lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "m0");
 }
 
-// Writes score_key of the chunk into keys[] and adds the top 11 bits of every
-// key to sh.hist (which must be zero).
-__device__ __forceinline__ void stage_keys(const ChunkItem &it, const float4 (&v)[PF],
-                                           uint32_t *keys, SelectShared &sh) {
-    const int tid = threadIdx.x;
+// Issues the loads of a chunk into the LDS stage (stage[c] = score of chunk
+// column c, c < len; group u of wave w: columns 4 * (u * TPB + 64 * w) + 0..255).
+// 16-byte direct-to-LDS loads when rows allow them, else plain loads and LDS
+// stores.  Columns past len are left unwritten (and dropped when the keys are
+// formed); a 16-byte load may read up to 3 of them, still inside the row.
+__device__ __forceinline__ void stage_chunk(const ChunkItem &it, float *stage, int tid) {
+    const int w = tid >> 6, l = tid & 63;
+    if (it.vec) {
+        uint64_t base = (uint64_t)(uintptr_t)it.row;
+        // (readfirstlane returns int: widen through uint32_t)
+        base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+               (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-        const int j = u * TPB + tid;
-        if (j < it.n4) {
-            const uint32_t k0 = score_key(v[u].x), k1 = score_key(v[u].y);
-            const uint32_t k2 = score_key(v[u].z), k3 = score_key(v[u].w);
-            *reinterpret_cast<uint4 *>(&keys[4 * j]) = uint4{k0, k1, k2, k3};
-            atomicAdd(&sh.hist[k0 >> 21], 1u);
-            atomicAdd(&sh.hist[k1 >> 21], 1u);
-            atomicAdd(&sh.hist[k2 >> 21], 1u);
-            atomicAdd(&sh.hist[k3 >> 21], 1u);
+        for (int u = 0; u < CH_V4; ++u) {
+            const int c = 4 * (u * TPB + 64 * w + l);
+            if (c < it.len)
+                dma16s(base, 4u * (uint32_t)c, (const DSA_LDS void *)(stage + 4 * (u * TPB + 64 * w)));
         }
-    }
-    for (int i = 4 * it.n4 + tid; i < it.len; i += TPB) {
-        const uint32_t key = score_key(it.row[i]);
-        keys[i] = key;
-        atomicAdd(&sh.hist[key >> 21], 1u);
+    } else {
+        for (int c = tid; c < it.len; c += TPB) stage[c] = it.row[c];
     }
 }
 
@@ -343,66 +399,87 @@ __device__ __forceinline__ void stage_keys(const ChunkItem &it, const float4 (&v
 
 // Persistent: workgroup g takes the (row, chunk) items g, g + gridDim.x, ...
 // of the T * nchunk items (item = row * nchunk + chunk).  Chunk c covers
-// visible columns [c*TOPK_CHUNK, min((c+1)*TOPK_CHUNK, nvis)).  The loads of
-// the next item are issued before the current one is selected.
-__global__ __launch_bounds__(TPB) void topk_chunk_kernel(TopkParams p, int nitems) {
-    __shared__ __attribute__((aligned(16))) uint32_t keys[TOPK_CHUNK];
-    __shared__ __attribute__((aligned(16))) uint32_t cand[CAND_CAP];
+// visible columns [c*TOPK_CHUNK, min((c+1)*TOPK_CHUNK, nvis)).  The next
+// item's scores stream into an LDS stage while the current item is selected
+// from registers.
+__global__ __launch_bounds__(TPB, 2) void topk_chunk_kernel(TopkParams p, int nitems) {
+    __shared__ __attribute__((aligned(16))) float stage[TOPK_CHUNK];
     __shared__ SelectShared sh;
     const int tid = threadIdx.x, k = p.k;
     int item = blockIdx.x;
     if (item >= nitems) return;
     ChunkItem nxt = chunk_item(p, item);
-    float4 v[PF];
-    prefetch(nxt, v);
+    if (nxt.len > 0) stage_chunk(nxt, stage, tid);
     for (; item < nitems; item += gridDim.x) {
+        // the thread index rebuilt from an opaque zero (item < 2^30): per-key
+        // column arithmetic then stays inside the loop instead of being held
+        // in registers across it
+        const int tz = tid + (item >> 30);
         const ChunkItem it = nxt;
-        int32_t *out = p.idx + (int64_t)it.t * k;
-        if (it.len > 0) {
-            init_select(sh, k);
-            lds_barrier();
-            stage_keys(it, v, keys, sh);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's part of the stage
+        lds_barrier();
+        uint32_t kr[4 * CH_V4];
+#pragma unroll
+        for (int u = 0; u < CH_V4; ++u) {
+            const int c = 4 * (u * TPB + tz);
+            const float4 f4 = c < it.len ? *reinterpret_cast<const float4 *>(stage + c) : float4{0.f, 0.f, 0.f, 0.f};
+            const float f[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kr[4 * u + i] = c + i < it.len ? score_key(f[i]) : 0u;
         }
+        lds_barrier();   // stage read by every thread: the next item may land in it
         if (item + (int)gridDim.x < nitems) {
             nxt = chunk_item(p, item + gridDim.x);
-            prefetch(nxt, v);
+            if (nxt.len > 0) stage_chunk(nxt, stage, tz);
         }
+        int32_t *out = p.idx + (int64_t)it.t * k;
         if (it.n <= k) {  // everything visible is selected
             if (it.c == 0)
-                for (int j = tid; j < k; j += TPB) out[j] = j < it.n ? j : -1;
+                for (int j = tz; j < k; j += TPB) out[j] = j < it.n ? j : -1;
             continue;
         }
         if (it.len == 0) continue;  // chunk past the visible end
         const int c0 = it.c0, len = it.len;
-        if (it.n <= TOPK_CHUNK) {
-            select_emit(keys, len, k, sh, cand, [&](uint32_t slot, int i) { out[slot] = c0 + i; });
-            continue;
-        }
+        const int ngroups = (len + 4 * TPB - 1) / (4 * TPB);
         // multi-chunk row: local top-min(k, len) candidates of this chunk
+        const bool multi = it.n > TOPK_CHUNK;
         uint32_t *ck = p.cand_key + ((int64_t)it.t * p.nchunk + it.c) * k;
         int32_t *cp = p.cand_pos + ((int64_t)it.t * p.nchunk + it.c) * k;
-        if (len <= k) {
-            lds_barrier();
-            for (int j = tid; j < k; j += TPB) {
-                ck[j] = j < len ? keys[j] : 0u;
-                cp[j] = j < len ? c0 + j : -1;
+        if (multi && len <= k) {   // the whole chunk, in column order, padded
+#pragma unroll
+            for (int u = 0; u < CH_V4; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = 4 * (u * TPB + tz) + i;
+                    if (c < len) {
+                        ck[c] = kr[4 * u + i];
+                        cp[c] = c0 + c;
+                    }
+                }
+            for (int j = len + tz; j < k; j += TPB) {
+                ck[j] = 0u;
+                cp[j] = -1;
             }
-            lds_barrier();
             continue;
         }
-        select_emit(keys, len, k, sh, cand, [&](uint32_t slot, int i) {
-            ck[slot] = keys[i];
-            cp[slot] = c0 + i;
-        });
+        select_regs<CH_V4>(kr, ngroups, k, sh, tz, multi);
+        for (int j = tz; j < k; j += TPB) {
+            const int col = c0 + sh.ocol[j];
+            if (multi) {
+                ck[j] = sh.okey[j];
+                cp[j] = col;
+            } else {
+                out[j] = col;
+            }
+        }
+        lds_barrier();   // sh free for the next select
     }
 }
 
 // Grid: x = query row.  Merges the chunk candidates of rows longer than one
-// chunk.  Candidate blocks are in column order and padded with key 0 (below
-// the key of every non-NaN score), so array order = column order.
-__global__ __launch_bounds__(TPB) void topk_merge_kernel(TopkParams p) {
-    __shared__ __attribute__((aligned(16))) uint32_t keys[TOPK_MAX_CHUNKS * 2048];
-    __shared__ __attribute__((aligned(16))) uint32_t cand[CAND_CAP];
+// chunk.  Candidate blocks are in column order and padded with key 0 (no
+// key), so array order = column order.
+__global__ __launch_bounds__(TPB, 2) void topk_merge_kernel(TopkParams p) {
     __shared__ SelectShared sh;
     const int t = blockIdx.x, tid = threadIdx.x;
     const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
@@ -412,20 +489,24 @@ __global__ __launch_bounds__(TPB) void topk_merge_kernel(TopkParams p) {
     const int m = nch * k;
     const uint32_t *ck = p.cand_key + (int64_t)t * p.nchunk * k;
     const int32_t *cp = p.cand_pos + (int64_t)t * p.nchunk * k;
-    init_select(sh, k);
-    lds_barrier();
-    for (int i = tid; i < m; i += TPB) {
-        const uint32_t key = ck[i];
-        keys[i] = key;
-        atomicAdd(&sh.hist[key >> 21], 1u);
-    }
+    uint32_t kr[4 * MG_V4];
+#pragma unroll
+    for (int u = 0; u < MG_V4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 4 * (u * TPB + tid) + i;
+            kr[4 * u + i] = c < m ? ck[c] : 0u;
+        }
+    const int ngroups = (m + 4 * TPB - 1) / (4 * TPB);
     int32_t *out = p.idx + (int64_t)t * k;
-    select_emit(keys, m, k, sh, cand, [&](uint32_t slot, int i) { out[slot] = cp[i]; });
+    select_regs<MG_V4>(kr, ngroups, k, sh, tid, false);
+    for (int j = tid; j < k; j += TPB) out[j] = cp[sh.ocol[j]];
 }
 
 hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    // one resident workgroup per compute unit (the keys fill most of the LDS)
+    if (p.nchunk > TOPK_MAX_CHUNKS) return hipErrorInvalidValue;
+    // persistent grid: one workgroup per compute unit (the stage fills the LDS)
     static int ncu = 0;
     if (ncu == 0) {
         int dev = 0, n = 0;
