@@ -227,14 +227,47 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
 
 // ---------------------------------------------------------------------------
 // Decode variant: one workgroup = one query row x one chunk of keys; the 4
-// waves split the chunk and stream their keys straight from HBM into the B
-// operand registers, one 64-key group ahead (a key is used by a single query
-// row, so staging it in LDS would buy nothing).  Grid: x = query row, y = key
-// chunk.
+// waves split the chunk into 64-key groups (wave w: groups w, w+4, ...).  A
+// key is used by a single query row, so nothing is shared: each wave streams
+// its own groups, DC_NBUF deep, into a private LDS ring with direct-to-LDS
+// loads (no registers held while they fly, no barriers), then reads each
+// 16-key B operand back as two 16-byte LDS reads.  Every load moves one
+// contiguous KB (8 key rows) in its natural order, so each touches the fewest
+// cache lines; the operand layout comes from the LDS reads.  Grid: x = query
+// row, y = key chunk.
 // ---------------------------------------------------------------------------
 constexpr int DC_WAVES = 4;
+// Groups in flight per wave.  One: a smaller LDS ring leaves room for more
+// resident workgroups (four per compute unit), and more independent streams
+// beat a deeper ring per wave (measured on the 64-sequence decode batch).
+constexpr int DC_NBUF = 1;
+constexpr int DC_GROUP = 64 * DI;           // bytes of one 64-key group
+constexpr int DC_LOADS = 9;                 // loads per group: 8 x 1 KB of keys + the scales
 
-__global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
+// Direct-to-LDS loads (16 or 4 bytes per lane) from sbase + voff (scalar base,
+// 32-bit lane offset) to LDS lds + size * lane.  Issued from asm: the
+// compiler's wait insertion does not track them; the kernel waits with
+// explicit vmcnt.  M0 must be written one instruction ahead of the load.
+__device__ __forceinline__ void dma_b128(uint64_t sbase, uint32_t voff, const DSA_LDS void *lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "m0");
+}
+__device__ __forceinline__ void dma_b32(uint64_t sbase, uint32_t voff, const DSA_LDS void *lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "m0");
+}
+// A wave-uniform 64-bit pointer value in scalar registers.  (readfirstlane
+// returns int: widen through uint32_t, or the low word is sign-extended.)
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+           (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+}
+
+__global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t kst[DC_WAVES][DC_NBUF][DC_GROUP];
+    __shared__ __attribute__((aligned(16))) float sst[DC_WAVES][DC_NBUF][64];
     const int t = blockIdx.x;
     const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
     const int c0 = blockIdx.y * p.key_chunk;
@@ -243,53 +276,67 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
     const int fill_end = p.fill_masked ? (c_end < ri.ctx ? c_end : ri.ctx) : comp_end;
     if (c0 >= fill_end) return;
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = lane_id();
     i32x8 qa[4];
     float wq[4][4];
     load_query(p, t, true, qa, wq);
 
-    // Wave w takes the 64-key groups w, w+4, ... of the chunk; the keys of
-    // the next group are loaded (straight from HBM into B operands) before
-    // the current group is computed.
     const int row = l & 15, grp = l >> 4;
-    auto kload = [&](int g0, i32x8 (&kb)[4], float &ks) {
+    const uint64_t kbase = uniform_u64((uint64_t)(uintptr_t)(p.k + ri.kv0 * DI));
+    const uint64_t sbase = uniform_u64((uint64_t)(uintptr_t)(p.k_scale + ri.kv0));
+    // Loads of group g0 into ring slot b.  Keys past the visible end load key
+    // c0 instead (their scores are not stored), so that every group issues
+    // exactly DC_LOADS loads, which the vmcnt waits below count on.
+    auto issue = [&](int g0, int b) {
+        // this wave's LDS reads of slot b (an earlier group) have completed
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int key = g0 + 16 * st + row;
-            const bool in = key < comp_end;
-            const i32x4 *s4 = reinterpret_cast<const i32x4 *>(p.k + (ri.kv0 + (in ? key : c0)) * DI + 32 * grp);
-            const i32x4 lo = s4[0], hi = s4[1];
-            kb[st] = in ? i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}
-                        : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        for (int j = 0; j < 8; ++j) {   // keys 8j .. 8j+7 of the group, lane l: key 8j + l/8, bytes 16*(l%8)
+            const int key = g0 + 8 * j + (l >> 3);
+            const uint32_t kk = (uint32_t)(key < comp_end ? key : c0);
+            dma_b128(kbase, kk * DI + 16 * (l & 7), (const DSA_LDS void *)&kst[wave][b][j * 1024]);
         }
         const int key = g0 + l;
-        ks = key < comp_end ? p.k_scale[ri.kv0 + key] : 0.f;
+        dma_b32(sbase, 4u * (uint32_t)(key < comp_end ? key : c0), (const DSA_LDS void *)&sst[wave][b][0]);
     };
-    auto compute = [&](int g0, const i32x8 (&kb)[4], float ks) {
+    auto compute = [&](int g0, int b) {
         float part[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
+            const uint8_t *kr = &kst[wave][b][(16 * st + row) * DI + 32 * grp];
+            const i32x4 lo = *reinterpret_cast<const i32x4 *>(kr);
+            const i32x4 hi = *reinterpret_cast<const i32x4 *>(kr + 16);
+            const i32x8 kb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             f32x4 c[4];
-            block_mfma(qa, kb[st], c);
+            block_mfma(qa, kb, c);
             part[st] = block_epilogue(c, wq);
         }
         const float v = reduce_scatter4(part);
+        const float ks = sst[wave][b][l];
         const int key = g0 + l;
         if (key < fill_end) p.scores[(int64_t)t * p.ld + key] = key < comp_end ? v * ks : -INFINITY;
     };
     constexpr int STRIDE = 64 * DC_WAVES;
-    i32x8 kA[4], kB[4];
-    float sA = 0.f, sB = 0.f;
     int g0 = c0 + 64 * wave;
-    if (g0 < fill_end) kload(g0, kA, sA);
-    // unrolled by two so that both key buffers stay in registers
-    for (; g0 < fill_end; g0 += 2 * STRIDE) {
-        if (g0 + STRIDE < fill_end) kload(g0 + STRIDE, kB, sB);
-        compute(g0, kA, sA);
-        if (g0 + STRIDE >= fill_end) break;
-        if (g0 + 2 * STRIDE < fill_end) kload(g0 + 2 * STRIDE, kA, sA);
-        compute(g0 + STRIDE, kB, sB);
+#pragma unroll
+    for (int j = 0; j < DC_NBUF; ++j)
+        if (g0 + j * STRIDE < fill_end) issue(g0 + j * STRIDE, j);
+    for (int i = 0; g0 < fill_end; g0 += STRIDE, ++i) {
+        // wait for this group's loads; the later groups' loads (at most
+        // DC_NBUF - 1 groups, issued after this one) may still fly
+        static_assert(DC_NBUF >= 1 && DC_NBUF <= 3, "vmcnt waits written for a ring of 1 to 3 groups");
+        const int ahead = (fill_end - 1 - g0) / STRIDE;   // groups after this one
+        const int fly = ahead < DC_NBUF - 1 ? ahead : DC_NBUF - 1;   // of them already issued
+        if (fly >= 2)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DC_LOADS - 16) | (1 << 14));   // vmcnt(2 * DC_LOADS) = 18
+        else if (fly == 1)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | DC_LOADS);   // vmcnt(DC_LOADS)
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+        const int b = i % DC_NBUF;
+        compute(g0, b);
+        if (g0 + DC_NBUF * STRIDE < fill_end) issue(g0 + DC_NBUF * STRIDE, b);
     }
 }
 
