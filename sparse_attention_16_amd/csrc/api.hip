@@ -34,11 +34,28 @@ size_t topk_ws(const dsa_batch *b, int k) {
     return 2 * up((size_t)b->total_q * nch * k * 4);
 }
 
-// Split-KV factor for the attention: enough workgroups to fill 256 CUs twice.
+// Compute units of the current device (256 on MI355X), queried once.
+int device_cus() {
+    static int ncu = 0;
+    if (ncu == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        ncu = n;
+    }
+    return ncu;
+}
+
+// Split-KV factor for the attention: enough workgroups to give every compute
+// unit one (the attention workgroup fills a compute unit's LDS, so a second
+// round of workgroups would repeat the per-workgroup query load and partial
+// write instead of overlapping them).
 int mla_splits(int T, int k) {
     const int nblk = (k + MLA_BK - 1) / MLA_BK;
-    if (T <= 0 || T >= 512) return 1;
-    int s = (512 + T - 1) / T;
+    const int ncu = device_cus();
+    if (T <= 0 || T >= ncu) return 1;
+    int s = (ncu + T - 1) / T;
     if (s > nblk) s = nblk;
     return s < 1 ? 1 : s;
 }
@@ -46,7 +63,7 @@ int mla_splits(int T, int k) {
 size_t mla_ws(const dsa_batch *b, int k) {
     const int s = mla_splits(b->total_q, k);
     if (s <= 1) return 0;
-    return up((size_t)b->total_q * s * kH * kDv * 4) + up((size_t)b->total_q * s * kH * 4);
+    return up((size_t)b->total_q * s * kH * kDv * 2) + up((size_t)b->total_q * s * kH * 4);
 }
 
 int64_t score_ld(int max_kv) { return ((int64_t)max_kv + 63) / 64 * 64; }
@@ -120,9 +137,9 @@ MlaParams make_mla(const dsa_batch *b, const uint16_t *q, const uint16_t *kv, co
     p.o_part = nullptr;
     p.lse_part = nullptr;
     if (p.splits > 1) {
-        p.o_part = reinterpret_cast<float *>(ws);
+        p.o_part = reinterpret_cast<uint16_t *>(ws);
         p.lse_part = reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                               up((size_t)b->total_q * p.splits * kH * kDv * 4));
+                                               up((size_t)b->total_q * p.splits * kH * kDv * 2));
     }
     return p;
 }

@@ -57,7 +57,7 @@ struct MlaParams {
     float *lse;             // [T, 128]
     int splits;             // workgroups per query row (split-KV)
     int blocks_per_split;   // MLA_BK-key blocks per split
-    float *o_part;          // [T, splits, 128, 512] (splits > 1)
+    uint16_t *o_part;       // [T, splits, 128, 512] bf16 (splits > 1)
     float *lse_part;        // [T, splits, 128]
 };
 

@@ -158,7 +158,7 @@ __device__ __forceinline__ void qk_drain(f32x4 (&s)[NHT][MT]) {
 // (no store of the kernel can clobber idx).
 __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     MlaParams p, const int32_t *__restrict__ idx, uint16_t *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ o_part, float *__restrict__ lse_part) {
+    float *__restrict__ lse, uint16_t *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t buf2[BUF_BYTES];
@@ -508,14 +508,21 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
                 *reinterpret_cast<bf16x4 *>(orow + 16 * ct) = v;
             }
         } else {
-            float *orow = o_part + (((int64_t)t * p.splits + split) * H + h) * DV + c0;
+            uint16_t *orow = o_part + (((int64_t)t * p.splits + split) * H + h) * DV + c0;
 #pragma unroll
-            for (int ct = 0; ct < CT_W; ++ct) *reinterpret_cast<f32x4 *>(orow + 16 * ct) = o[T][ct] * inv;
+            for (int ct = 0; ct < CT_W; ++ct) {
+                const bf16x4 v = {(__bf16)(o[T][ct][0] * inv), (__bf16)(o[T][ct][1] * inv),
+                                  (__bf16)(o[T][ct][2] * inv), (__bf16)(o[T][ct][3] * inv)};
+                *reinterpret_cast<bf16x4 *>(orow + 16 * ct) = v;
+            }
         }
     }
 }
 
 // Combines split partials: lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) o_s.
+// The partials o_s are normalised and stored in bf16 (half the bytes of the
+// round trip through memory; their rounding, 2^-9 relative, is of the order
+// of the final bf16 rounding of out); the combination runs in fp32.
 // Grid: x = query row, y = pair of heads; 128 threads x 4 value columns per head.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
     const int t = blockIdx.x;
@@ -534,9 +541,10 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
         for (int s = 0; s < S; ++s) {
             const float ls = lp[(int64_t)s * H];
             if (ls == -INFINITY) continue;
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(
+            const bf16x4 v = *reinterpret_cast<const bf16x4 *>(
                 p.o_part + (((int64_t)t * S + s) * H + h) * DV + c);
-            acc += v * expf(ls - L);
+            const float wgt = expf(ls - L);
+            acc += f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]} * wgt;
         }
     }
     const bf16x4 v = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
