@@ -50,10 +50,10 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     ("prefill_32k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "43ea6b7d2d7e0de9", "fetch_kib": 11415301, "write_kib": 4220696},
+        "sha256_16": "e382679c64b6de86", "fetch_kib": 11479831, "write_kib": 4353271},
     ("decode_64k", "indexer_decode_kernel"): {
         "sources": ("indexer.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "824953ea7f23f2f0", "fetch_kib": 289457, "write_kib": 17469},
+        "sha256_16": "b1b3ab6daf95ccb4", "fetch_kib": 289238, "write_kib": 17469},
 }
 
 
