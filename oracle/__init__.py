@@ -55,6 +55,9 @@ def lib():
         L.ora_sparse_attn.argtypes = [i32, p, p, p, p, i64, i32, i32, i32, dbl, p, i32, p, i32, p, i32, p, p]
         L.ora_dense_attn.argtypes = [i32, p, p, p, p, i64, i32, i32, i32, dbl, p, i32, p, i32, p, p]
         L.ora_num_threads.restype = i32
+        L.ora_e4m3_encode.argtypes = [ctypes.c_float]
+        L.ora_e4m3_encode.restype = ctypes.c_uint8
+        L.ora_quant_rows.argtypes = [p, i64, i64, p, p]
         _lib = L
     return _lib
 
@@ -100,6 +103,23 @@ def e4m3_table() -> np.ndarray:
     t = np.zeros(256, dtype=np.float64)
     lib().ora_e4m3_decode_all(_ptr(t))
     return t
+
+
+def e4m3_encode(y: float) -> int:
+    """Nearest E4M3FN code of the binary32 value y (ties to even, saturating)."""
+    return int(lib().ora_e4m3_encode(float(y)))
+
+
+def quant_rows(x: np.ndarray):
+    """Per-group absmax E4M3FN quantisation of x [rows, cols] (binary32):
+    returns (codes uint8 [rows, cols], scale float32 [rows])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scale = np.zeros(rows, dtype=np.float32)
+    if lib().ora_quant_rows(_ptr(x), rows, cols, _ptr(codes), _ptr(scale)) != 0:
+        raise ValueError("ora_quant_rows: bad arguments")
+    return codes, scale
 
 
 def bf16_value(bits: int) -> float:

@@ -36,6 +36,12 @@
  *      o[t,h,c] = sum_s exp(z_s - M) kv[s,c] / sum_s exp(z_s - M) for c < Dv,
  *      lse = M + ln(sum_s exp(z_s - M)), M = max z.  Exact softmax, not online.
  *   5. Dense causal attention: step 4 over every visible s (brute force).
+ *   6. FP8 quantisation of a row group, the step before the index score
+ *      ([R] "Молниеносный индексатор": the indexer runs on FP8 values): one
+ *      scale per group s = absmax / 448 (binary32; 1 for an all-zero group),
+ *      y = x / s (binary32), code = the E4M3FN code nearest to y by
+ *      exhaustive search over the finite codes, ties to the code with an even
+ *      mantissa; |y| above 448 takes 448; the sign bit is that of y.
  *
  * Batch description shared by every function: B sequences; query rows of
  * sequence b are [cu_q[b], cu_q[b+1]); its cache rows are
@@ -87,6 +93,51 @@ void ora_e4m3_decode_all(double *table256)
 {
     for (int c = 0; c < 256; c++)
         table256[c] = ora_e4m3_value((uint8_t)c);
+}
+
+/* E4M3FN code nearest to y (binary32), by exhaustive search over the finite
+ * non-negative codes 0x00..0x7E (their values increase with the code), ties to
+ * the even code (even mantissa); values above 448 take 448 (the largest finite
+ * code); the sign bit is copied from y.  NaN input is not supported. */
+uint8_t ora_e4m3_encode(float y)
+{
+    const double a = fabs((double)y);
+    int best = 0;
+    double bd = a;   /* distance to code 0 (value 0) */
+    for (int c = 1; c <= 0x7E; c++) {
+        const double d = fabs(ora_e4m3_value((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/* Quantises `rows` groups of `cols` binary32 values: scale[r] = absmax/448 of
+ * group r in binary32 (1 for an all-zero group), codes[r, i] =
+ * ora_e4m3_encode(x[r, i] / scale[r]) with the division in binary32. */
+int ora_quant_rows(const float *x, int64_t rows, int64_t cols, uint8_t *codes, float *scale)
+{
+    if (!x || !codes || !scale || rows < 0 || cols <= 0)
+        return ORA_ERR;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        const float *xr = x + r * cols;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < cols; i++) {
+            const float v = fabsf(xr[i]);
+            if (v > amax)
+                amax = v;
+        }
+        const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+        scale[r] = s;
+        for (int64_t i = 0; i < cols; i++) {
+            volatile float y = xr[i] / s;   /* rounded to binary32 here */
+            codes[r * cols + i] = ora_e4m3_encode(y);
+        }
+    }
+    return ORA_OK;
 }
 
 /* ------------------------------------------------------------ batch rows */
