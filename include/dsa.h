@@ -144,6 +144,34 @@ dsa_status dsa_prefill_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse,
 dsa_status dsa_decode_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse,
                           int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 
+/* FP8 quantisation of the indexer queries, the step before the index score
+ * ([R] "Молниеносный индексатор": the indexer runs on FP8 values).  Per
+ * token t, one scale over its HI x DI values:
+ *   s_t = absmax_t / 448 in fp32 (1 for an all-zero token),
+ *   q_fp8[t,j,d] = E4M3FN(q[t,j,d] / s_t): the division in fp32 (correctly
+ *   rounded), then the nearest E4M3FN code, ties to the even mantissa,
+ *   magnitudes above 448 saturate to 448, sign bit from the quotient;
+ *   q_scale[t,j] = s_t for every head j.
+ *   q [T, HI, DI] fp32 (finite)   q_fp8 [T, HI, DI] uint8 out   q_scale [T, HI] fp32 out
+ * HI = 64, DI = 128 (else DSA_ERR_UNSUPPORTED).  All pointers device, 16-byte
+ * aligned, caller-owned; the call only enqueues work on `stream`. */
+dsa_status dsa_quantize_queries(const float *q, int64_t T, int HI, int DI, uint8_t *q_fp8,
+                                float *q_scale, void *stream);
+
+/* Cache append: the R new tokens' indexer keys are quantised as above, one
+ * scale per key row (k_scale[row] = absmax/448), and written with their scale
+ * to rows dst_rows[r] of the FP8 key cache; their bf16 latent rows are copied
+ * to the same rows of the latent cache.  Rows r whose dst_rows[r] lies
+ * outside [0, N) are skipped.
+ *   k_new [R, DI] fp32 (finite)   kv_new [R, D] bf16 bits (NULL: keys only)
+ *   dst_rows [R] int64 device
+ *   k_fp8 [N, DI] uint8, k_scale [N] fp32, kv [N, D] bf16 (NULL with kv_new NULL)
+ * DI = 128, D = 576 (else DSA_ERR_UNSUPPORTED).  Device pointers, 16-byte
+ * aligned; rows of one call must be distinct (else the last write wins). */
+dsa_status dsa_append_cache(const float *k_new, const uint16_t *kv_new, int64_t R, int DI, int D,
+                            const int64_t *dst_rows, uint8_t *k_fp8, float *k_scale, uint16_t *kv,
+                            int64_t N, void *stream);
+
 typedef enum {
     DSA_WS_TOPK = 0,
     DSA_WS_SPARSE_MLA = 1,

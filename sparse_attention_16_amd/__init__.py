@@ -31,7 +31,8 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE = range(4)
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_fwd",
-           "dsa_decode_fwd", "dsa_workspace_size", "dsa_status_string", "dsa_version")
+           "dsa_decode_fwd", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
+           "dsa_status_string", "dsa_version")
 
 
 class DsaError(RuntimeError):
@@ -64,6 +65,8 @@ _lib.dsa_sparse_mla_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P,
 _lib.dsa_prefill_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_decode_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_workspace_size.argtypes = [_I, _BP, _I, _I, _I]
+_lib.dsa_quantize_queries.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
+_lib.dsa_append_cache.argtypes = [_P, _P, _I64, _I, _I, _P, _P, _P, _P, _I64, _P]
 _lib.dsa_workspace_size.restype = _SZ
 _lib.dsa_status_string.argtypes = [_I]
 _lib.dsa_status_string.restype = ctypes.c_char_p
@@ -145,6 +148,26 @@ def indexer_scores(batch: Batch, q_fp8, q_scale, w, k_fp8, k_scale, scores, ld=N
                                  _ptr(scores), int(ld), _stream(stream))
     _check(st, "dsa_indexer_scores")
     return scores
+
+
+def quantize_queries(q, q_fp8, q_scale, stream=None):
+    """FP8 E4M3FN quantisation of indexer queries q [T, 64, 128] fp32 into
+    q_fp8 [T, 64, 128] uint8 and q_scale [T, 64] fp32 (see dsa_quantize_queries)."""
+    st = _lib.dsa_quantize_queries(_ptr(q), q.shape[0], q.shape[1], q.shape[2], _ptr(q_fp8), _ptr(q_scale),
+                                   _stream(stream))
+    _check(st, "dsa_quantize_queries")
+    return q_fp8, q_scale
+
+
+def append_cache(k_new, kv_new, dst_rows, k_fp8, k_scale, kv, stream=None):
+    """Quantise new indexer keys k_new [R, 128] fp32 into rows dst_rows of the
+    FP8 key cache (k_fp8 [N, 128] uint8, k_scale [N] fp32) and copy the new
+    latent rows kv_new [R, 576] bf16 (or None) into kv [N, 576] (see
+    dsa_append_cache)."""
+    D = kv.shape[1] if kv is not None else 576
+    st = _lib.dsa_append_cache(_ptr(k_new), _ptr(kv_new), k_new.shape[0], k_new.shape[1], D, _ptr(dst_rows),
+                               _ptr(k_fp8), _ptr(k_scale), _ptr(kv), k_fp8.shape[0], _stream(stream))
+    _check(st, "dsa_append_cache")
 
 
 def topk(batch: Batch, scores, k: int, idx, ld=None, ws=None, stream=None):

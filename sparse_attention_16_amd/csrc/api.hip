@@ -202,6 +202,33 @@ dsa_status run_fwd(const dsa_fwd_args *a, uint16_t *out, float *lse, int32_t *id
 
 extern "C" {
 
+dsa_status dsa_quantize_queries(const float *q, int64_t T, int HI, int DI, uint8_t *q_fp8,
+                                float *q_scale, void *stream) {
+    if (HI != kHI || DI != kDI) return DSA_ERR_UNSUPPORTED;
+    if (T < 0) return DSA_ERR_INVALID_ARG;
+    if (T == 0) return DSA_OK;
+    if (T > INT32_MAX) return DSA_ERR_UNSUPPORTED;
+    if (!q || !q_fp8 || !q_scale || !al16(q) || !al16(q_fp8) || !al16(q_scale)) return DSA_ERR_INVALID_ARG;
+    return hip_status(launch_quant_queries(q, T, q_fp8, q_scale, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status dsa_append_cache(const float *k_new, const uint16_t *kv_new, int64_t R, int DI, int D,
+                            const int64_t *dst_rows, uint8_t *k_fp8, float *k_scale, uint16_t *kv,
+                            int64_t N, void *stream) {
+    if (DI != kDI || D != kD) return DSA_ERR_UNSUPPORTED;
+    if (R < 0 || N < 0) return DSA_ERR_INVALID_ARG;
+    if (R == 0) return DSA_OK;
+    if (R > (int64_t)INT32_MAX * 8) return DSA_ERR_UNSUPPORTED;
+    if (!k_new || !dst_rows || !k_fp8 || !k_scale) return DSA_ERR_INVALID_ARG;
+    if ((kv_new == nullptr) != (kv == nullptr)) return DSA_ERR_INVALID_ARG;
+    const void *ptrs[] = {k_new, dst_rows, k_fp8, k_scale};
+    for (const void *p : ptrs)
+        if (!al16(p)) return DSA_ERR_INVALID_ARG;
+    if (kv_new && (!al16(kv_new) || !al16(kv))) return DSA_ERR_INVALID_ARG;
+    return hip_status(launch_append_cache(k_new, kv_new, R, dst_rows, k_fp8, k_scale, kv, N,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_indexer_scores(const dsa_batch *batch, const uint8_t *q_fp8, const float *q_scale,
                               const float *w, const uint8_t *k_fp8, const float *k_scale, int HI,
                               int DI, float *scores, int64_t ld, void *stream) {

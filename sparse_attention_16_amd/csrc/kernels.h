@@ -69,5 +69,8 @@ hipError_t launch_indexer(const IndexerParams &p, int T, int max_q, bool decode_
                           hipStream_t s);
 hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s);
+hipError_t launch_quant_queries(const float *q, int64_t T, uint8_t *q_fp8, float *q_scale, hipStream_t s);
+hipError_t launch_append_cache(const float *k_new, const uint16_t *kv_new, int64_t R, const int64_t *dst,
+                               uint8_t *k_fp8, float *k_scale, uint16_t *kv, int64_t N, hipStream_t s);
 
 }  // namespace dsa

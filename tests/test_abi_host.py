@@ -144,3 +144,22 @@ def test_tiny_fp32_configuration_is_unsupported(dsa):
     b = _batch(dsa, 256, 256)
     a = dsa.dsa_fwd_args(b, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 8, 80, 64, 32, 80 ** -0.5)
     assert lib.dsa_prefill_fwd(ctypes.byref(a), FAKE, FAKE, None, FAKE, 1 << 40, None) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_quantize_and_append_validation(dsa):
+    lib = dsa.raw_lib()
+    # queries: shape support, null / misaligned pointers, empty input
+    assert lib.dsa_quantize_queries(FAKE, 4, 32, 128, FAKE, FAKE, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_quantize_queries(FAKE, 4, 64, 64, FAKE, FAKE, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_quantize_queries(None, 4, 64, 128, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_quantize_queries(FAKE, 4, 64, 128, FAKE + 8, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_quantize_queries(FAKE, -1, 64, 128, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_quantize_queries(None, 0, 64, 128, None, None, None) == dsa.DSA_OK
+    # cache append
+    assert lib.dsa_append_cache(FAKE, FAKE, 4, 64, 576, FAKE, FAKE, FAKE, FAKE, 100, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_append_cache(FAKE, FAKE, 4, 128, 512, FAKE, FAKE, FAKE, FAKE, 100, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_append_cache(FAKE, FAKE, 4, 128, 576, None, FAKE, FAKE, FAKE, 100, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_append_cache(FAKE, None, 4, 128, 576, FAKE, FAKE, FAKE, FAKE, 100, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_append_cache(FAKE, FAKE, 4, 128, 576, FAKE, FAKE, FAKE + 4, FAKE, 100, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_append_cache(FAKE, FAKE, -1, 128, 576, FAKE, FAKE, FAKE, FAKE, 100, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_append_cache(None, None, 0, 128, 576, None, None, None, None, 0, None) == dsa.DSA_OK
