@@ -37,6 +37,7 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
 HI, DI, H, D, DV = 64, 128, 128, 576, 512
+SEED_QUANT = 0xD5A6        # seed of the quantise + append inputs
 
 # HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch, one run each).  The raw
@@ -162,6 +163,99 @@ def cpu_baseline(wl, target_s=15.0):
                       f"{dt:.1f} s wall"}
 
 
+# ---------------------------------------------------------- quantise + append
+
+QUANT_METRIC = "FP8 quantise + cache append tokens/s (indexer queries and keys, latent rows), 32K prefill"
+
+
+def quant_append_bench(args, dsa):
+    """One step = the 32768 new tokens of a 32K prefill: their indexer queries
+    [T, 64, 128] fp32 quantised to E4M3FN with one scale per token, their
+    indexer keys [T, 128] fp32 quantised (one scale per key) and appended to the
+    FP8 key cache, their bf16 latent rows [T, 576] appended to the latent cache.
+    Inputs are seeded standard normals (the distribution the index-score
+    inputs are drawn from), resident in HBM."""
+    import torch
+    say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+    T = N = 32768
+    g = torch.Generator("cuda").manual_seed(SEED_QUANT)
+    q = torch.randn((T, HI, DI), dtype=torch.float32, device="cuda", generator=g)
+    k_new = torch.randn((T, DI), dtype=torch.float32, device="cuda", generator=g)
+    kv_new = torch.randn((T, D), dtype=torch.float32, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+    dst = torch.arange(T, dtype=torch.int64, device="cuda")
+    q_fp8 = torch.empty((T, HI, DI), dtype=torch.uint8, device="cuda")
+    q_scale = torch.empty((T, HI), dtype=torch.float32, device="cuda")
+    k_fp8 = torch.empty((N, DI), dtype=torch.uint8, device="cuda")
+    k_scale = torch.empty((N,), dtype=torch.float32, device="cuda")
+    kv = torch.empty((N, D), dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+    say(f"[bench] workload quant_append_32k: T={T} tokens, cache rows N={N}")
+
+    def step():
+        dsa.quantize_queries(q, q_fp8, q_scale)
+        dsa.append_cache(k_new, kv_new, dst, k_fp8, k_scale, kv)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = T * args.steps / elapsed
+    say(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, {tokens_per_s:,.0f} tokens/s")
+
+    # dominant kernel: the query quantiser (4 B read + 1 B written per value, 64 scales per token)
+    stream = torch.cuda.current_stream()
+    nbytes = T * HI * DI * (4 + 1) + T * HI * 4
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        dsa.quantize_queries(q, q_fp8, q_scale)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    achieved = nbytes / (kms * 1e-3) / 1e9
+    roof = {"kernel": "quant_groups_kernel<8192,256>", "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None, "avg_ms": round(kms, 4), "algorithmic_bytes": nbytes}
+    say(f"[bench] query quantiser: {kms:.3f} ms/launch, {achieved:.1f} GB/s ({100 * roof['frac']:.1f}% of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        say("[bench] timing the CPU oracle on a sample of the workload ...")
+        threads = oracle.num_threads()
+
+        def run(n):
+            rows = np.unique(np.linspace(0, T - 1, n).astype(np.int64))
+            x = q[torch.from_numpy(rows).cuda()].reshape(len(rows), HI * DI).cpu().numpy()
+            kx = k_new[torch.from_numpy(rows).cuda()].cpu().numpy()
+            t1 = time.perf_counter()
+            oracle.quant_rows(x)
+            oracle.quant_rows(kx)
+            return len(rows), time.perf_counter() - t1
+        n0, dt = run(64)
+        n = int(min(T, max(64, args.cpu_seconds / max(dt / n0, 1e-9))))
+        n, dt = run(n)
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n} tokens evenly spaced over the {T} of the workload (query and key "
+                         f"quantisation; the latent copy is not timed), {dt:.1f} s wall"}
+        say(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s on {threads} threads")
+
+    cfg = {"workload": "quant_append_32k", "query_tokens": T, "cache_rows": N, "indexer_heads": HI,
+           "indexer_dim": DI, "d_latent": D, "entry": "dsa_quantize_queries + dsa_append_cache"}
+    line = {"metric": QUANT_METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32->e4m3",
+            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------- bench
 
 def main(argv=None):
@@ -170,7 +264,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_32k",
-                    choices=["prefill_32k", "prefill_4k", "decode_64k", "chunked_128k"])
+                    choices=["prefill_32k", "prefill_4k", "decode_64k", "chunked_128k", "quant_append_32k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=5,
@@ -198,6 +292,8 @@ def main(argv=None):
         return 0
     import sparse_attention_16_amd as dsa
 
+    if args.workload == "quant_append_32k":
+        return quant_append_bench(args, dsa)
     wl, entry = make_workload(args.workload)
     b = wl.batch
     say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731

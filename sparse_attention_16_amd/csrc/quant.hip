@@ -9,10 +9,14 @@
 //   code = E4M3FN(x / s): the nearest code to the binary32 quotient, ties to
 //          the even mantissa, magnitudes above 448 saturate to 448, the sign
 //          bit follows the quotient.
-// The division is the correctly rounded binary32 division; the rounding to
+// The quotient is the correctly rounded binary32 division; the rounding to
 // E4M3FN is done in software (exact power-of-two scaling, then round to
 // nearest even on the scaled value), so the codes do not depend on the
-// hardware conversion's saturation mode.
+// hardware conversion's saturation mode.  The code only depends on which side
+// of an E4M3FN rounding midpoint the quotient lies, so it is first taken from
+// x * RN(1/s), which is within 2 ulp of the correctly rounded quotient; a
+// value whose product lies within 2^-16 (scaled units, far more than 2 ulp)
+// of a midpoint is redone with the correctly rounded division.
 //
 // HBM-bound: 4 bytes read and 1 byte written per value, one group per 32 (key)
 // or 256 (query) threads, 16-byte loads.
@@ -23,18 +27,23 @@ namespace dsa {
 
 namespace {
 
-// E4M3FN code of a binary32 value (round to nearest even, saturating).
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+// E4M3FN code of a binary32 value (round to nearest even, saturating).  When
+// near is given, it is set if y lies within 2^-16 of a rounding midpoint in
+// the scaled units (value / code step).
+__device__ __forceinline__ uint32_t e4m3_rne(float y, bool *near = nullptr) {
     const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
     const float a = fabsf(y);
     uint32_t code;
+    float t = 0.f;                                       // value in code steps
     if (a >= 448.f) {
         code = 0x7Eu;                                    // largest finite value
     } else if (a < 0.015625f) {                          // below 2^-6: steps of 2^-9
-        code = (uint32_t)rintf(a * 512.f);               // 0..8; 8 is 2^-6, code 0x08
+        t = a * 512.f;
+        code = (uint32_t)rintf(t);                       // 0..8; 8 is 2^-6, code 0x08
     } else {
         int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // -6 .. 8
-        uint32_t m = (uint32_t)rintf(ldexpf(a, 3 - e));            // 8 .. 16
+        t = ldexpf(a, 3 - e);                                      // [8, 16)
+        uint32_t m = (uint32_t)rintf(t);                           // 8 .. 16
         if (m == 16u) {
             m = 8u;
             e += 1;
@@ -42,6 +51,7 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
         code = ((uint32_t)(e + 7) << 3) | (m - 8u);
         code = code > 0x7Eu ? 0x7Eu : code;
     }
+    if (near) *near = fabsf(t - truncf(t) - 0.5f) < 1.52587890625e-5f;   // 2^-16 (saturated: t = 0, false)
     return code | sign;
 }
 
@@ -87,6 +97,7 @@ __global__ __launch_bounds__(256) void quant_groups_kernel(const float *__restri
         for (int w = 0; w < (NT + 63) / 64; ++w) amax = fmaxf(amax, red[g][w]);
     }
     const float s = amax == 0.f ? 1.f : amax / 448.f;
+    const float rs = 1.f / s;    // correctly rounded reciprocal
 
     if (orow < 0 || orow >= nout) return;
     uint8_t *cr = codes + orow * COLS;
@@ -94,7 +105,12 @@ __global__ __launch_bounds__(256) void quant_groups_kernel(const float *__restri
     for (int u = 0; u < VPT / 4; ++u) {
         uint32_t packed = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) packed |= e4m3_rne(v[4 * u + j] / s) << (8 * j);
+        for (int j = 0; j < 4; ++j) {
+            bool near;
+            uint32_t c = e4m3_rne(v[4 * u + j] * rs, &near);
+            if (near) c = e4m3_rne(v[4 * u + j] / s);   // rare: the exact quotient decides
+            packed |= c << (8 * j);
+        }
         *reinterpret_cast<uint32_t *>(cr + 4 * (i + NT * u)) = packed;
     }
     for (int j = i; j < rep; j += NT) scale[orow * rep + j] = s;
