@@ -55,6 +55,9 @@ COUNTERS = {
     ("decode_64k", "indexer_decode_kernel"): {
         "sources": ("indexer.hip", "dsa_device.h", "kernels.h", "api.hip"),
         "sha256_16": "b1b3ab6daf95ccb4", "fetch_kib": 289238, "write_kib": 17469},
+    ("quant_append_32k", "quant_groups_kernel<8192,256>"): {
+        "sources": ("quant.hip", "dsa_device.h", "kernels.h", "api.hip"),
+        "sha256_16": "bcacf21ceb2dd66d", "fetch_kib": 524451, "write_kib": 270336},
 }
 
 
@@ -222,6 +225,11 @@ def quant_append_bench(args, dsa):
     roof = {"kernel": "quant_groups_kernel<8192,256>", "bound": "hbm", "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": None, "avg_ms": round(kms, 4), "algorithmic_bytes": nbytes}
+    tr = measured_traffic("quant_append_32k", "quant_groups_kernel<8192,256>")
+    if tr is not None:
+        roof["traffic"] = round(tr["fetch"] + tr["write"])
+        roof["traffic_unit"] = "bytes/launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
+        roof["traffic_fetch"], roof["traffic_write"] = round(tr["fetch"]), round(tr["write"])
     say(f"[bench] query quantiser: {kms:.3f} ms/launch, {achieved:.1f} GB/s ({100 * roof['frac']:.1f}% of peak)")
 
     cpu = None
