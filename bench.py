@@ -38,6 +38,7 @@ PEAK_HBM_GBS = 8000.0
 
 HI, DI, H, D, DV = 64, 128, 128, 576, 512
 SEED_QUANT = 0xD5A6        # seed of the quantise + append inputs
+SEED_SHORT = 0xD5A7        # seed of the short-prompt (2048-token) prefill
 
 # HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch, one run each).  The raw
@@ -134,6 +135,9 @@ def make_workload(name):
         return synth.decode(64), "decode"
     if name == "chunked_128k":
         return synth.chunked_prefill(4096, 131072), "prefill"
+    if name == "short_prefill_2k":
+        # every row sees at most k keys: the fused entry runs the short-sequence mode
+        return synth.prefill(2048, seed=SEED_SHORT), "prefill"
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -272,7 +276,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_32k",
-                    choices=["prefill_32k", "prefill_4k", "decode_64k", "chunked_128k", "quant_append_32k"])
+                    choices=["prefill_32k", "prefill_4k", "decode_64k", "chunked_128k", "quant_append_32k",
+                             "short_prefill_2k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=5,
@@ -340,7 +345,18 @@ def main(argv=None):
     # ---- dominant kernel, timed alone with HIP events on its stream
     nvis = visible_counts(b.cu_q, b.cu_kv, b.pos0)
     stream = torch.cuda.current_stream()
-    if entry == "prefill":
+    short = b.max_kv <= wl.k
+    if short:
+        # short-sequence mode: the attention kernel over every visible key
+        name = "sparse_mla_kernel"
+        flops = dense_mla_flops(nvis)
+        mws = torch.empty(max(1, dsa.workspace_size(dsa.WS_DENSE_MLA, batch, 1)),
+                          dtype=torch.uint8, device="cuda")
+        out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+
+        def kernel():
+            dsa.dense_mla_fwd(batch, dev["q"], dev["kv"], wl.scale, out2, lse2, ws=mws)
+    elif entry == "prefill":
         name = "sparse_mla_kernel"
         flops = mla_flops(nvis, wl.k)
         mws = torch.empty(max(1, dsa.workspace_size(dsa.WS_SPARSE_MLA, batch, wl.k)),
@@ -387,6 +403,35 @@ def main(argv=None):
     say(f"[bench] {name}: {kms:.3f} ms/launch, {roof['achieved']} {roof['unit']} "
         f"({100 * roof['frac']:.1f}% of peak)")
 
+    three = None
+    if short:
+        # the same forward through the three separate steps (indexer -> top-k ->
+        # sparse attention over the -1 padded selection), for comparison
+        ld = ((b.max_kv + 63) // 64) * 64
+        scores = torch.empty((b.T, ld), dtype=torch.float32, device="cuda")
+        idx3 = torch.empty_like(idx)
+        tws = torch.empty(max(1, dsa.workspace_size(dsa.WS_TOPK, batch, wl.k)), dtype=torch.uint8, device="cuda")
+        sws = torch.empty(max(1, dsa.workspace_size(dsa.WS_SPARSE_MLA, batch, wl.k)), dtype=torch.uint8,
+                          device="cuda")
+
+        def three_step():
+            dsa.indexer_scores(batch, dev["qi"], dev["qs"], dev["w"], dev["ki"], dev["ks"], scores)
+            dsa.topk(batch, scores, wl.k, idx3, ws=tws)
+            dsa.sparse_mla_fwd(batch, dev["q"], dev["kv"], idx3, wl.scale, out2, lse2, ws=sws)
+        three_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            three_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t3 = e0.elapsed_time(e1) / args.steps
+        three = {"three_step_ms": round(t3, 4), "short_mode_ms": round(ms_per_step, 4),
+                 "speedup": round(t3 / ms_per_step, 3)}
+        say(f"[bench] indexer -> top-k -> sparse attention on the same inputs: {t3:.3f} ms/step "
+            f"({three['speedup']:.2f}x the short-sequence mode's time)")
+
     cpu = None
     if not args.no_cpu_baseline:
         say("[bench] timing the CPU oracle on a sample of the workload ...")
@@ -403,6 +448,9 @@ def main(argv=None):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "fp8+bf16", "data": "synthetic", "config": cfg, "roofline": roof,
             "cpu_baseline": cpu}
+    if three is not None:
+        cfg["entry"] += " (short-sequence mode: no indexer, no select)"
+        line["short_mode"] = three
     print(json.dumps(line), flush=True)
     return 0
 

@@ -115,6 +115,27 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const uint16_t *q, const u
                               uint16_t *out, float *lse, void *ws, size_t ws_bytes,
                               void *stream);
 
+/* "MHA with mask", the short-sequence mode of [R] "Стоимость": for short
+ * sequences the pages run a separate masked dense mode that reproduces DSA's
+ * result.  Each query row attends to every key it can see (positions
+ * 0..min(pos, ctx_b-1)), with the same arithmetic, layouts and outputs as
+ * dsa_sparse_mla_fwd:
+ *   z_s = scale * sum_{d<D} q[t,h,d] * kv[s,d]     for s = 0 .. nvis_t - 1
+ *   out[t,h,c] = sum_s softmax(z)_s * kv[s,c]  (c < Dv),  lse[t,h] = ln sum_s exp(z_s)
+ * Where every row sees at most k keys, DSA's top-k keeps all of them, so
+ * this equals the indexer -> top-k -> dsa_sparse_mla_fwd path (the fused
+ * entries below switch to it on their own).  No scores, no idx.  The
+ * attention stays in MLA's latent (MQA) form over the 576-dim cache rows; a
+ * per-head decompressed form would need the up-projections, which are not
+ * inputs of this library.
+ *   q [T, H, D] bf16, kv [N, D] bf16, out [T, H, Dv] bf16, lse [T, H] fp32
+ * Supported: max_kv <= 2048 (else DSA_ERR_UNSUPPORTED).  A row that sees no
+ * key gives out = 0, lse = -inf.  Workspace:
+ * dsa_workspace_size(DSA_WS_DENSE_MLA, ...) (split-KV partials; may be 0). */
+dsa_status dsa_dense_mla_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, int H, int D,
+                             int Dv, float scale, uint16_t *out, float *lse, void *ws, size_t ws_bytes,
+                             void *stream);
+
 /* All inputs of one DSA forward (indexer + top-k + sparse MQA attention). */
 typedef struct {
     dsa_batch batch;
@@ -136,6 +157,11 @@ typedef struct {
  * dsa_prefill_fwd is tuned for many query rows per sequence (prefill, chunked
  * prefill); dsa_decode_fwd for one or a few query rows per sequence over long
  * contexts (split-KV).  Both accept any batch.
+ * Short sequences: when every context fits in k (max_kv <= k) the top-k of
+ * each row is all of its visible keys, so both entries skip the indexer and
+ * the select, write that selection to idx_out, and run the dense masked
+ * attention of dsa_dense_mla_fwd (the "MHA with mask" mode of [R]
+ * "Стоимость"); out and lse are bit-identical to the three-step path.
  *   out [T, H, Dv] bf16, lse [T, H] fp32, idx_out [T, k] int32 (nullable:
  *   the selected positions, as dsa_topk returns them).
  * Workspace: dsa_workspace_size(DSA_WS_PREFILL or DSA_WS_DECODE, ...). */
@@ -176,7 +202,8 @@ typedef enum {
     DSA_WS_TOPK = 0,
     DSA_WS_SPARSE_MLA = 1,
     DSA_WS_PREFILL = 2,
-    DSA_WS_DECODE = 3
+    DSA_WS_DECODE = 3,
+    DSA_WS_DENSE_MLA = 4       /* k is ignored (pass any 1..2048) */
 } dsa_ws_entry;
 
 /* Workspace bytes the given entry point needs for this batch (host only; reads

@@ -7,7 +7,8 @@ memory and streams only.  Importing this package fails loudly when the built
 library is missing: there is no fallback implementation.
 
 Entry points (same names as the C ABI, without the ``dsa_`` prefix):
-    indexer_scores, topk, sparse_mla_fwd, prefill_fwd, decode_fwd,
+    indexer_scores, topk, sparse_mla_fwd, dense_mla_fwd, prefill_fwd, decode_fwd,
+    quantize_queries, append_cache,
     workspace_size, status_string, version
 """
 from __future__ import annotations
@@ -28,9 +29,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
-WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE = range(4)
+WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE, WS_DENSE_MLA = range(5)
 
-EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_fwd",
+EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_dense_mla_fwd", "dsa_prefill_fwd",
            "dsa_decode_fwd", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
            "dsa_status_string", "dsa_version")
 
@@ -62,6 +63,7 @@ _BP = ctypes.POINTER(dsa_batch)
 _lib.dsa_indexer_scores.argtypes = [_BP, _P, _P, _P, _P, _P, _I, _I, _P, _I64, _P]
 _lib.dsa_topk.argtypes = [_BP, _P, _I64, _I, _P, _P, _SZ, _P]
 _lib.dsa_sparse_mla_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
+_lib.dsa_dense_mla_fwd.argtypes = [_BP, _P, _P, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
 _lib.dsa_prefill_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_decode_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_workspace_size.argtypes = [_I, _BP, _I, _I, _I]
@@ -189,6 +191,16 @@ def sparse_mla_fwd(batch: Batch, q, kv, idx, scale: float, out, lse, Dv: int = 5
                                  q.shape[1], q.shape[2], int(Dv), float(scale), _ptr(out), _ptr(lse),
                                  _ptr(ws), nbytes, _stream(stream))
     _check(st, "dsa_sparse_mla_fwd")
+    return out, lse
+
+
+def dense_mla_fwd(batch: Batch, q, kv, scale: float, out, lse, Dv: int = 512, ws=None, stream=None):
+    """Dense masked attention of every row over all its visible keys, the
+    short-sequence mode (see dsa_dense_mla_fwd)."""
+    ws, nbytes = _workspace(WS_DENSE_MLA, batch, 1, ws, q.device)
+    st = _lib.dsa_dense_mla_fwd(ctypes.byref(batch.c), _ptr(q), _ptr(kv), q.shape[1], q.shape[2], int(Dv),
+                                float(scale), _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "dsa_dense_mla_fwd")
     return out, lse
 
 

@@ -68,6 +68,9 @@ size_t mla_ws(const dsa_batch *b, int k) {
 
 int64_t score_ld(int max_kv) { return ((int64_t)max_kv + 63) / 64 * 64; }
 
+// Slot budget of the dense attention: the longest context (at least 1).
+int dense_slots(const dsa_batch *b) { return b->max_kv < 1 ? 1 : b->max_kv; }
+
 size_t fwd_ws(const dsa_batch *b, int k) {
     return up((size_t)b->total_q * score_ld(b->max_kv) * 4) + up((size_t)b->total_q * k * 4) +
            topk_ws(b, k) + mla_ws(b, k);
@@ -116,7 +119,7 @@ TopkParams make_topk(const dsa_batch *b, const float *scores, int64_t ld, int k,
 }
 
 MlaParams make_mla(const dsa_batch *b, const uint16_t *q, const uint16_t *kv, const int32_t *idx,
-                   int k, float scale, uint16_t *out, float *lse, void *ws) {
+                   int k, float scale, uint16_t *out, float *lse, void *ws, int dense = 0) {
     MlaParams p;
     p.cu_q = b->cu_q;
     p.cu_kv = b->cu_kv;
@@ -128,6 +131,7 @@ MlaParams make_mla(const dsa_batch *b, const uint16_t *q, const uint16_t *kv, co
     p.kv = kv;
     p.idx = idx;
     p.k = k;
+    p.dense = dense;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.out = out;
     p.lse = lse;
@@ -185,6 +189,19 @@ dsa_status run_fwd(const dsa_fwd_args *a, uint16_t *out, float *lse, int32_t *id
     void *tws = w;
     w += topk_ws(b, a->k);
     void *mws = w;
+
+    // Short sequences (every context within k): the select keeps every visible
+    // key, so the result is dense causal attention.  Run it without scoring or
+    // selecting ("MHA with mask"); the split layout is the one the three-step
+    // path uses for this k, so both give the same bits.
+    if (b->max_kv <= a->k) {
+        if (idx_out) {
+            TopkParams tp = make_topk(b, nullptr, 0, a->k, idx_out, nullptr);
+            if ((st = hip_status(launch_select_all_visible(tp, b->total_q, s))) != DSA_OK) return st;
+        }
+        MlaParams mp = make_mla(b, a->q, a->kv, nullptr, a->k, a->scale, out, lse, mws, 1);
+        return hip_status(launch_sparse_mla(mp, b->total_q, s));
+    }
 
     if (b->max_kv > 0) {
         IndexerParams ip = make_indexer(b, a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, scores,
@@ -282,6 +299,25 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const uint16_t *q, const u
     return hip_status(launch_sparse_mla(p, batch->total_q, static_cast<hipStream_t>(stream)));
 }
 
+dsa_status dsa_dense_mla_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, int H, int D,
+                             int Dv, float scale, uint16_t *out, float *lse, void *ws, size_t ws_bytes,
+                             void *stream) {
+    dsa_status st = check_batch(batch);
+    if (st != DSA_OK) return st;
+    if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
+    if (batch->max_kv > kKMax) return DSA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return DSA_ERR_INVALID_ARG;
+    if (batch->total_q == 0) return DSA_OK;
+    if (!q || !out || !lse) return DSA_ERR_INVALID_ARG;
+    if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
+    if (!al16(q) || !al16(out) || !al16(lse) || (kv && !al16(kv))) return DSA_ERR_INVALID_ARG;
+    const int kd = dense_slots(batch);
+    const size_t need = mla_ws(batch, kd);
+    if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
+    MlaParams p = make_mla(batch, q, kv, nullptr, kd, scale, out, lse, ws, 1);
+    return hip_status(launch_sparse_mla(p, batch->total_q, static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_prefill_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse, int32_t *idx_out,
                            void *ws, size_t ws_bytes, void *stream) {
     return run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, false);
@@ -301,6 +337,7 @@ size_t dsa_workspace_size(dsa_ws_entry entry, const dsa_batch *batch, int k, int
         case DSA_WS_SPARSE_MLA: return mla_ws(batch, k);
         case DSA_WS_PREFILL:
         case DSA_WS_DECODE: return fwd_ws(batch, k);
+        case DSA_WS_DENSE_MLA: return batch->max_kv > kKMax ? 0 : mla_ws(batch, dense_slots(batch));
     }
     return 0;
 }

@@ -50,8 +50,9 @@ struct MlaParams {
     int max_kv;
     const uint16_t *q;      // [T, 128, 576] bf16
     const uint16_t *kv;     // [N, 576] bf16
-    const int32_t *idx;     // [T, k]
-    int k;
+    const int32_t *idx;     // [T, k] (unused when dense)
+    int k;                  // slots per row (dense: the slot budget, >= every row's visible count)
+    int dense;              // 1: slot j of a row is position j for j < its visible count (idx unused)
     float scale_log2;       // softmax scale * log2(e)
     uint16_t *out;          // [T, 128, 512] bf16
     float *lse;             // [T, 128]
@@ -68,6 +69,7 @@ constexpr int MLA_BK = 32;            // keys per gathered block
 hipError_t launch_indexer(const IndexerParams &p, int T, int max_q, bool decode_variant,
                           hipStream_t s);
 hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s);
+hipError_t launch_select_all_visible(const TopkParams &p, int T, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s);
 hipError_t launch_quant_queries(const float *q, int64_t T, uint8_t *q_fp8, float *q_scale, hipStream_t s);
 hipError_t launch_append_cache(const float *k_new, const uint16_t *kv_new, int64_t R, const int64_t *dst,

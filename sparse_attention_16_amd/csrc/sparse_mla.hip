@@ -168,7 +168,9 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     __shared__ float lsh[H];
     __shared__ int restart_flag[NWAVES];
 
-    const int t = blockIdx.x, split = blockIdx.y;
+    // rows in reverse order: in a causal batch the last rows see the most keys,
+    // so the longest rows start first and the short ones fill the tail
+    const int t = (int)gridDim.x - 1 - (int)blockIdx.x, split = blockIdx.y;
     const int wave = threadIdx.x >> 6, l = lane_id();
     const int row16 = l & 15, grp = l >> 4;
     const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
@@ -177,9 +179,13 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     const int j0 = split * p.blocks_per_split * BK;
     int j1 = j0 + p.blocks_per_split * BK;
     j1 = j1 < p.k ? j1 : p.k;
-    const int nsel = (j1 > j0 && ri.ctx > 0) ? j1 - j0 : 0;
+    int nsel = (j1 > j0 && ri.ctx > 0) ? j1 - j0 : 0;
+    if (p.dense) {   // the row's visible keys 0 .. nvis-1, in order
+        const int je = ri.nvis < j1 ? ri.nvis : j1;
+        nsel = je > j0 ? je - j0 : 0;
+    }
     const int32_t *__restrict__ idx_row = idx + (int64_t)t * p.k + j0;
-    const int nblk = (nsel + BK - 1) / BK;
+    int nblk = (nsel + BK - 1) / BK;
 
     // query operands: lane holds head h0 + 16*ht + row16, dims 32*ks + 8*grp .. +7
     const int h0 = wave * 16;
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     // the slice's slot positions, clamped to [0, ctx) and padded to whole
     // blocks (unusable slots load row 0; the masks below exclude them)
     for (int j = threadIdx.x; j < nblk * BK; j += NTHREADS) {
-        const int v = j < nsel ? idx_row[j] : -1;
+        const int v = j < nsel ? (p.dense ? j0 + j : idx_row[j]) : -1;
         sel[j] = (v >= 0 && v < ri.ctx) ? v : 0;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query operands resident before the pipeline
@@ -211,9 +217,16 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     uint32_t maskv = 0;
     for (int it = 0; it * kWave < nsel; ++it) {
         const int j = it * kWave + l;
-        const bool ok = j < nsel && (uint32_t)idx_row[j < nsel ? j : 0] < (uint32_t)ri.ctx;
+        const bool ok = j < nsel && (p.dense || (uint32_t)idx_row[j] < (uint32_t)ri.ctx);
         const uint64_t m = __ballot(ok);
         maskv = l == 2 * it ? (uint32_t)m : (l == 2 * it + 1 ? (uint32_t)(m >> 32) : maskv);
+    }
+    // blocks after the last usable slot add nothing: stop there (a row of
+    // n < k selected keys followed by -1 padding runs ceil(n / BK) blocks)
+    {
+        const uint64_t live = __ballot(maskv != 0u);
+        const int nlive = live ? 64 - (int)__builtin_clzll(live) : 0;
+        nblk = nblk < nlive ? nblk : nlive;
     }
 
     // per-lane LDS read offsets (buffer-relative)

@@ -503,6 +503,30 @@ __global__ __launch_bounds__(TPB, 2) void topk_merge_kernel(TopkParams p) {
     for (int j = tid; j < k; j += TPB) out[j] = cp[sh.ocol[j]];
 }
 
+// The selection of a row that sees no more than k keys: every visible key,
+// ascending, then -1 (the select's own result for such a row, written without
+// reading any score).  One row per workgroup, 4 slots per thread.
+__global__ __launch_bounds__(256) void select_all_visible_kernel(TopkParams p) {
+    const int t = blockIdx.x;
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    int32_t *row = p.idx + (int64_t)t * p.k;
+    for (int j = 4 * (int)threadIdx.x; j < p.k; j += 4 * 256) {
+        if (j + 4 <= p.k && (p.k & 3) == 0) {
+            const int4 v = {j < ri.nvis ? j : -1, j + 1 < ri.nvis ? j + 1 : -1,
+                            j + 2 < ri.nvis ? j + 2 : -1, j + 3 < ri.nvis ? j + 3 : -1};
+            *reinterpret_cast<int4 *>(row + j) = v;
+        } else {
+            for (int i = j; i < j + 4 && i < p.k; ++i) row[i] = i < ri.nvis ? i : -1;
+        }
+    }
+}
+
+hipError_t launch_select_all_visible(const TopkParams &p, int T, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(select_all_visible_kernel, dim3(T), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     if (p.nchunk > TOPK_MAX_CHUNKS) return hipErrorInvalidValue;

@@ -122,6 +122,34 @@ def test_sparse_mla_validation(dsa):
     assert ok
 
 
+def test_dense_mla_validation(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa, 2048, 2048)
+
+    def call(q=FAKE, kv=FAKE, H=128, D=576, Dv=512, scale=0.04, out=FAKE, lse=FAKE, ws=None, nbytes=0,
+             batch=b):
+        return lib.dsa_dense_mla_fwd(ctypes.byref(batch) if batch is not None else None, q, kv, H, D, Dv,
+                                     scale, out, lse, ws, nbytes, None)
+
+    assert call(batch=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(H=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(D=512) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(batch=_batch(dsa, 4096, 4096)) == dsa.DSA_ERR_UNSUPPORTED   # longer than the short mode
+    assert call(q=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(kv=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(lse=FAKE + 4) == dsa.DSA_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == dsa.DSA_ERR_INVALID_ARG
+    # few rows: split-KV partials need a workspace
+    few = _batch(dsa, T=4, N=4 * 2048, B=4, max_q=1, max_kv=2048)
+    need = lib.dsa_workspace_size(dsa.WS_DENSE_MLA, ctypes.byref(few), 1, 128, 512)
+    assert need > 0
+    assert call(batch=few) == dsa.DSA_ERR_WORKSPACE
+    assert call(batch=few, ws=FAKE, nbytes=need - 1) == dsa.DSA_ERR_WORKSPACE
+    assert lib.dsa_workspace_size(dsa.WS_DENSE_MLA, ctypes.byref(b), 1, 128, 512) == 0
+    assert lib.dsa_workspace_size(dsa.WS_DENSE_MLA, ctypes.byref(_batch(dsa, 4, 4096, max_kv=4096)), 1, 128,
+                                  512) == 0
+
+
 def test_fused_validation(dsa):
     lib = dsa.raw_lib()
     b = _batch(dsa)
