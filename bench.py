@@ -52,15 +52,17 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     ("prefill_32k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "e382679c64b6de86", "fetch_kib": 11479831, "write_kib": 4353271},
+        "sha256_16": "a769acb8e38afea7", "fetch_kib": 11618602, "write_kib": 4352330},
+    ("short_prefill_2k", "sparse_mla_kernel"): {
+        "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h", "api.hip"),
+        "sha256_16": "a769acb8e38afea7", "fetch_kib": 192978, "write_kib": 272097},
     ("decode_64k", "indexer_decode_kernel"): {
         "sources": ("indexer.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "b1b3ab6daf95ccb4", "fetch_kib": 289238, "write_kib": 17469},
+        "sha256_16": "93d32f97cf3c6ed9", "fetch_kib": 289241, "write_kib": 17469},
     ("quant_append_32k", "quant_groups_kernel<8192,256>"): {
         "sources": ("quant.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "bcacf21ceb2dd66d", "fetch_kib": 524451, "write_kib": 270336},
+        "sha256_16": "e70cb8e83ba30b28", "fetch_kib": 524451, "write_kib": 270336},
 }
-
 
 def measured_traffic(workload, kernel):
     """Scaled FETCH+WRITE bytes per launch, or None when no counters were taken
