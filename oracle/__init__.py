@@ -54,6 +54,7 @@ def lib():
         L.ora_topk.argtypes = [i32, p, p, p, p, i64, p, i64, i32, p]
         L.ora_sparse_attn.argtypes = [i32, p, p, p, p, i64, i32, i32, i32, dbl, p, i32, p, i32, p, i32, p, p]
         L.ora_dense_attn.argtypes = [i32, p, p, p, p, i64, i32, i32, i32, dbl, p, i32, p, i32, p, p]
+        L.ora_indexer_kl.argtypes = [i32, p, p, p, p, i64, i32, i32, dbl, p, i32, p, i32, p, i64, p, i32, p, p]
         L.ora_num_threads.restype = i32
         L.ora_e4m3_encode.argtypes = [ctypes.c_float]
         L.ora_e4m3_encode.restype = ctypes.c_uint8
@@ -219,3 +220,36 @@ def dense_attn(cu_q, cu_kv, pos0, q, kv, Dv, scale, rows=None):
     if rc != 0:
         raise ValueError("ora_dense_attn failed")
     return o, lse
+
+
+def indexer_kl(cu_q, cu_kv, pos0, q, kv, scale, scores, idx=None, rows=None, want_p=False):
+    """Indexer KL loss per row (the target: head-summed, L1-normalised main
+    attention over the key set; the loss: KL(target || softmax of the index
+    scores) over the same set).  idx None: dense warm-up over every visible
+    key; else the sparse stage over the slots idx [nrows, k].  scores
+    [nrows, ld] f32 hold I at column s.  Returns kl [nrows] f64 and, if
+    want_p, the target p ([nrows, k] per slot, or [nrows, ld] per column with
+    NaN beyond the visible keys)."""
+    cu_q, cu_kv, pos0, B = _batch(cu_q, cu_kv, pos0)
+    T, H, D = q.shape
+    r, nrows = _rows(rows, T)
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    assert scores.shape[0] == nrows
+    ld = scores.shape[1]
+    q = np.ascontiguousarray(q)
+    kv = np.ascontiguousarray(kv)
+    k = 0
+    if idx is not None:
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        assert idx.shape[0] == nrows
+        k = idx.shape[1]
+    kl = np.empty(nrows, dtype=np.float64)
+    p = None
+    if want_p:
+        p = np.full((nrows, k if idx is not None else ld), np.nan, dtype=np.float64)
+    rc = lib().ora_indexer_kl(B, _ptr(cu_q), _ptr(cu_kv), _ptr(pos0), _ptr(r), nrows, H, D, float(scale),
+                              _ptr(q), _vtype(q), _ptr(kv), _vtype(kv), _ptr(scores), ld,
+                              _ptr(idx), k, _ptr(kl), _ptr(p))
+    if rc != 0:
+        raise ValueError("ora_indexer_kl failed (index out of range or bad batch)")
+    return (kl, p) if want_p else kl

@@ -42,6 +42,11 @@
  *      y = x / s (binary32), code = the E4M3FN code nearest to y by
  *      exhaustive search over the finite codes, ties to the code with an even
  *      mantissa; |y| above 448 takes 448; the sign bit is that of y.
+ *   7. Indexer KL loss, [R] "Как учили индексатор": the target is the main
+ *      attention's probabilities (step 4's exact per-head softmax over the key
+ *      set) summed over the heads and L1-normalised; the loss is
+ *      KL(target || softmax of I) over the same set: every visible key
+ *      (dense warm-up) or the selected slots (sparse stage).
  *
  * Batch description shared by every function: B sequences; query rows of
  * sequence b are [cu_q[b], cu_q[b+1]); its cache rows are
@@ -516,6 +521,136 @@ int ora_dense_attn(int B, const int32_t *cu_q, const int64_t *cu_kv,
             err = 1;
         }
         ora_attn_ws_free(&w);
+    }
+    return err ? ORA_ERR : ORA_OK;
+}
+
+/*
+ * Indexer KL loss, [R] "Как учили индексатор": the indexer is trained toward
+ * the main attention.  Its target p[t,:] is the attention's probabilities
+ * summed over all heads and L1-normalised over the key set; the loss of row
+ * t is KL(p[t,:] || softmax(I[t,:])) over the same set.  Two stages:
+ *   dense warm-up (idx == NULL): the set is every visible key 0..nvis-1;
+ *   sparse stage: the selected slots idx[i, 0..k-1] (negative entries are
+ *   skipped; a position listed twice is two slots, as in the attention).
+ * Steps for one row, in the order the section gives them:
+ *   1. z[j,h] = scale * <q[t,h,:], kv[s_j,:]>, and per head the softmax over
+ *      the set: P[j,h] = exp(z[j,h] - M_h) / Z_h (the main attention);
+ *   2. a[j] = sum_h P[j,h];  p[j] = a[j] / sum_j a[j]   (L1 normalisation);
+ *   3. r = softmax over the set of I[t, s_j];
+ *   4. kl = sum_j p[j] * (ln p[j] - ln r[j]), with 0 * ln 0 = 0.
+ *   q [T,H,D], kv [N,D]: types as in ora_sparse_attn
+ *   scores [nrows, ld] f32: I[t, s] of the rows asked for, at column s
+ *   kl  [nrows] f64 out (0 for an empty set)
+ *   p   [nrows, k] (sparse: per slot, 0 for skipped slots) or [nrows, ld]
+ *       (dense: columns 0..nvis-1) f64 out, nullable
+ */
+int ora_indexer_kl(int B, const int32_t *cu_q, const int64_t *cu_kv,
+                   const int32_t *pos0, const int32_t *rows, int64_t nrows,
+                   int H, int D, double scale,
+                   const void *q, int q_type, const void *kv, int kv_type,
+                   const float *scores, int64_t ld, const int32_t *idx, int k,
+                   double *kl, double *p)
+{
+    int err = 0;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; i++) {
+        ora_row r;
+        int64_t t = ora_pick_row(rows, i);
+        if (ora_row_info(B, cu_q, cu_kv, pos0, t, &r)) {
+            #pragma omp atomic write
+            err = 1;
+            continue;
+        }
+        const int64_t m = idx ? k : r.nvis;          /* slots of the row */
+        const int64_t pw = idx ? k : ld;              /* width of a p row */
+        int64_t *pos = (int64_t *)malloc(sizeof(int64_t) * (size_t)(m > 0 ? m : 1));
+        double *z = (double *)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1) * H);
+        double *a = (double *)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
+        double *qd = (double *)malloc(sizeof(double) * (size_t)H * D);
+        double *kd = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!pos || !z || !a || !qd || !kd) {
+            #pragma omp atomic write
+            err = 1;
+        } else {
+            int bad = 0;
+            for (int64_t j = 0; j < m; j++) {
+                pos[j] = idx ? (int64_t)idx[i * k + j] : j;
+                if (pos[j] >= r.ctx || pos[j] >= ld)
+                    bad = 1;
+            }
+            if (bad) {
+                #pragma omp atomic write
+                err = 1;
+            } else {
+                for (int h = 0; h < H; h++)
+                    for (int d = 0; d < D; d++)
+                        qd[h * D + d] = ora_load(q, q_type, (t * H + h) * (int64_t)D + d);
+                /* step 1: logits and the per-head softmax */
+                for (int64_t j = 0; j < m; j++) {
+                    if (pos[j] < 0)
+                        continue;
+                    for (int d = 0; d < D; d++)
+                        kd[d] = ora_load(kv, kv_type, (r.kv0 + pos[j]) * D + d);
+                    for (int h = 0; h < H; h++) {
+                        double dot = 0.0;
+                        for (int d = 0; d < D; d++)
+                            dot += qd[h * D + d] * kd[d];
+                        z[j * H + h] = scale * dot;
+                    }
+                }
+                for (int64_t j = 0; j < m; j++)
+                    a[j] = 0.0;
+                for (int h = 0; h < H; h++) {
+                    double M = -INFINITY, Z = 0.0;
+                    for (int64_t j = 0; j < m; j++)
+                        if (pos[j] >= 0 && z[j * H + h] > M)
+                            M = z[j * H + h];
+                    for (int64_t j = 0; j < m; j++)
+                        if (pos[j] >= 0)
+                            Z += exp(z[j * H + h] - M);
+                    /* step 2 (first half): the sum over heads */
+                    for (int64_t j = 0; j < m; j++)
+                        if (pos[j] >= 0)
+                            a[j] += exp(z[j * H + h] - M) / Z;
+                }
+                /* step 2 (second half): L1 normalisation over the set */
+                double asum = 0.0;
+                for (int64_t j = 0; j < m; j++)
+                    if (pos[j] >= 0)
+                        asum += a[j];
+                /* step 3: the indexer's softmax over the same set */
+                double MI = -INFINITY, ZI = 0.0;
+                for (int64_t j = 0; j < m; j++)
+                    if (pos[j] >= 0 && (double)scores[i * ld + pos[j]] > MI)
+                        MI = (double)scores[i * ld + pos[j]];
+                for (int64_t j = 0; j < m; j++)
+                    if (pos[j] >= 0)
+                        ZI += exp((double)scores[i * ld + pos[j]] - MI);
+                const double lnZI = MI + log(ZI);
+                /* step 4: the divergence */
+                double sum = 0.0;
+                for (int64_t j = 0; j < m; j++) {
+                    if (pos[j] < 0) {
+                        if (p && idx)
+                            p[i * pw + j] = 0.0;
+                        continue;
+                    }
+                    const double pj = a[j] / asum;
+                    const double lnr = (double)scores[i * ld + pos[j]] - lnZI;
+                    if (pj > 0.0)
+                        sum += pj * (log(pj) - lnr);
+                    if (p)
+                        p[i * pw + (idx ? j : pos[j])] = pj;
+                }
+                kl[i] = asum > 0.0 ? sum : 0.0;
+            }
+        }
+        free(pos);
+        free(z);
+        free(a);
+        free(qd);
+        free(kd);
     }
     return err ? ORA_ERR : ORA_OK;
 }
