@@ -52,16 +52,16 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     ("prefill_32k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "a769acb8e38afea7", "fetch_kib": 11618602, "write_kib": 4352330},
+        "sha256_16": "1c84730cb82ad104", "fetch_kib": 11618602, "write_kib": 4352330},
     ("short_prefill_2k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "a769acb8e38afea7", "fetch_kib": 192978, "write_kib": 272097},
+        "sha256_16": "1c84730cb82ad104", "fetch_kib": 192978, "write_kib": 272097},
     ("decode_64k", "indexer_decode_kernel"): {
         "sources": ("indexer.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "93d32f97cf3c6ed9", "fetch_kib": 289241, "write_kib": 17469},
+        "sha256_16": "203ed68eb27b3dc4", "fetch_kib": 289241, "write_kib": 17469},
     ("quant_append_32k", "quant_groups_kernel<8192,256>"): {
         "sources": ("quant.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "e70cb8e83ba30b28", "fetch_kib": 524451, "write_kib": 270336},
+        "sha256_16": "de88c3e3a58f257f", "fetch_kib": 524451, "write_kib": 270336},
 }
 
 def measured_traffic(workload, kernel):
@@ -174,6 +174,107 @@ def cpu_baseline(wl, target_s=15.0):
 
 # ---------------------------------------------------------- quantise + append
 
+KL_METRIC = "indexer KL loss tokens/s (sparse stage over the top-2048 selection), 32K prefill"
+
+
+def kl_bench(args, dsa):
+    """One step = the indexer KL loss of every row of a 32K prefill in the
+    sparse training stage: the target (the attention's probabilities over the
+    2048 selected rows, summed over the 128 heads, L1-normalised) against the
+    softmax of the index scores.  Its inputs (index scores, selection,
+    attention lse) come from the library's own forward, run once before the
+    timed region; q and the latent cache are the prefill_32k inputs."""
+    import torch
+    say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+    wl, _ = make_workload("prefill_32k")
+    b = wl.batch
+    t0 = time.time()
+    dev = wl.device("cuda")
+    batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0)
+    ld = ((b.max_kv + 63) // 64) * 64
+    scores = torch.empty((b.T, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty((b.T, wl.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((b.T, H, DV), dtype=torch.int16, device="cuda")
+    lse = torch.empty((b.T, H), dtype=torch.float32, device="cuda")
+    dsa.indexer_scores(batch, dev["qi"], dev["qs"], dev["w"], dev["ki"], dev["ks"], scores)
+    dsa.topk(batch, scores, wl.k, idx)
+    dsa.sparse_mla_fwd(batch, dev["q"], dev["kv"], idx, wl.scale, out, lse)
+    del out
+    kl = torch.empty(b.T, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, dsa.workspace_size(dsa.WS_INDEXER_KL, batch, wl.k)), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    say(f"[bench] workload indexer_kl_32k: T={b.T} k={wl.k}; inputs and forward ready ({time.time() - t0:.1f} s)")
+
+    def step():
+        dsa.indexer_kl_fwd(batch, dev["q"], dev["kv"], lse, wl.scale, scores, kl, idx=idx, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = b.T * args.steps / elapsed
+    say(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, {tokens_per_s:,.0f} tokens/s")
+
+    nvis = visible_counts(b.cu_q, b.cu_kv, b.pos0)
+    flops = float(np.sum(np.minimum(nvis, wl.k))) * H * 2.0 * D      # the logits of the selected pairs
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    achieved = flops / (kms * 1e-3) / 1e12
+    roof = {"kernel": "indexer_kl_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None, "avg_ms": round(kms, 4), "algorithmic_flops": flops}
+    tr = measured_traffic("indexer_kl_32k", "indexer_kl_kernel")
+    if tr is not None:
+        roof["traffic"] = round(tr["fetch"] + tr["write"])
+        roof["traffic_unit"] = "bytes/launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
+        roof["traffic_fetch"], roof["traffic_write"] = round(tr["fetch"]), round(tr["write"])
+    say(f"[bench] indexer_kl_kernel: {kms:.3f} ms/launch, {achieved:.1f} TFLOP/s ({100 * roof['frac']:.1f}% of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        say("[bench] timing the CPU oracle on a sample of the workload ...")
+        threads = oracle.num_threads()
+        host_idx = idx.cpu().numpy()
+
+        def run(n):
+            rows = np.unique(np.linspace(0, b.T - 1, n).astype(np.int64))
+            inp = wl.sampled_host(rows)
+            s_rows = scores[torch.from_numpy(rows).cuda()].cpu().numpy()
+            t2 = time.perf_counter()
+            oracle.indexer_kl(b.cu_q, b.cu_kv, b.pos0, inp.q, inp.kv, wl.scale, s_rows, idx=host_idx[rows],
+                              rows=rows)
+            return len(rows), time.perf_counter() - t2
+        n0, dt = run(16)
+        n = int(min(b.T, max(16, args.cpu_seconds / max(dt / n0, 1e-9))))
+        n, dt = run(n)
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n} query rows evenly spaced over the {b.T} of the workload (exact per-head softmax, "
+                         f"head sum, KL over the 2048 selected keys), {dt:.1f} s wall"}
+        say(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s on {threads} threads")
+
+    cfg = {"workload": "indexer_kl_32k", "batch": b.B, "query_tokens": b.T, "cache_rows": b.N, "topk": wl.k,
+           "heads": H, "d_qk": D, "entry": "dsa_indexer_kl_fwd (sparse stage)"}
+    line = {"metric": KL_METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 QUANT_METRIC = "FP8 quantise + cache append tokens/s (indexer queries and keys, latent rows), 32K prefill"
 
 
@@ -279,7 +380,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_32k",
                     choices=["prefill_32k", "prefill_4k", "decode_64k", "chunked_128k", "quant_append_32k",
-                             "short_prefill_2k"])
+                             "short_prefill_2k", "indexer_kl_32k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=5,
@@ -309,6 +410,8 @@ def main(argv=None):
 
     if args.workload == "quant_append_32k":
         return quant_append_bench(args, dsa)
+    if args.workload == "indexer_kl_32k":
+        return kl_bench(args, dsa)
     wl, entry = make_workload(args.workload)
     b = wl.batch
     say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731

@@ -109,7 +109,8 @@ dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld, int
  *   q   [T, H, D] bf16      kv [N, D] bf16 (latent rows; value = first Dv)
  *   idx [T, k] int32        out [T, H, Dv] bf16        lse [T, H] fp32
  * Workspace (dsa_workspace_size(DSA_WS_SPARSE_MLA, ...)) holds split-KV
- * partial results when the batch has few query rows; it may be 0 bytes. */
+ * partial results when the batch has few query rows; it may be 0 bytes.
+ * Supported contexts: max_kv <= 2^21. */
 dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv,
                               const int32_t *idx, int k, int H, int D, int Dv, float scale,
                               uint16_t *out, float *lse, void *ws, size_t ws_bytes,
@@ -135,6 +136,29 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const uint16_t *q, const u
 dsa_status dsa_dense_mla_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, int H, int D,
                              int Dv, float scale, uint16_t *out, float *lse, void *ws, size_t ws_bytes,
                              void *stream);
+
+/* Indexer KL loss, [R] "Как учили индексатор": the indexer learns where the
+ * main attention looks.  For query row t over its key set (idx == NULL: every
+ * visible key, the dense warm-up; else the valid slots of idx[t,:], the sparse
+ * stage; a position listed twice is two slots):
+ *   q_s   = sum_h exp(scale * <q[t,h,:], kv[s,:]> - lse[t,h])
+ *           (the attention's probabilities summed over the heads),
+ *   p_s   = q_s / sum_s q_s                        (L1 normalisation),
+ *   kl[t] = sum_s p_s * (ln p_s - ln softmax_s(scores[t, s]))   (natural log).
+ * lse must be the attention's log-sum-exp over the same set (what
+ * dsa_sparse_mla_fwd / dsa_dense_mla_fwd return for it); a head with a
+ * non-finite lse contributes nothing.  A row with no usable slot gives 0.
+ *   q [T, H, D] bf16, kv [N, D] bf16, lse [T, H] fp32, scores [T, ld] fp32
+ *   (the index scores, e.g. from dsa_indexer_scores), idx [T, k] int32 or NULL
+ *   kl [T] fp32 out; p_out (nullable) fp32 out: the target p, [T, k] per slot
+ *   (0 for unusable slots) in the sparse stage, [T, ld] per column (columns
+ *   0..nvis-1 written) in the dense one.
+ * Supported: H = 128, D = 576, 1 <= k <= 2048, max_kv <= 2^21, ld >= max_kv.
+ * Workspace (required): dsa_workspace_size(DSA_WS_INDEXER_KL, batch, k, ...)
+ * with the same k (any 1..2048 for the dense stage). */
+dsa_status dsa_indexer_kl_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, const float *lse,
+                              int H, int D, float scale, const float *scores, int64_t ld, const int32_t *idx,
+                              int k, float *kl, float *p_out, void *ws, size_t ws_bytes, void *stream);
 
 /* All inputs of one DSA forward (indexer + top-k + sparse MQA attention). */
 typedef struct {
@@ -203,7 +227,8 @@ typedef enum {
     DSA_WS_SPARSE_MLA = 1,
     DSA_WS_PREFILL = 2,
     DSA_WS_DECODE = 3,
-    DSA_WS_DENSE_MLA = 4       /* k is ignored (pass any 1..2048) */
+    DSA_WS_DENSE_MLA = 4,      /* k is ignored (pass any 1..2048) */
+    DSA_WS_INDEXER_KL = 5
 } dsa_ws_entry;
 
 /* Workspace bytes the given entry point needs for this batch (host only; reads

@@ -7,7 +7,7 @@ memory and streams only.  Importing this package fails loudly when the built
 library is missing: there is no fallback implementation.
 
 Entry points (same names as the C ABI, without the ``dsa_`` prefix):
-    indexer_scores, topk, sparse_mla_fwd, dense_mla_fwd, prefill_fwd, decode_fwd,
+    indexer_scores, topk, sparse_mla_fwd, dense_mla_fwd, indexer_kl_fwd, prefill_fwd, decode_fwd,
     quantize_queries, append_cache,
     workspace_size, status_string, version
 """
@@ -29,9 +29,10 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
-WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE, WS_DENSE_MLA = range(5)
+WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE, WS_DENSE_MLA, WS_INDEXER_KL = range(6)
 
-EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_dense_mla_fwd", "dsa_prefill_fwd",
+EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_dense_mla_fwd", "dsa_indexer_kl_fwd",
+           "dsa_prefill_fwd",
            "dsa_decode_fwd", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
            "dsa_status_string", "dsa_version")
 
@@ -64,6 +65,7 @@ _lib.dsa_indexer_scores.argtypes = [_BP, _P, _P, _P, _P, _P, _I, _I, _P, _I64, _
 _lib.dsa_topk.argtypes = [_BP, _P, _I64, _I, _P, _P, _SZ, _P]
 _lib.dsa_sparse_mla_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
 _lib.dsa_dense_mla_fwd.argtypes = [_BP, _P, _P, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
+_lib.dsa_indexer_kl_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _F, _P, _I64, _P, _I, _P, _P, _P, _SZ, _P]
 _lib.dsa_prefill_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_decode_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_workspace_size.argtypes = [_I, _BP, _I, _I, _I]
@@ -202,6 +204,20 @@ def dense_mla_fwd(batch: Batch, q, kv, scale: float, out, lse, Dv: int = 512, ws
                                 float(scale), _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream(stream))
     _check(st, "dsa_dense_mla_fwd")
     return out, lse
+
+
+def indexer_kl_fwd(batch: Batch, q, kv, lse, scale: float, scores, kl, idx=None, p_out=None, ld=None, ws=None,
+                   stream=None):
+    """Indexer KL loss per row into kl [T] (see dsa_indexer_kl_fwd); idx None
+    is the dense warm-up over every visible key."""
+    ld = scores.shape[1] if ld is None else ld
+    k = idx.shape[1] if idx is not None else 1
+    ws, nbytes = _workspace(WS_INDEXER_KL, batch, k, ws, q.device)
+    st = _lib.dsa_indexer_kl_fwd(ctypes.byref(batch.c), _ptr(q), _ptr(kv), _ptr(lse), q.shape[1], q.shape[2],
+                                 float(scale), _ptr(scores), int(ld), _ptr(idx), int(k), _ptr(kl), _ptr(p_out),
+                                 _ptr(ws), nbytes, _stream(stream))
+    _check(st, "dsa_indexer_kl_fwd")
+    return kl
 
 
 def fwd_args(batch: Batch, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, k: int, scale: float,

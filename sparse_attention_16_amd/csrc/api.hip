@@ -66,6 +66,24 @@ size_t mla_ws(const dsa_batch *b, int k) {
     return up((size_t)b->total_q * s * kH * kDv * 2) + up((size_t)b->total_q * s * kH * 4);
 }
 
+// Splits of the KL loss: enough workgroups for two per compute unit (the
+// kernel's LDS allows two), each split a whole number of 32-slot blocks.
+int kl_splits(int T, int64_t slots) {
+    const int64_t nblk = (slots + KL_BK - 1) / KL_BK;
+    const int want = 2 * device_cus();
+    if (T <= 0 || T >= want || nblk <= 1) return 1;
+    int64_t s = (want + T - 1) / T;
+    if (s > nblk) s = nblk;
+    return s < 1 ? 1 : (int)s;
+}
+
+// Partial sums of the KL loss (both stages: the larger split count).
+size_t kl_ws(const dsa_batch *b, int k) {
+    const int s1 = kl_splits(b->total_q, k), s2 = kl_splits(b->total_q, b->max_kv);
+    const int s = s1 > s2 ? s1 : s2;
+    return up((size_t)b->total_q * s * 5 * 4);
+}
+
 int64_t score_ld(int max_kv) { return ((int64_t)max_kv + 63) / 64 * 64; }
 
 // Slot budget of the dense attention: the longest context (at least 1).
@@ -287,6 +305,7 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const uint16_t *q, const u
     if (st != DSA_OK) return st;
     if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
     if ((st = check_k(k)) != DSA_OK) return st;
+    if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return DSA_ERR_INVALID_ARG;
     if (batch->total_q == 0) return DSA_OK;
     if (!q || !idx || !out || !lse) return DSA_ERR_INVALID_ARG;
@@ -318,6 +337,50 @@ dsa_status dsa_dense_mla_fwd(const dsa_batch *batch, const uint16_t *q, const ui
     return hip_status(launch_sparse_mla(p, batch->total_q, static_cast<hipStream_t>(stream)));
 }
 
+dsa_status dsa_indexer_kl_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, const float *lse,
+                              int H, int D, float scale, const float *scores, int64_t ld, const int32_t *idx,
+                              int k, float *kl, float *p_out, void *ws, size_t ws_bytes, void *stream) {
+    dsa_status st = check_batch(batch);
+    if (st != DSA_OK) return st;
+    if (H != kH || D != kD) return DSA_ERR_UNSUPPORTED;
+    if (idx && (st = check_k(k)) != DSA_OK) return st;
+    if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return DSA_ERR_INVALID_ARG;
+    if (batch->total_q == 0) return DSA_OK;
+    if (!q || !lse || !scores || !kl) return DSA_ERR_INVALID_ARG;
+    if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
+    if (ld < batch->max_kv || ld < 1) return DSA_ERR_INVALID_ARG;
+    if (!al16(q) || !al16(lse) || !al16(scores) || !al16(kl) || (kv && !al16(kv)) || (idx && !al16(idx)) ||
+        (p_out && !al16(p_out)))
+        return DSA_ERR_INVALID_ARG;
+    const size_t need = kl_ws(batch, idx ? k : 1);
+    if (!ws || ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
+    KlParams p;
+    p.cu_q = batch->cu_q;
+    p.cu_kv = batch->cu_kv;
+    p.pos0 = batch->pos0;
+    p.B = batch->batch;
+    p.total_kv = batch->total_kv;
+    p.max_kv = batch->max_kv;
+    p.q = q;
+    p.kv = kv;
+    p.lse = lse;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.scores = scores;
+    p.ld = ld;
+    p.idx = idx;
+    p.k = idx ? k : 0;
+    p.kl = kl;
+    p.p_out = p_out;
+    const int64_t slots = idx ? k : batch->max_kv;
+    p.splits = kl_splits(batch->total_q, slots);
+    const int64_t nblk = (slots + KL_BK - 1) / KL_BK;
+    p.blocks_per_split = (int)((nblk + p.splits - 1) / p.splits);
+    if (p.blocks_per_split < 1) p.blocks_per_split = 1;
+    p.part = static_cast<float *>(ws);
+    return hip_status(launch_indexer_kl(p, batch->total_q, static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_prefill_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse, int32_t *idx_out,
                            void *ws, size_t ws_bytes, void *stream) {
     return run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, false);
@@ -338,6 +401,7 @@ size_t dsa_workspace_size(dsa_ws_entry entry, const dsa_batch *batch, int k, int
         case DSA_WS_PREFILL:
         case DSA_WS_DECODE: return fwd_ws(batch, k);
         case DSA_WS_DENSE_MLA: return batch->max_kv > kKMax ? 0 : mla_ws(batch, dense_slots(batch));
+        case DSA_WS_INDEXER_KL: return batch->max_kv > MAX_KV_ATTN ? 0 : kl_ws(batch, k);
     }
     return 0;
 }

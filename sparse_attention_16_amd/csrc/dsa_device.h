@@ -66,6 +66,19 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// One 16-byte-per-lane direct-to-LDS load from sbase + voff (a scalar base
+// and a 32-bit per-lane offset) to LDS lds + 16 * lane.  Issued from asm, so
+// the compiler's wait insertion does not track it (it cannot tell which LDS
+// buffer the load writes and would fence later LDS reads of unrelated buffers
+// with a wait for it); a kernel using it waits for these loads explicitly
+// with vmcnt before the barrier that publishes the buffer.  M0 must be
+// written one instruction ahead of the load.
+__device__ __forceinline__ void dma16s(uint64_t sbase, uint32_t voff, const DSA_LDS void *lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "m0");
+}
+
 // float -> bf16 bits, round to nearest even (inputs are finite here).
 __device__ __forceinline__ uint16_t f2bf(float f) {
     uint32_t u = __float_as_uint(f);

@@ -62,15 +62,40 @@ struct MlaParams {
     float *lse_part;        // [T, splits, 128]
 };
 
+struct KlParams {
+    const int32_t *cu_q;
+    const int64_t *cu_kv;
+    const int32_t *pos0;
+    int B;
+    int64_t total_kv;
+    int max_kv;
+    const uint16_t *q;      // [T, 128, 576] bf16
+    const uint16_t *kv;     // [N, 576] bf16
+    const float *lse;       // [T, 128] attention log-sum-exp (natural log)
+    float scale_log2;       // softmax scale * log2(e)
+    const float *scores;    // [T, ld] index scores
+    int64_t ld;
+    const int32_t *idx;     // [T, k] selected slots, or null: every visible key
+    int k;
+    float *kl;              // [T]
+    float *p_out;           // nullable: [T, k] per slot, or [T, ld] per column
+    int splits;             // workgroups per row
+    int blocks_per_split;   // KL_BK-slot blocks per split
+    float *part;            // [T, splits, 5] partial sums (workspace)
+};
+
 constexpr int TOPK_CHUNK = 32768;     // columns selected per workgroup in LDS
 constexpr int TOPK_MAX_CHUNKS = 8;    // merge capacity: 8 x 2048 candidates
 constexpr int MLA_BK = 32;            // keys per gathered block
+constexpr int KL_BK = 32;             // slots per block of the KL loss
+constexpr int MAX_KV_ATTN = 1 << 21;  // per-sequence rows the gathers address with 32-bit offsets
 
 hipError_t launch_indexer(const IndexerParams &p, int T, int max_q, bool decode_variant,
                           hipStream_t s);
 hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s);
 hipError_t launch_select_all_visible(const TopkParams &p, int T, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s);
+hipError_t launch_indexer_kl(const KlParams &p, int T, hipStream_t s);
 hipError_t launch_quant_queries(const float *q, int64_t T, uint8_t *q_fp8, float *q_scale, hipStream_t s);
 hipError_t launch_append_cache(const float *k_new, const uint16_t *kv_new, int64_t R, const int64_t *dst,
                                uint8_t *k_fp8, float *k_scale, uint16_t *kv, int64_t N, hipStream_t s);

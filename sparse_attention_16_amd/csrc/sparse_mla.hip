@@ -79,19 +79,6 @@ typedef DSA_LDS uint8_t lds_u8;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
-// One 16-byte-per-lane direct-to-LDS load from sbase + voff (a scalar base
-// and a 32-bit per-lane offset) to LDS lds + 16 * lane.  Issued from asm, so
-// the compiler's wait insertion does not track it (it cannot tell which LDS
-// buffer the load writes and would fence later LDS reads of unrelated buffers
-// with a wait for it); the kernel waits for these loads explicitly with vmcnt
-// before each barrier (no other vector-memory load is issued inside the block
-// loop).  M0 must be written one instruction ahead of the load.
-__device__ __forceinline__ void dma16s(uint64_t sbase, uint32_t voff, const DSA_LDS void *lds) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-                 : "m0");
-}
-
 // Maximum over the four 16-lane groups (lanes l, l^16, l^32, l^48) with two
 // VALU lane swaps: no LDS traffic and no exec-mask change.
 __device__ __forceinline__ float group4_max(float x) {

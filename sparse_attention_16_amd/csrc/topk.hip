@@ -361,17 +361,6 @@ __device__ __forceinline__ ChunkItem chunk_item(const TopkParams &p, int item) {
     return it;
 }
 
-// One 16-byte-per-lane direct-to-LDS load from sbase + voff (a scalar base
-// and a 32-bit per-lane offset) to LDS lds + 16 * lane.  Issued from asm, so
-// the compiler's wait insertion does not track it; the kernel waits with an
-// explicit vmcnt(0) before it reads the staged chunk.  M0 must be written one
-// instruction ahead of the load.
-__device__ __forceinline__ void dma16s(uint64_t sbase, uint32_t voff, const DSA_LDS void *lds) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-                 : "m0");
-}
-
 // Issues the loads of a chunk into the LDS stage (stage[c] = score of chunk
 // column c, c < len; group u of wave w: columns 4 * (u * TPB + 64 * w) + 0..255).
 // 16-byte direct-to-LDS loads when rows allow them, else plain loads and LDS

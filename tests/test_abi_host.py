@@ -150,6 +150,38 @@ def test_dense_mla_validation(dsa):
                                   512) == 0
 
 
+def test_indexer_kl_validation(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa, 4096, 4096)
+    need = lib.dsa_workspace_size(dsa.WS_INDEXER_KL, ctypes.byref(b), 2048, 128, 512)
+    assert need >= 4096 * 5 * 4
+
+    def call(q=FAKE, kv=FAKE, lse=FAKE, H=128, D=576, scale=0.04, scores=FAKE, ld=4096, idx=FAKE, k=2048,
+             kl=FAKE, p_out=None, ws=FAKE, nbytes=need, batch=b):
+        return lib.dsa_indexer_kl_fwd(ctypes.byref(batch) if batch is not None else None, q, kv, lse, H, D, scale,
+                                      scores, ld, idx, k, kl, p_out, ws, nbytes, None)
+
+    assert call(batch=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(H=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(D=512) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(k=0) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED
+    huge = _batch(dsa, 4, 3 << 21, B=1, max_kv=3 << 21)
+    assert call(batch=huge, ld=3 << 21) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(q=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(lse=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(scores=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(kl=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ld=4095) == dsa.DSA_ERR_INVALID_ARG
+    assert call(p_out=FAKE + 4) == dsa.DSA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ws=None, nbytes=0) == dsa.DSA_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == dsa.DSA_ERR_WORKSPACE
+    # the sparse attention shares the 2^21-row context limit of the gathers
+    assert lib.dsa_sparse_mla_fwd(ctypes.byref(huge), FAKE, FAKE, FAKE, 2048, 128, 576, 512, 0.04, FAKE, FAKE,
+                                  None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+
+
 def test_fused_validation(dsa):
     lib = dsa.raw_lib()
     b = _batch(dsa)
