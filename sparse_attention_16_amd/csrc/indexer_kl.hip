@@ -40,6 +40,8 @@ constexpr int BUF = RB + BK * 128;        // 37888 bytes per block buffer
 constexpr int NPART = 5;                  // Q, A, B, max I, sum exp(I - max)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994530942f;
+constexpr float FLT_MIN_NORMAL = 1.17549435e-38f;
+constexpr int AHEAD = 3;                  // k-steps of K operands read ahead
 
 typedef DSA_LDS uint8_t lds_u8;
 
@@ -181,15 +183,30 @@ __global__ __launch_bounds__(NT, 2) void indexer_kl_kernel(KlParams p) {
         for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) s[ht][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // K operands are read AHEAD k-steps before their MFMAs (a ring of
+        // registers), so the LDS latency hides behind the MFMAs in between
+        auto koff = [&](int ks, int mt) {
+            return ks < 16 ? kA + mt * 16 * PA + 64 * ks : (ks == 16 ? kR16 : kR17) + mt * 2048;
+        };
+        bf16x8 kr[AHEAD + 1][2];
+#pragma unroll
+        for (int ks = 0; ks < AHEAD; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) kr[ks][mt] = *reinterpret_cast<const DSA_LDS bf16x8 *>(buf + koff(ks, mt));
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
+            if (ks + AHEAD < KS) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int off = ks < 16 ? kA + mt * 16 * PA + 64 * ks : (ks == 16 ? kR16 : kR17) + mt * 2048;
-                const bf16x8 a = *reinterpret_cast<const DSA_LDS bf16x8 *>(buf + off);
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht) s[ht][mt] = mfma_bf16_16x16x32(a, qb[ht][ks], s[ht][mt]);
+                for (int mt = 0; mt < 2; ++mt)
+                    kr[(ks + AHEAD) % (AHEAD + 1)][mt] =
+                        *reinterpret_cast<const DSA_LDS bf16x8 *>(buf + koff(ks + AHEAD, mt));
             }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht)
+                    s[ht][mt] = mfma_bf16_16x16x32(kr[ks % (AHEAD + 1)][mt], qb[ht][ks], s[ht][mt]);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // probabilities summed over the wave's 32 heads, one value per slot
@@ -198,8 +215,8 @@ __global__ __launch_bounds__(NT, 2) void indexer_kl_kernel(KlParams p) {
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                e[mt][r] = row_sum16(exp2f(s[0][mt][r] * p.scale_log2 - lse2[0]) +
-                                     exp2f(s[1][mt][r] * p.scale_log2 - lse2[1]));
+                e[mt][r] = row_sum16(__builtin_amdgcn_exp2f(fmaf(s[0][mt][r], p.scale_log2, -lse2[0])) +
+                                     __builtin_amdgcn_exp2f(fmaf(s[1][mt][r], p.scale_log2, -lse2[1])));
         if (row16 < 8) {
             const int mt = row16 >> 2, r = row16 & 3;
             float v = e[0][0];
@@ -215,13 +232,14 @@ __global__ __launch_bounds__(NT, 2) void indexer_kl_kernel(KlParams p) {
             const float qv = red[cur][0][l] + red[cur][1][l] + red[cur][2][l] + red[cur][3][l];
             const float iv = icur;
             aQ += qv;
-            if (qv > 0.f) aA += qv * (log2f(qv) * LN2);
+            // (the raw exp2 flushes results below 2^-126 to 0: qv is 0 or normal)
+            if (qv >= FLT_MIN_NORMAL) aA += qv * (__builtin_amdgcn_logf(qv) * LN2);
             aB += qv * iv;
             if (iv > mI) {
-                sI = sI * exp2f((mI - iv) * LOG2E) + 1.f;
+                sI = sI * __builtin_amdgcn_exp2f((mI - iv) * LOG2E) + 1.f;
                 mI = iv;
             } else if (iv > -INFINITY) {
-                sI += exp2f((iv - mI) * LOG2E);
+                sI += __builtin_amdgcn_exp2f((iv - mI) * LOG2E);
             }
             if (p.p_out) {
                 const int64_t col = dense ? (int64_t)pcur : (int64_t)(j0 + b * BK + l);
