@@ -59,6 +59,9 @@ COUNTERS = {
     ("decode_64k", "indexer_decode_kernel"): {
         "sources": ("indexer.hip", "dsa_device.h", "kernels.h", "api.hip"),
         "sha256_16": "203ed68eb27b3dc4", "fetch_kib": 289241, "write_kib": 17469},
+    ("indexer_kl_32k", "indexer_kl_kernel"): {
+        "sources": ("indexer_kl.hip", "dsa_device.h", "kernels.h", "api.hip"),
+        "sha256_16": "056372b83dc6dfa0", "fetch_kib": 18370464, "write_kib": 1340},
     ("quant_append_32k", "quant_groups_kernel<8192,256>"): {
         "sources": ("quant.hip", "dsa_device.h", "kernels.h", "api.hip"),
         "sha256_16": "de88c3e3a58f257f", "fetch_kib": 524451, "write_kib": 270336},
