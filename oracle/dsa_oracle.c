@@ -47,6 +47,10 @@
  *      set) summed over the heads and L1-normalised; the loss is
  *      KL(target || softmax of I) over the same set: every visible key
  *      (dense warm-up) or the selected slots (sparse stage).
+ *   8. Backward of step 4 over the same selection: the exact softmax's
+ *      backward (dZ = P (dP - delta)), then the two products that use z
+ *      (query and key sides) and the one that uses the value (the first Dv
+ *      dims of the same latent row), summed over heads per selected row.
  *
  * Batch description shared by every function: B sequences; query rows of
  * sequence b are [cu_q[b], cu_q[b+1]); its cache rows are
@@ -651,6 +655,159 @@ int ora_indexer_kl(int B, const int32_t *cu_q, const int64_t *cu_kv,
         free(a);
         free(qd);
         free(kd);
+    }
+    return err ? ORA_ERR : ORA_OK;
+}
+
+/*
+ * Backward of the sparse MQA attention (step 4) over the same selection,
+ * [R] "Как учили индексатор" (in the sparse stage all parameters learn, so
+ * gradients flow through the attention over the selected rows).  Given
+ * dout = dL/do [T, H, Dv] (type dout_type), for the rows asked for, in double:
+ *   z[j,h]  = scale * <q[t,h,:], kv[s_j,:]>,  P = exact softmax over the slots,
+ *   o[h,c]  = sum_j P[j,h] kv[s_j,c]                  (c < Dv),
+ *   dP[j,h] = <dout[t,h,:], kv[s_j,:Dv]>,
+ *   delta_h = sum_c dout[t,h,c] o[h,c]   (= sum_j P[j,h] dP[j,h]),
+ *   dZ[j,h] = P[j,h] (dP[j,h] - delta_h)           (the softmax's backward),
+ *   dq[i,h,d]   = scale * sum_j dZ[j,h] kv[s_j,d]             (d < D),
+ *   dkv[s_j,d] += scale * sum_h dZ[j,h] q[t,h,d]             (d < D: the key),
+ *   dkv[s_j,c] += sum_h P[j,h] dout[t,h,c]                   (c < Dv: the value).
+ * Negative idx entries are skipped; a position listed twice is two slots.
+ *   dq [nrows, H, D] f64 out; dkv [N, D] f64, accumulated (the caller zeroes).
+ */
+int ora_sparse_attn_bwd(int B, const int32_t *cu_q, const int64_t *cu_kv,
+                        const int32_t *pos0, const int32_t *rows, int64_t nrows,
+                        int H, int D, int Dv, double scale,
+                        const void *q, int q_type, const void *kv, int kv_type,
+                        const void *dout, int dout_type, const int32_t *idx, int k,
+                        double *dq, double *dkv)
+{
+    int err = 0;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; i++) {
+        ora_row r;
+        int64_t t = ora_pick_row(rows, i);
+        if (ora_row_info(B, cu_q, cu_kv, pos0, t, &r)) {
+            #pragma omp atomic write
+            err = 1;
+            continue;
+        }
+        const int64_t m = k > 0 ? k : 1;
+        double *qd = (double *)malloc(sizeof(double) * (size_t)H * D);
+        double *gd = (double *)malloc(sizeof(double) * (size_t)H * Dv);
+        double *kd = (double *)malloc(sizeof(double) * (size_t)m * D);
+        double *P = (double *)malloc(sizeof(double) * (size_t)m * H);
+        double *dZ = (double *)malloc(sizeof(double) * (size_t)m * H);
+        double *o = (double *)malloc(sizeof(double) * (size_t)H * Dv);
+        double *delta = (double *)malloc(sizeof(double) * (size_t)H);
+        double *g = (double *)malloc(sizeof(double) * (size_t)m * D);
+        int64_t *pos = (int64_t *)malloc(sizeof(int64_t) * (size_t)m);
+        if (!qd || !gd || !kd || !P || !dZ || !o || !delta || !g || !pos) {
+            #pragma omp atomic write
+            err = 1;
+        } else {
+            int bad = 0;
+            for (int64_t j = 0; j < k; j++) {
+                pos[j] = idx[i * k + j];
+                if (pos[j] >= r.ctx)
+                    bad = 1;
+            }
+            if (bad) {
+                #pragma omp atomic write
+                err = 1;
+            } else {
+                for (int h = 0; h < H; h++) {
+                    for (int d = 0; d < D; d++)
+                        qd[h * D + d] = ora_load(q, q_type, (t * H + h) * (int64_t)D + d);
+                    for (int c = 0; c < Dv; c++)
+                        gd[h * Dv + c] = ora_load(dout, dout_type, (t * H + h) * (int64_t)Dv + c);
+                }
+                for (int64_t j = 0; j < k; j++)
+                    if (pos[j] >= 0)
+                        for (int d = 0; d < D; d++)
+                            kd[j * D + d] = ora_load(kv, kv_type, (r.kv0 + pos[j]) * D + d);
+                /* the forward: logits and the exact softmax per head, then o */
+                for (int h = 0; h < H; h++) {
+                    double M = -INFINITY, Z = 0.0;
+                    for (int64_t j = 0; j < k; j++) {
+                        if (pos[j] < 0)
+                            continue;
+                        double dot = 0.0;
+                        for (int d = 0; d < D; d++)
+                            dot += qd[h * D + d] * kd[j * D + d];
+                        P[j * H + h] = scale * dot;        /* z for now */
+                        if (P[j * H + h] > M)
+                            M = P[j * H + h];
+                    }
+                    for (int64_t j = 0; j < k; j++)
+                        if (pos[j] >= 0)
+                            Z += exp(P[j * H + h] - M);
+                    for (int64_t j = 0; j < k; j++)
+                        P[j * H + h] = pos[j] >= 0 ? exp(P[j * H + h] - M) / Z : 0.0;
+                    for (int c = 0; c < Dv; c++) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < k; j++)
+                            if (pos[j] >= 0)
+                                acc += P[j * H + h] * kd[j * D + c];
+                        o[h * Dv + c] = acc;
+                    }
+                    /* the backward of o = P V, then of the softmax */
+                    double dl = 0.0;
+                    for (int c = 0; c < Dv; c++)
+                        dl += gd[h * Dv + c] * o[h * Dv + c];
+                    delta[h] = dl;
+                    for (int64_t j = 0; j < k; j++) {
+                        if (pos[j] < 0) {
+                            dZ[j * H + h] = 0.0;
+                            continue;
+                        }
+                        double dp = 0.0;
+                        for (int c = 0; c < Dv; c++)
+                            dp += gd[h * Dv + c] * kd[j * D + c];
+                        dZ[j * H + h] = P[j * H + h] * (dp - delta[h]);
+                    }
+                    /* the backward of z = scale q . kv, query side */
+                    for (int d = 0; d < D; d++) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < k; j++)
+                            if (pos[j] >= 0)
+                                acc += dZ[j * H + h] * kd[j * D + d];
+                        dq[(i * H + h) * (int64_t)D + d] = scale * acc;
+                    }
+                }
+                /* key side and value side, per slot (summed over the heads) */
+                for (int64_t j = 0; j < k; j++) {
+                    if (pos[j] < 0)
+                        continue;
+                    for (int d = 0; d < D; d++) {
+                        double acc = 0.0;
+                        for (int h = 0; h < H; h++)
+                            acc += dZ[j * H + h] * qd[h * D + d];
+                        g[j * D + d] = scale * acc;
+                    }
+                    for (int c = 0; c < Dv; c++) {
+                        double acc = 0.0;
+                        for (int h = 0; h < H; h++)
+                            acc += P[j * H + h] * gd[h * Dv + c];
+                        g[j * D + c] += acc;
+                    }
+                }
+                #pragma omp critical(ora_dkv)
+                for (int64_t j = 0; j < k; j++)
+                    if (pos[j] >= 0)
+                        for (int d = 0; d < D; d++)
+                            dkv[(r.kv0 + pos[j]) * D + d] += g[j * D + d];
+            }
+        }
+        free(qd);
+        free(gd);
+        free(kd);
+        free(P);
+        free(dZ);
+        free(o);
+        free(delta);
+        free(g);
+        free(pos);
     }
     return err ? ORA_ERR : ORA_OK;
 }
