@@ -281,6 +281,111 @@ def kl_bench(args, dsa):
     return 0
 
 
+BWD_METRIC = "sparse MLA backward tokens/s (dq and dkv over the top-2048 selection), 32K prefill"
+SEED_DOUT = 0xD5A8         # seed of the attention output gradient
+
+
+def bwd_bench(args, dsa):
+    """One step = the backward of the sparse attention of a 32K prefill (dq of
+    every row, dkv of the latent cache) for a seeded bf16 output gradient.
+    The selection, out and lse come from the library's own forward, run once
+    before the timed region; q and the latent cache are the prefill_32k inputs."""
+    import torch
+    say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+    wl, _ = make_workload("prefill_32k")
+    b = wl.batch
+    t0 = time.time()
+    dev = wl.device("cuda")
+    batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0)
+    fargs = dsa.fwd_args(batch, dev["qi"], dev["qs"], dev["w"], dev["ki"], dev["ks"], dev["q"], dev["kv"], wl.k,
+                         wl.scale)
+    out = torch.empty((b.T, H, DV), dtype=torch.int16, device="cuda")
+    lse = torch.empty((b.T, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((b.T, wl.k), dtype=torch.int32, device="cuda")
+    dsa.prefill_fwd(fargs, batch, out, lse, idx)
+    g = torch.Generator("cuda").manual_seed(SEED_DOUT)
+    dout = torch.randn((b.T, H, DV), dtype=torch.float32, device="cuda", generator=g).to(torch.bfloat16) \
+        .view(torch.int16)
+    dq = torch.empty((b.T, H, D), dtype=torch.float32, device="cuda")
+    dkv = torch.empty((b.N, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, dsa.workspace_size(dsa.WS_SPARSE_MLA_BWD, batch, wl.k)), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    say(f"[bench] workload sparse_bwd_32k: T={b.T} k={wl.k}; inputs and forward ready ({time.time() - t0:.1f} s)")
+
+    def step():
+        dsa.sparse_mla_bwd(batch, dev["q"], dev["kv"], idx, wl.scale, out, lse, dout, dq, dkv, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = b.T * args.steps / elapsed
+    say(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, {tokens_per_s:,.0f} tokens/s")
+
+    # algorithmic work of the whole backward: per selected (row, key) pair and head,
+    # the logits (576), dP (512), dq (576), the key side (576) and the value side (512)
+    nvis = visible_counts(b.cu_q, b.cu_kv, b.pos0)
+    pairs = float(np.sum(np.minimum(nvis, wl.k)))
+    flops = pairs * H * 2.0 * (D + DV + D + D + DV)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    achieved = flops / (kms * 1e-3) / 1e12
+    roof = {"kernel": "dsa_sparse_mla_bwd (bwd_prep, bwd_dz, bwd_dq, bwd_dkv launches)", "bound": "mfma",
+            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "avg_ms": round(kms, 4),
+            "algorithmic_flops": flops}
+    say(f"[bench] backward: {kms:.3f} ms/launch, {achieved:.1f} TFLOP/s ({100 * roof['frac']:.1f}% of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        say("[bench] timing the CPU oracle on a sample of the workload ...")
+        threads = oracle.num_threads()
+
+        def run(n):
+            # the backward's inputs for the sampled rows from the oracle itself (untimed)
+            rows = np.unique(np.linspace(0, b.T - 1, n).astype(np.int64))
+            inp = wl.sampled_host(rows)
+            s_rows = oracle.indexer(b.cu_q, b.cu_kv, b.pos0, inp.qi, inp.qi_scale, inp.w, inp.ki, inp.ki_scale,
+                                    rows=rows)
+            i_rows = oracle.topk(b.cu_q, b.cu_kv, b.pos0, s_rows, wl.k, rows=rows)
+            gd = np.zeros((b.T, H, DV), np.float32)
+            gd[rows] = np.random.default_rng(SEED_DOUT).standard_normal((len(rows), H, DV)).astype(np.float32)
+            t2 = time.perf_counter()
+            oracle.sparse_attn_bwd(b.cu_q, b.cu_kv, b.pos0, inp.q, inp.kv, gd, i_rows, wl.Dv, wl.scale, rows=rows)
+            return len(rows), time.perf_counter() - t2
+        n0, dt = run(16)
+        n = int(min(b.T, 512, max(16, args.cpu_seconds / max(dt / n0, 1e-9))))
+        n, dt = run(n)
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n} query rows evenly spaced over the {b.T} of the workload (exact softmax backward, "
+                         f"dq and the rows' dkv contributions over the 2048 selected keys; the oracle's scores and "
+                         f"selection for those rows made first, untimed), {dt:.1f} s wall"}
+        say(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s on {threads} threads")
+
+    cfg = {"workload": "sparse_bwd_32k", "batch": b.B, "query_tokens": b.T, "cache_rows": b.N, "topk": wl.k,
+           "heads": H, "d_qk": D, "d_v": DV, "entry": "dsa_sparse_mla_bwd"}
+    line = {"metric": BWD_METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 QUANT_METRIC = "FP8 quantise + cache append tokens/s (indexer queries and keys, latent rows), 32K prefill"
 
 
@@ -386,7 +491,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_32k",
                     choices=["prefill_32k", "prefill_4k", "decode_64k", "chunked_128k", "quant_append_32k",
-                             "short_prefill_2k", "indexer_kl_32k"])
+                             "short_prefill_2k", "indexer_kl_32k", "sparse_bwd_32k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=5,
@@ -418,6 +523,8 @@ def main(argv=None):
         return quant_append_bench(args, dsa)
     if args.workload == "indexer_kl_32k":
         return kl_bench(args, dsa)
+    if args.workload == "sparse_bwd_32k":
+        return bwd_bench(args, dsa)
     wl, entry = make_workload(args.workload)
     b = wl.batch
     say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731

@@ -160,6 +160,31 @@ dsa_status dsa_indexer_kl_fwd(const dsa_batch *batch, const uint16_t *q, const u
                               int H, int D, float scale, const float *scores, int64_t ld, const int32_t *idx,
                               int k, float *kl, float *p_out, void *ws, size_t ws_bytes, void *stream);
 
+/* Backward of dsa_sparse_mla_fwd over the same selection, for the sparse
+ * training stage of [R] "Как учили индексатор" (all parameters learn).  With
+ * P[h,j] = exp(scale <q[t,h,:], kv[s_j,:]> - lse[t,h]) over the valid slots j
+ * of idx[t,:] (positions s_j), dP[h,j] = <dout[t,h,:], kv[s_j,:Dv]> and
+ * delta[h] = <dout[t,h,:], out[t,h,:]>:
+ *   dZ[h,j]      = P[h,j] (dP[h,j] - delta[h])
+ *   dq[t,h,:]    = scale * sum_j dZ[h,j] kv[s_j,:]
+ *   dkv[s_j,:]  += scale * sum_h dZ[h,j] q[t,h,:]      (all D dims: the key)
+ *   dkv[s_j,:Dv] += sum_h P[h,j] dout[t,h,:]           (the value)
+ * summed over every row and slot that selects a cache row (a position listed
+ * twice counts twice).  out and lse are the forward's outputs for the same
+ * inputs.  P and dZ are rounded to bf16 before the products that consume them
+ * (the usual precision of attention backward passes); accumulation in fp32.
+ *   q [T,H,D] bf16, kv [N,D] bf16, idx [T,k] int32, out [T,H,Dv] bf16,
+ *   lse [T,H] fp32, dout [T,H,Dv] bf16
+ *   dq [T,H,D] fp32 out (overwritten); dkv [N,D] fp32 out (overwritten: zeroed,
+ *   then accumulated with atomics, so its low bits vary from call to call).
+ * Supported: H = 128, D = 576, Dv = 512, 1 <= k <= 2048, max_kv <= 2^21.
+ * Workspace (required when T > 0): dsa_workspace_size(DSA_WS_SPARSE_MLA_BWD,
+ * ...), 2 * T * ceil(k/32)*32 * H * 2 bytes + T * H * 4. */
+dsa_status dsa_sparse_mla_bwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                              int k, int H, int D, int Dv, float scale, const uint16_t *out, const float *lse,
+                              const uint16_t *dout, float *dq, float *dkv, void *ws, size_t ws_bytes,
+                              void *stream);
+
 /* All inputs of one DSA forward (indexer + top-k + sparse MQA attention). */
 typedef struct {
     dsa_batch batch;
@@ -228,7 +253,8 @@ typedef enum {
     DSA_WS_PREFILL = 2,
     DSA_WS_DECODE = 3,
     DSA_WS_DENSE_MLA = 4,      /* k is ignored (pass any 1..2048) */
-    DSA_WS_INDEXER_KL = 5
+    DSA_WS_INDEXER_KL = 5,
+    DSA_WS_SPARSE_MLA_BWD = 6
 } dsa_ws_entry;
 
 /* Workspace bytes the given entry point needs for this batch (host only; reads

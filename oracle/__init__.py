@@ -56,7 +56,7 @@ def lib():
         L.ora_dense_attn.argtypes = [i32, p, p, p, p, i64, i32, i32, i32, dbl, p, i32, p, i32, p, p]
         L.ora_indexer_kl.argtypes = [i32, p, p, p, p, i64, i32, i32, dbl, p, i32, p, i32, p, i64, p, i32, p, p]
         L.ora_sparse_attn_bwd.argtypes = [i32, p, p, p, p, i64, i32, i32, i32, dbl, p, i32, p, i32, p, i32, p, i32,
-                                          p, p]
+                                          p, i32, p, p]
         L.ora_num_threads.restype = i32
         L.ora_e4m3_encode.argtypes = [ctypes.c_float]
         L.ora_e4m3_encode.restype = ctypes.c_uint8
@@ -257,10 +257,13 @@ def indexer_kl(cu_q, cu_kv, pos0, q, kv, scale, scores, idx=None, rows=None, wan
     return (kl, p) if want_p else kl
 
 
-def sparse_attn_bwd(cu_q, cu_kv, pos0, q, kv, dout, idx, Dv, scale, rows=None):
+def sparse_attn_bwd(cu_q, cu_kv, pos0, q, kv, dout, idx, Dv, scale, rows=None, out=None):
     """Backward of the sparse MQA attention over idx rows [nrows, k]: given
     dout = dL/do [T, H, Dv] (float32 or bf16 bits), returns dq [nrows, H, D]
-    and dkv [N, D] (float64; dkv holds the contributions of the rows asked for)."""
+    and dkv [N, D] (float64; dkv holds the contributions of the rows asked for).
+    out [T, H, Dv] (optional): the forward output delta = <dout, out> is taken
+    from (as a backward handed the forward's rounded output does); default:
+    the exact output."""
     cu_q, cu_kv, pos0, B = _batch(cu_q, cu_kv, pos0)
     T, H, D = q.shape
     N = kv.shape[0]
@@ -271,10 +274,14 @@ def sparse_attn_bwd(cu_q, cu_kv, pos0, q, kv, dout, idx, Dv, scale, rows=None):
     kv = np.ascontiguousarray(kv)
     dout = np.ascontiguousarray(dout)
     assert dout.shape == (T, H, Dv)
+    if out is not None:
+        out = np.ascontiguousarray(out)
+        assert out.shape == (T, H, Dv)
     dq = np.empty((nrows, H, D), dtype=np.float64)
     dkv = np.zeros((N, D), dtype=np.float64)
     rc = lib().ora_sparse_attn_bwd(B, _ptr(cu_q), _ptr(cu_kv), _ptr(pos0), _ptr(r), nrows, H, D, Dv, float(scale),
                                    _ptr(q), _vtype(q), _ptr(kv), _vtype(kv), _ptr(dout), _vtype(dout),
+                                   _ptr(out), _vtype(out) if out is not None else 0,
                                    _ptr(idx), idx.shape[1], _ptr(dq), _ptr(dkv))
     if rc != 0:
         raise ValueError("ora_sparse_attn_bwd failed (index out of range or bad batch)")

@@ -673,14 +673,17 @@ int ora_indexer_kl(int B, const int32_t *cu_q, const int64_t *cu_kv,
  *   dkv[s_j,d] += scale * sum_h dZ[j,h] q[t,h,d]             (d < D: the key),
  *   dkv[s_j,c] += sum_h P[j,h] dout[t,h,c]                   (c < Dv: the value).
  * Negative idx entries are skipped; a position listed twice is two slots.
+ * out (nullable, [T, H, Dv], type out_type): the forward output to take delta
+ * from, delta_h = sum_c dout[t,h,c] out[t,h,c] (what a backward that is handed
+ * the forward's rounded output computes); NULL: the exact o above.
  *   dq [nrows, H, D] f64 out; dkv [N, D] f64, accumulated (the caller zeroes).
  */
 int ora_sparse_attn_bwd(int B, const int32_t *cu_q, const int64_t *cu_kv,
                         const int32_t *pos0, const int32_t *rows, int64_t nrows,
                         int H, int D, int Dv, double scale,
                         const void *q, int q_type, const void *kv, int kv_type,
-                        const void *dout, int dout_type, const int32_t *idx, int k,
-                        double *dq, double *dkv)
+                        const void *dout, int dout_type, const void *out, int out_type,
+                        const int32_t *idx, int k, double *dq, double *dkv)
 {
     int err = 0;
     #pragma omp parallel for schedule(dynamic, 1)
@@ -754,7 +757,8 @@ int ora_sparse_attn_bwd(int B, const int32_t *cu_q, const int64_t *cu_kv,
                     /* the backward of o = P V, then of the softmax */
                     double dl = 0.0;
                     for (int c = 0; c < Dv; c++)
-                        dl += gd[h * Dv + c] * o[h * Dv + c];
+                        dl += gd[h * Dv + c] *
+                              (out ? ora_load(out, out_type, (t * H + h) * (int64_t)Dv + c) : o[h * Dv + c]);
                     delta[h] = dl;
                     for (int64_t j = 0; j < k; j++) {
                         if (pos[j] < 0) {

@@ -7,7 +7,8 @@ memory and streams only.  Importing this package fails loudly when the built
 library is missing: there is no fallback implementation.
 
 Entry points (same names as the C ABI, without the ``dsa_`` prefix):
-    indexer_scores, topk, sparse_mla_fwd, dense_mla_fwd, indexer_kl_fwd, prefill_fwd, decode_fwd,
+    indexer_scores, topk, sparse_mla_fwd, dense_mla_fwd, indexer_kl_fwd, sparse_mla_bwd, prefill_fwd,
+    decode_fwd,
     quantize_queries, append_cache,
     workspace_size, status_string, version
 """
@@ -29,10 +30,10 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
-WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE, WS_DENSE_MLA, WS_INDEXER_KL = range(6)
+WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE, WS_DENSE_MLA, WS_INDEXER_KL, WS_SPARSE_MLA_BWD = range(7)
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_dense_mla_fwd", "dsa_indexer_kl_fwd",
-           "dsa_prefill_fwd",
+           "dsa_sparse_mla_bwd", "dsa_prefill_fwd",
            "dsa_decode_fwd", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
            "dsa_status_string", "dsa_version")
 
@@ -66,6 +67,7 @@ _lib.dsa_topk.argtypes = [_BP, _P, _I64, _I, _P, _P, _SZ, _P]
 _lib.dsa_sparse_mla_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
 _lib.dsa_dense_mla_fwd.argtypes = [_BP, _P, _P, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
 _lib.dsa_indexer_kl_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _F, _P, _I64, _P, _I, _P, _P, _P, _SZ, _P]
+_lib.dsa_sparse_mla_bwd.argtypes = [_BP, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_prefill_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_decode_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_workspace_size.argtypes = [_I, _BP, _I, _I, _I]
@@ -218,6 +220,20 @@ def indexer_kl_fwd(batch: Batch, q, kv, lse, scale: float, scores, kl, idx=None,
                                  _ptr(ws), nbytes, _stream(stream))
     _check(st, "dsa_indexer_kl_fwd")
     return kl
+
+
+def sparse_mla_bwd(batch: Batch, q, kv, idx, scale: float, out, lse, dout, dq, dkv, Dv: int = 512, ws=None,
+                   stream=None):
+    """Backward of sparse_mla_fwd over the same idx: dq [T, H, D] fp32 and
+    dkv [N, D] fp32 (overwritten) from dout [T, H, Dv] bf16 and the forward's
+    out and lse (see dsa_sparse_mla_bwd)."""
+    k = idx.shape[1]
+    ws, nbytes = _workspace(WS_SPARSE_MLA_BWD, batch, k, ws, q.device)
+    st = _lib.dsa_sparse_mla_bwd(ctypes.byref(batch.c), _ptr(q), _ptr(kv), _ptr(idx), int(k), q.shape[1],
+                                 q.shape[2], int(Dv), float(scale), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                 _ptr(dkv), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "dsa_sparse_mla_bwd")
+    return dq, dkv
 
 
 def fwd_args(batch: Batch, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, k: int, scale: float,

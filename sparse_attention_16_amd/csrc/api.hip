@@ -84,6 +84,14 @@ size_t kl_ws(const dsa_batch *b, int k) {
     return up((size_t)b->total_q * s * 5 * 4);
 }
 
+// Backward workspace: P and scale * dZ per (row, slot, head) in bf16, with
+// k rounded up to whole 32-slot blocks, then delta per (row, head).
+int bwd_kpad(int k) { return (k + 31) / 32 * 32; }
+size_t bwd_ws(const dsa_batch *b, int k) {
+    const size_t z = up((size_t)b->total_q * bwd_kpad(k) * kH * 2);
+    return 2 * z + up((size_t)b->total_q * kH * 4);
+}
+
 int64_t score_ld(int max_kv) { return ((int64_t)max_kv + 63) / 64 * 64; }
 
 // Slot budget of the dense attention: the longest context (at least 1).
@@ -381,6 +389,51 @@ dsa_status dsa_indexer_kl_fwd(const dsa_batch *batch, const uint16_t *q, const u
     return hip_status(launch_indexer_kl(p, batch->total_q, static_cast<hipStream_t>(stream)));
 }
 
+dsa_status dsa_sparse_mla_bwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                              int k, int H, int D, int Dv, float scale, const uint16_t *out, const float *lse,
+                              const uint16_t *dout, float *dq, float *dkv, void *ws, size_t ws_bytes,
+                              void *stream) {
+    dsa_status st = check_batch(batch);
+    if (st != DSA_OK) return st;
+    if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
+    if ((st = check_k(k)) != DSA_OK) return st;
+    if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return DSA_ERR_INVALID_ARG;
+    if (batch->total_q == 0 && batch->total_kv == 0) return DSA_OK;
+    if (batch->total_kv > 0 && (!kv || !dkv)) return DSA_ERR_INVALID_ARG;
+    if (batch->total_q > 0 && (!q || !idx || !out || !lse || !dout || !dq)) return DSA_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, kv, idx, out, lse, dout, dq, dkv};
+    for (const void *ptr : ptrs)
+        if (ptr && !al16(ptr)) return DSA_ERR_INVALID_ARG;
+    const size_t need = bwd_ws(batch, k);
+    if (batch->total_q > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
+    BwdParams p;
+    p.cu_q = batch->cu_q;
+    p.cu_kv = batch->cu_kv;
+    p.pos0 = batch->pos0;
+    p.B = batch->batch;
+    p.total_kv = batch->total_kv;
+    p.max_kv = batch->max_kv;
+    p.q = q;
+    p.kv = kv;
+    p.idx = idx;
+    p.k = k;
+    p.kpad = bwd_kpad(k);
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.out = out;
+    p.lse = lse;
+    p.dout = dout;
+    p.dq = dq;
+    p.dkv = dkv;
+    char *w = static_cast<char *>(ws);
+    const size_t z = up((size_t)batch->total_q * p.kpad * kH * 2);
+    p.ps = reinterpret_cast<uint16_t *>(w);
+    p.dzs = w ? reinterpret_cast<uint16_t *>(w + z) : nullptr;
+    p.delta = w ? reinterpret_cast<float *>(w + 2 * z) : nullptr;
+    return hip_status(launch_sparse_mla_bwd(p, batch->total_q, static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_prefill_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse, int32_t *idx_out,
                            void *ws, size_t ws_bytes, void *stream) {
     return run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, false);
@@ -402,6 +455,7 @@ size_t dsa_workspace_size(dsa_ws_entry entry, const dsa_batch *batch, int k, int
         case DSA_WS_DECODE: return fwd_ws(batch, k);
         case DSA_WS_DENSE_MLA: return batch->max_kv > kKMax ? 0 : mla_ws(batch, dense_slots(batch));
         case DSA_WS_INDEXER_KL: return batch->max_kv > MAX_KV_ATTN ? 0 : kl_ws(batch, k);
+        case DSA_WS_SPARSE_MLA_BWD: return batch->max_kv > MAX_KV_ATTN ? 0 : bwd_ws(batch, k);
     }
     return 0;
 }

@@ -84,6 +84,30 @@ struct KlParams {
     float *part;            // [T, splits, 5] partial sums (workspace)
 };
 
+struct BwdParams {
+    const int32_t *cu_q;
+    const int64_t *cu_kv;
+    const int32_t *pos0;
+    int B;
+    int64_t total_kv;
+    int max_kv;
+    const uint16_t *q;      // [T, 128, 576] bf16
+    const uint16_t *kv;     // [N, 576] bf16
+    const int32_t *idx;     // [T, k]
+    int k;
+    int kpad;               // k rounded up to whole 32-slot blocks
+    float scale;            // softmax scale
+    float scale_log2;       // scale * log2(e)
+    const uint16_t *out;    // [T, 128, 512] bf16 forward output
+    const float *lse;       // [T, 128] forward log-sum-exp (natural log)
+    const uint16_t *dout;   // [T, 128, 512] bf16 gradient of out
+    float *dq;              // [T, 128, 576] out
+    float *dkv;             // [N, 576] out (zeroed, then accumulated)
+    uint16_t *ps;           // [T, kpad, 128] bf16 workspace: P
+    uint16_t *dzs;          // [T, kpad, 128] bf16 workspace: scale * dZ
+    float *delta;           // [T, 128] workspace
+};
+
 constexpr int TOPK_CHUNK = 32768;     // columns selected per workgroup in LDS
 constexpr int TOPK_MAX_CHUNKS = 8;    // merge capacity: 8 x 2048 candidates
 constexpr int MLA_BK = 32;            // keys per gathered block
@@ -95,6 +119,7 @@ hipError_t launch_indexer(const IndexerParams &p, int T, int max_q, bool decode_
 hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s);
 hipError_t launch_select_all_visible(const TopkParams &p, int T, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s);
+hipError_t launch_sparse_mla_bwd(const BwdParams &p, int T, hipStream_t s);
 hipError_t launch_indexer_kl(const KlParams &p, int T, hipStream_t s);
 hipError_t launch_quant_queries(const float *q, int64_t T, uint8_t *q_fp8, float *q_scale, hipStream_t s);
 hipError_t launch_append_cache(const float *k_new, const uint16_t *kv_new, int64_t R, const int64_t *dst,

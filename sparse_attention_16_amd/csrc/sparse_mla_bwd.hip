@@ -1,0 +1,465 @@
+// sparse_mla_bwd.hip — backward of the sparse MQA-mode attention on gfx950.
+//
+// Page "Техотчёт DeepSeek-V3.2 (2025): разреженное внимание DSA и
+// масштабирование RL": the attention of section "Отбор и основное внимание"
+// (one selected set and one latent row per key, shared by all 128 heads; the
+// value is the row's first 512 dims) is trained in the sparse stage of
+// section "Как учили индексатор", where all parameters learn.  For query row
+// t, head h and selected slot j (position s_j):
+//   P[h,j]   = exp(scale <q[t,h,:], kv[s_j,:]> - lse[t,h])
+//   dP[h,j]  = <dout[t,h,:], kv[s_j,:512]>,   delta[h] = <dout[t,h,:], out[t,h,:]>
+//   dZs[h,j] = scale P[h,j] (dP[h,j] - delta[h])      (the softmax's backward, scaled)
+//   dq[t,h,:]    = sum_j dZs[h,j] kv[s_j,:]
+//   dkv[s_j,:]  += sum_h dZs[h,j] q[t,h,:]   +   [sum_h P[h,j] dout[t,h,:], 0 .. 0]
+// Four launches, each one workgroup per query row (the longest rows first):
+//   bwd_prep: delta per (row, head); dkv zeroed;
+//   bwd_dz:   the logits and dP on the bf16 MFMA (each 32-slot block of rows
+//             gathered into LDS with direct-to-LDS loads, the forward's
+//             layout; q and dout rows in VGPRs), P and dZs rounded to bf16
+//             into a workspace [row][slot][head] (bf16 is also what the
+//             products below take as MFMA operands);
+//   bwd_dq:   dq^T = K^T dZs^T: both operands through LDS transpose reads,
+//             the accumulators (a wave's dims x all heads) in registers;
+//   bwd_dkv:  per block [dZs^T | P^T] [q | dout] over the 128 heads, with the
+//             row's q and dout resident in VGPRs in head-contraction layout,
+//             added to dkv with fp32 atomics.
+#include "dsa_device.h"
+#include "kernels.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int H = 128, D = 576, DV = 512;
+constexpr int BK = 32;                    // slots per block
+constexpr int NW = 8;                     // waves per workgroup
+constexpr int NT = NW * kWave;
+constexpr int KS = D / 32;                // 18 k-steps over the dims (16 latent + 2 rope)
+constexpr int KSV = DV / 32;              // 16 k-steps over the value dims
+constexpr int ROWB = D * 2;               // 1152 bytes per latent row
+constexpr int PA = 1056;                  // LDS pitch of a row's first 1024 bytes
+constexpr int RB = BK * PA;               // rope slabs: 4 x (8 rows x 128 B)
+constexpr int BUF = RB + BK * 128;        // 37888 bytes per gathered block
+constexpr int ZP = H * 2;                 // 256 bytes per slot row of a P / dZs block
+constexpr int ZBUF = BK * ZP;             // 8 KB per P / dZs block
+constexpr int MAX_SEL = 2048;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int AHEAD = 3;                  // k-steps of K operands read ahead in bwd_dz
+
+typedef DSA_LDS uint8_t lds_u8;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+
+// The row's selected positions in LDS (-1 for an unusable slot: -1 entry,
+// outside the context, past k), and the number of 32-slot blocks up to the
+// last usable one.  maskv: lane b holds block b's 32-bit usable-slot mask.
+struct Slots {
+    int nblk;
+    uint32_t maskv;
+};
+__device__ __forceinline__ Slots stage_slots(const BwdParams &p, int t, const RowInfo &ri, int32_t *sel) {
+    const int nsel = ri.ctx > 0 ? p.k : 0;
+    const int32_t *__restrict__ idx_row = p.idx + (int64_t)t * p.k;
+    Slots s;
+    s.nblk = (nsel + BK - 1) / BK;
+    for (int j = threadIdx.x; j < s.nblk * BK; j += NT) {
+        const int v = j < nsel ? idx_row[j] : -1;
+        sel[j] = (v >= 0 && v < ri.ctx) ? v : -1;
+    }
+    const int l = lane_id();
+    s.maskv = 0;
+    for (int it = 0; it * kWave < nsel; ++it) {
+        const int j = it * kWave + l;
+        const bool ok = j < nsel && (uint32_t)idx_row[j] < (uint32_t)ri.ctx;
+        const uint64_t m = __ballot(ok);
+        s.maskv = l == 2 * it ? (uint32_t)m : (l == 2 * it + 1 ? (uint32_t)(m >> 32) : s.maskv);
+    }
+    const uint64_t live = __ballot(s.maskv != 0u);
+    const int nlive = live ? 64 - (int)__builtin_clzll(live) : 0;
+    s.nblk = s.nblk < nlive ? s.nblk : nlive;
+    return s;
+}
+
+__device__ __forceinline__ uint64_t seq_base(const uint16_t *kv, int64_t kv0) {
+    const uint64_t b = (uint64_t)(uintptr_t)kv + (uint64_t)kv0 * ROWB;
+    // (readfirstlane returns int: widen through uint32_t, or the low word is sign-extended)
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+           (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+}
+
+// Loads block blk's 32 rows into buf: wave w the latent parts of rows
+// 4w .. 4w+3 (1 KB each), waves 0..3 the rope slab of rows 8w .. 8w+7 (lane
+// l: row 8w + l/8, its 16-byte chunk (l%8) ^ (l/8)).  Unusable slots load
+// the sequence's row 0 (the row must have a context).
+__device__ __forceinline__ void gather8(const DSA_LDS int32_t *sel, int blk, int wave, int l, uint64_t kvb,
+                                        lds_u8 *buf) {
+    const i32x4 a = *reinterpret_cast<const DSA_LDS i32x4 *>(sel + blk * BK + 4 * wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int pos = __builtin_amdgcn_readfirstlane(a[i]);
+        const uint32_t row = pos < 0 ? 0u : (uint32_t)pos;
+        dma16s(kvb + (uint64_t)row * ROWB, 16u * (uint32_t)l, buf + (4 * wave + i) * PA);
+    }
+    if (wave < 4) {
+        const int ps = sel[blk * BK + 8 * wave + (l >> 3)];
+        const uint32_t row = ps < 0 ? 0u : (uint32_t)ps;
+        dma16s(kvb, row * ROWB + 1024u + 16u * (uint32_t)((l & 7) ^ (l >> 3)), buf + RB + wave * 1024);
+    }
+}
+
+// One 8 KB block [32 slots][128 heads] of a workspace array into LDS (wave w:
+// slots 4w .. 4w+3, one 1 KB load).
+__device__ __forceinline__ void load_zblock(const uint16_t *src, int wave, int l, lds_u8 *buf) {
+    uint64_t base = (uint64_t)(uintptr_t)src + (uint64_t)wave * 1024;
+    base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+           (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
+    dma16s(base, 16u * (uint32_t)l, buf + wave * 1024);
+}
+
+__device__ __forceinline__ bf16x8 tr_pair(const lds_u8 *lo, const lds_u8 *hi) {
+    const i16x4 a = lds_read_tr16(lo), b = lds_read_tr16(hi);
+    const i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Byte offset (in a gathered block) of the 8 bytes a lane addresses for a
+// transpose read of K^T: key row kr, dims d0 .. d0+3 (d0 a multiple of 4).
+__device__ __forceinline__ int kt_off(int kr, int d0) {
+    if (d0 < 512) return kr * PA + 2 * d0;
+    const int c = (d0 - 512) >> 3, half = ((d0 - 512) >> 2) & 1, rr = kr & 7;
+    return RB + (kr >> 3) * 1024 + rr * 128 + 16 * (c ^ rr) + 8 * half;
+}
+
+}  // namespace
+
+// delta[t, h] = <dout[t,h,:], out[t,h,:]>; two threads per head.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+    const int t = blockIdx.x;
+    const int h = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const uint16_t *g = p.dout + ((int64_t)t * H + h) * DV + 256 * half;
+    const uint16_t *o = p.out + ((int64_t)t * H + h) * DV + 256 * half;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < 256; c += 8) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(g + c);
+        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(o + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+    }
+    acc += __shfl_xor(acc, 1, kWave);
+    if (half == 0) p.delta[(int64_t)t * H + h] = acc;
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float4 *x, int64_t n4) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+        x[i] = float4{0.f, 0.f, 0.f, 0.f};
+}
+
+// P and dZs of every usable block of a row.  Wave w owns heads 16w .. 16w+15:
+// its q (18 k-steps) and dout (16 k-steps) operands stay in VGPRs.
+__global__ __launch_bounds__(NT) void bwd_dz_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t kb[2][BUF];
+    __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
+    __shared__ __attribute__((aligned(16))) uint16_t tz[NW][2][BK * 16];   // per wave: P, dZs of a block
+
+    const int t = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
+    const int row16 = l & 15, grp = l >> 4;
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    const Slots sl = stage_slots(p, t, ri, sel);
+    const int nblk = sl.nblk;
+
+    const int h = 16 * wave + row16;
+    bf16x8 qb[KS], gb[KSV];
+    {
+        const uint16_t *qrow = p.q + ((int64_t)t * H + h) * D + 8 * grp;
+        const uint16_t *grow = p.dout + ((int64_t)t * H + h) * DV + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks) gb[ks] = *reinterpret_cast<const bf16x8 *>(grow + 32 * ks);
+    }
+    const float ls = p.lse[(int64_t)t * H + h];
+    const float lse2 = ls > -INFINITY && ls < INFINITY ? ls * LOG2E : INFINITY;   // no finite lse: P = 0
+    const float dl = p.delta[(int64_t)t * H + h];
+    const uint64_t kvb = seq_base(p.kv, ri.kv0);
+
+    const int rr = row16 & 7;
+    const int kA = row16 * PA + 16 * grp;
+    const int kR = RB + (row16 >> 3) * 1024 + rr * 128;
+    const int kR16 = kR + 16 * (grp ^ rr);
+    const int kR17 = kR + 16 * ((4 + grp) ^ rr);
+    auto koff = [&](int ks, int mt) {
+        return ks < 16 ? kA + mt * 16 * PA + 64 * ks : (ks == 16 ? kR16 : kR17) + mt * 2048;
+    };
+    DSA_LDS uint16_t *tp = (DSA_LDS uint16_t *)tz[wave][0];
+    DSA_LDS uint16_t *tzd = (DSA_LDS uint16_t *)tz[wave][1];
+    uint16_t *ps_row = p.ps + (int64_t)t * p.kpad * H;
+    uint16_t *dz_row = p.dzs + (int64_t)t * p.kpad * H;
+
+    __syncthreads();   // the slot positions
+    if (nblk > 0) gather8((const DSA_LDS int32_t *)sel, 0, wave, l, kvb, (lds_u8 *)kb[0]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    lds_barrier();
+
+    for (int b = 0; b < nblk; ++b) {
+        const int cur = b & 1;
+        const lds_u8 *buf = (const lds_u8 *)kb[cur];
+        if (b + 1 < nblk) gather8((const DSA_LDS int32_t *)sel, b + 1, wave, l, kvb, (lds_u8 *)kb[cur ^ 1]);
+
+        // S^T = K q^T and dP^T = V dout^T: lane = head row16, keys 16*mt + 4*grp + r
+        f32x4 s[2], g[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            g[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        bf16x8 kr[AHEAD + 1][2];
+#pragma unroll
+        for (int ks = 0; ks < AHEAD; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) kr[ks][mt] = *reinterpret_cast<const DSA_LDS bf16x8 *>(buf + koff(ks, mt));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + AHEAD < KS) {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    kr[(ks + AHEAD) % (AHEAD + 1)][mt] =
+                        *reinterpret_cast<const DSA_LDS bf16x8 *>(buf + koff(ks + AHEAD, mt));
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                s[mt] = mfma_bf16_16x16x32(kr[ks % (AHEAD + 1)][mt], qb[ks], s[mt]);
+                if (ks < KSV) g[mt] = mfma_bf16_16x16x32(kr[ks % (AHEAD + 1)][mt], gb[ks], g[mt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // P and dZs of the block's slots (0 for unusable ones), transposed
+        // through the wave's LDS tiles to [slot][16 heads] rows
+        const uint32_t vmask = __builtin_amdgcn_readlane(sl.maskv, b);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int slot = 16 * mt + 4 * grp + r;
+                const bool ok = (vmask >> slot) & 1u;
+                const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(s[mt][r], p.scale_log2, -lse2)) : 0.f;
+                const float dz = p.scale * pe * (g[mt][r] - dl);
+                tp[slot * 16 + row16] = __builtin_bit_cast(uint16_t, (__bf16)pe);
+                tzd[slot * 16 + row16] = __builtin_bit_cast(uint16_t, (__bf16)dz);
+            }
+        {
+            // lane l: slot l/2, heads 8*(l%2) .. +7 of the wave's 16
+            const int slot = l >> 1, hh = 8 * (l & 1);
+            const int64_t o = (int64_t)(b * BK + slot) * H + 16 * wave + hh;
+            *reinterpret_cast<bf16x8 *>(ps_row + o) = *reinterpret_cast<const DSA_LDS bf16x8 *>(tp + slot * 16 + hh);
+            *reinterpret_cast<bf16x8 *>(dz_row + o) = *reinterpret_cast<const DSA_LDS bf16x8 *>(tzd + slot * 16 + hh);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of block b+1
+        lds_barrier();
+    }
+}
+
+// dq^T[dims x heads] = sum over blocks of K^T[dims x 32] dZs^T[32 x heads].
+// Wave w owns latent dim tiles 4w .. 4w+3 and, for w < 4, rope tile w.
+__global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t kb[2][BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t zb[2][ZBUF];
+    __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
+
+    const int t = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
+    const int row16 = l & 15, grp = l >> 4;
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    const Slots sl = stage_slots(p, t, ri, sel);
+    const int nblk = sl.nblk;
+    const int nct = wave < 4 ? 5 : 4;
+    const uint64_t kvb = seq_base(p.kv, ri.kv0);
+    const uint16_t *dz_row = p.dzs + (int64_t)t * p.kpad * H;
+
+    // transpose-read addressing: lane row16 of a 16-lane group points at row
+    // (4*grp + row16/4) [+16 for the second half], 4 columns 4*(row16%4) ..
+    const int trow = 4 * grp + (row16 >> 2), tcol = 4 * (row16 & 3);
+    auto dim_tile = [&](int i) { return i < 4 ? 4 * wave + i : 32 + wave; };
+
+    f32x4 acc[5][8];
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+#pragma unroll
+        for (int T = 0; T < 8; ++T) acc[i][T] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();
+    if (nblk > 0) {
+        gather8((const DSA_LDS int32_t *)sel, 0, wave, l, kvb, (lds_u8 *)kb[0]);
+        load_zblock(dz_row, wave, l, (lds_u8 *)zb[0]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+
+    for (int b = 0; b < nblk; ++b) {
+        const int cur = b & 1;
+        const lds_u8 *buf = (const lds_u8 *)kb[cur];
+        const lds_u8 *zbuf = (const lds_u8 *)zb[cur];
+        if (b + 1 < nblk) {
+            gather8((const DSA_LDS int32_t *)sel, b + 1, wave, l, kvb, (lds_u8 *)kb[cur ^ 1]);
+            load_zblock(dz_row + (int64_t)(b + 1) * BK * H, wave, l, (lds_u8 *)zb[cur ^ 1]);
+        }
+        bf16x8 a[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+            if (i < nct) {
+                const int d0 = 16 * dim_tile(i) + tcol;
+                a[i] = tr_pair(buf + kt_off(trow, d0), buf + kt_off(16 + trow, d0));
+            }
+#pragma unroll
+        for (int T = 0; T < 8; ++T) {
+            const int c0 = 2 * (16 * T + tcol);
+            const bf16x8 bz = tr_pair(zbuf + trow * ZP + c0, zbuf + (16 + trow) * ZP + c0);
+#pragma unroll
+            for (int i = 0; i < 5; ++i)
+                if (i < nct) acc[i][T] = mfma_bf16_16x16x32(a[i], bz, acc[i][T]);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_barrier();
+    }
+
+    // lane holds dims 16*tile + 4*grp + r of head 16*T + row16
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+        if (i < nct)
+#pragma unroll
+            for (int T = 0; T < 8; ++T) {
+                float *o = p.dq + ((int64_t)t * H + 16 * T + row16) * D + 16 * dim_tile(i) + 4 * grp;
+                *reinterpret_cast<f32x4 *>(o) = acc[i][T];
+            }
+}
+
+// dkv rows of a row's selected slots: per block, D[32 slots x dims] =
+// dZs^T[32 x 128 heads] q[128 x dims] (+ P^T dout on the value dims).
+// Wave w owns latent dim tiles 4w .. 4w+3 and, for w < 4, rope tile w; the
+// row's q and dout for those dims stay in VGPRs as MFMA B operands.
+__global__ __launch_bounds__(NT) void bwd_dkv_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t zb[2][ZBUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t pb[2][ZBUF];
+    __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
+
+    const int t = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
+    const int row16 = l & 15, grp = l >> 4;
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    const Slots sl = stage_slots(p, t, ri, sel);
+    const int nblk = sl.nblk;
+    const int nct = wave < 4 ? 5 : 4;
+    auto dim_tile = [&](int i) { return i < 4 ? 4 * wave + i : 32 + wave; };
+    const uint16_t *dz_row = p.dzs + (int64_t)t * p.kpad * H;
+    const uint16_t *ps_row = p.ps + (int64_t)t * p.kpad * H;
+    float *dkv0 = p.dkv + ri.kv0 * D;
+
+    // B operands: lane (dim row16 of a tile, group grp) holds heads
+    // 32*ks + 8*grp .. +7 at that dim.  Each pair of heads is packed into one
+    // word as it arrives (the empty asm keeps the packing here: left alone,
+    // the compiler keeps the 16-bit halves apart and packs them inside the
+    // block loop, spilling them in between).
+    auto gather8h = [&](const uint16_t *src, int64_t stride) {
+        i32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t v = (uint32_t)src[(int64_t)(2 * e) * stride] | ((uint32_t)src[(int64_t)(2 * e + 1) * stride] << 16);
+            asm volatile("" : "+v"(v));
+            w[e] = (int)v;
+        }
+        return __builtin_bit_cast(bf16x8, w);
+    };
+    bf16x8 qb[4][5], gb[4][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+            if (i < nct)
+                qb[ks][i] = gather8h(p.q + ((int64_t)t * H + 32 * ks + 8 * grp) * D + 16 * dim_tile(i) + row16, D);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            gb[ks][i] = gather8h(p.dout + ((int64_t)t * H + 32 * ks + 8 * grp) * DV + 16 * dim_tile(i) + row16, DV);
+    }
+
+    f32x4 acc[2][5];
+    // adds block b's results to dkv (slots whose position is -1 are skipped)
+    auto scatter = [&](int b) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pos = sel[b * BK + 16 * mt + 4 * grp + r];
+                if (pos >= 0) {
+                    float *dst = dkv0 + (int64_t)pos * D + row16;
+#pragma unroll
+                    for (int i = 0; i < 5; ++i)
+                        if (i < nct) atomicAdd(dst + 16 * dim_tile(i), acc[mt][i][r]);
+                }
+            }
+    };
+
+    __syncthreads();
+    if (nblk > 0) {
+        load_zblock(dz_row, wave, l, (lds_u8 *)zb[0]);
+        load_zblock(ps_row, wave, l, (lds_u8 *)pb[0]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+
+    for (int b = 0; b < nblk; ++b) {
+        const int cur = b & 1;
+        // the previous block's sums go out first (their atomics complete under
+        // this block's products), then this block's loads of the next one
+        if (b > 0) scatter(b - 1);
+        __builtin_amdgcn_sched_barrier(0);   // (the sums leave their registers before the next block's)
+        if (b + 1 < nblk) {
+            load_zblock(dz_row + (int64_t)(b + 1) * BK * H, wave, l, (lds_u8 *)zb[cur ^ 1]);
+            load_zblock(ps_row + (int64_t)(b + 1) * BK * H, wave, l, (lds_u8 *)pb[cur ^ 1]);
+        }
+        const lds_u8 *zbuf = (const lds_u8 *)zb[cur];
+        const lds_u8 *pbuf = (const lds_u8 *)pb[cur];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 5; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                // A: slot 16*mt + row16, heads 32*ks + 8*grp .. +7
+                const int off = (16 * mt + row16) * ZP + 2 * (32 * ks + 8 * grp);
+                const bf16x8 az = *reinterpret_cast<const DSA_LDS bf16x8 *>(zbuf + off);
+                const bf16x8 ap = *reinterpret_cast<const DSA_LDS bf16x8 *>(pbuf + off);
+#pragma unroll
+                for (int i = 0; i < 5; ++i)
+                    if (i < nct) acc[mt][i] = mfma_bf16_16x16x32(az, qb[ks][i], acc[mt][i]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mt][i] = mfma_bf16_16x16x32(ap, gb[ks][i], acc[mt][i]);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // (keeps the operand reads from all moving up front)
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_barrier();
+    }
+    if (nblk > 0) scatter(nblk - 1);
+}
+
+hipError_t launch_sparse_mla_bwd(const BwdParams &p, int T, hipStream_t s) {
+    const int64_t n4 = p.total_kv * D / 4;
+    if (n4 > 0) {
+        const int64_t want = (n4 + 255) / 256;
+        const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<float4 *>(p.dkv), n4);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(T), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(bwd_dz_kernel, dim3(T), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(T), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkv_kernel, dim3(T), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -182,6 +182,31 @@ def test_indexer_kl_validation(dsa):
                                   None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
 
 
+def test_sparse_mla_bwd_validation(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa, 4096, 4096)
+    need = lib.dsa_workspace_size(dsa.WS_SPARSE_MLA_BWD, ctypes.byref(b), 2048, 128, 512)
+    assert need >= 2 * 4096 * 2048 * 128 * 2 + 4096 * 128 * 4
+
+    def call(q=FAKE, kv=FAKE, idx=FAKE, k=2048, H=128, D=576, Dv=512, scale=0.04, out=FAKE, lse=FAKE,
+             dout=FAKE, dq=FAKE, dkv=FAKE, ws=FAKE, nbytes=need, batch=b):
+        return lib.dsa_sparse_mla_bwd(ctypes.byref(batch) if batch is not None else None, q, kv, idx, k, H, D, Dv,
+                                      scale, out, lse, dout, dq, dkv, ws, nbytes, None)
+
+    assert call(batch=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(H=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(Dv=576) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(k=0) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(batch=_batch(dsa, 4, 3 << 21, max_kv=3 << 21)) == dsa.DSA_ERR_UNSUPPORTED
+    for name in ("q", "kv", "idx", "out", "lse", "dout", "dq", "dkv"):
+        assert call(**{name: None}) == dsa.DSA_ERR_INVALID_ARG, name
+        assert call(**{name: FAKE + 8}) == dsa.DSA_ERR_INVALID_ARG, name
+    assert call(scale=float("nan")) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ws=None, nbytes=0) == dsa.DSA_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == dsa.DSA_ERR_WORKSPACE
+
+
 def test_fused_validation(dsa):
     lib = dsa.raw_lib()
     b = _batch(dsa)

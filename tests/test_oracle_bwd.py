@@ -11,7 +11,9 @@ Each pin ties the hand-derived backward to something other than itself:
   * one selected key: the softmax has zero gradient, so dq = 0 and dkv is
     sum_h dout[h] in the value dims, 0 in the rest;
   * identical key rows: dq = 0 (the softmax's gradient sums to 0 per head);
-  * linearity in dout.
+  * linearity in dout;
+  * delta from a given forward output: the exact output reproduces the exact
+    delta, and a perturbation moves dq by the closed-form amount.
 """
 import numpy as np
 import torch
@@ -101,3 +103,24 @@ def test_identical_keys_give_zero_query_gradient_and_linearity():
     dq2, dkv2 = oracle.sparse_attn_bwd(b.cu_q, b.cu_kv, b.pos0, q, kv, 2 * dout, idx, 4, 0.4)   # exact in f32
     assert np.allclose(dq2, 2 * dq1, rtol=1e-12, atol=1e-14)
     assert np.allclose(dkv2, 2 * dkv1, rtol=1e-12, atol=1e-14)
+
+
+def test_delta_from_a_given_forward_output():
+    # delta taken from the forward's own output (in double, as it returns it in
+    # f32) matches the exact one; a perturbed output moves dq by exactly
+    # -scale * d(delta)_h * sum_j P[j,h] kv[s_j,:]
+    b, q, kv, dout, idx = _case(seed=6)
+    scale = 0.45
+    o, _ = oracle.sparse_attn(b.cu_q, b.cu_kv, b.pos0, q, kv, idx, 4, scale)
+    dq0, dkv0 = oracle.sparse_attn_bwd(b.cu_q, b.cu_kv, b.pos0, q, kv, dout, idx, 4, scale)
+    dq1, dkv1 = oracle.sparse_attn_bwd(b.cu_q, b.cu_kv, b.pos0, q, kv, dout, idx, 4, scale, out=o)
+    assert np.allclose(dq1, dq0, rtol=1e-5, atol=1e-6) and np.allclose(dkv1, dkv0, rtol=1e-5, atol=1e-6)
+    o2 = o.copy()
+    o2[2, 1, :] += np.float32(0.25)
+    dq2, _ = oracle.sparse_attn_bwd(b.cu_q, b.cu_kv, b.pos0, q, kv, dout, idx, 4, scale, out=o2)
+    ddelta = 0.25 * float(np.sum(dout[2, 1].astype(np.float64)))
+    o_full, _ = oracle.sparse_attn(b.cu_q, b.cu_kv, b.pos0, q, kv, idx, 6, scale)   # sum_j P kv over all 6 dims
+    assert np.allclose(dq2[2, 1] - dq1[2, 1], -scale * ddelta * o_full[2, 1].astype(np.float64), rtol=1e-4,
+                       atol=1e-6)
+    assert np.allclose(np.delete(dq2.reshape(-1, 6), 2 * 3 + 1, axis=0), np.delete(dq1.reshape(-1, 6), 2 * 3 + 1,
+                                                                                     axis=0), rtol=0, atol=0)
