@@ -179,7 +179,7 @@ dsa_status dsa_indexer_kl_fwd(const dsa_batch *batch, const uint16_t *q, const u
  *   then accumulated with atomics, so its low bits vary from call to call).
  * Supported: H = 128, D = 576, Dv = 512, 1 <= k <= 2048, max_kv <= 2^21.
  * Workspace (required when T > 0): dsa_workspace_size(DSA_WS_SPARSE_MLA_BWD,
- * ...), 2 * T * ceil(k/32)*32 * H * 2 bytes + T * H * 4. */
+ * ...), 2 * T * ceil(k/32)*32 * H * 2 bytes. */
 dsa_status dsa_sparse_mla_bwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                               int k, int H, int D, int Dv, float scale, const uint16_t *out, const float *lse,
                               const uint16_t *dout, float *dq, float *dkv, void *ws, size_t ws_bytes,

@@ -85,12 +85,9 @@ size_t kl_ws(const dsa_batch *b, int k) {
 }
 
 // Backward workspace: P and scale * dZ per (row, slot, head) in bf16, with
-// k rounded up to whole 32-slot blocks, then delta per (row, head).
+// k rounded up to whole 32-slot blocks.
 int bwd_kpad(int k) { return (k + 31) / 32 * 32; }
-size_t bwd_ws(const dsa_batch *b, int k) {
-    const size_t z = up((size_t)b->total_q * bwd_kpad(k) * kH * 2);
-    return 2 * z + up((size_t)b->total_q * kH * 4);
-}
+size_t bwd_ws(const dsa_batch *b, int k) { return 2 * up((size_t)b->total_q * bwd_kpad(k) * kH * 2); }
 
 int64_t score_ld(int max_kv) { return ((int64_t)max_kv + 63) / 64 * 64; }
 
@@ -430,7 +427,6 @@ dsa_status dsa_sparse_mla_bwd(const dsa_batch *batch, const uint16_t *q, const u
     const size_t z = up((size_t)batch->total_q * p.kpad * kH * 2);
     p.ps = reinterpret_cast<uint16_t *>(w);
     p.dzs = w ? reinterpret_cast<uint16_t *>(w + z) : nullptr;
-    p.delta = w ? reinterpret_cast<float *>(w + 2 * z) : nullptr;
     return hip_status(launch_sparse_mla_bwd(p, batch->total_q, static_cast<hipStream_t>(stream)));
 }
 

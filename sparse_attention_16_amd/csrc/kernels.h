@@ -105,7 +105,6 @@ struct BwdParams {
     float *dkv;             // [N, 576] out (zeroed, then accumulated)
     uint16_t *ps;           // [T, kpad, 128] bf16 workspace: P
     uint16_t *dzs;          // [T, kpad, 128] bf16 workspace: scale * dZ
-    float *delta;           // [T, 128] workspace
 };
 
 constexpr int TOPK_CHUNK = 32768;     // columns selected per workgroup in LDS

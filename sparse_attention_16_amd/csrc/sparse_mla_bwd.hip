@@ -12,12 +12,12 @@
 //   dq[t,h,:]    = sum_j dZs[h,j] kv[s_j,:]
 //   dkv[s_j,:]  += sum_h dZs[h,j] q[t,h,:]   +   [sum_h P[h,j] dout[t,h,:], 0 .. 0]
 // Four launches, each one workgroup per query row (the longest rows first):
-//   bwd_prep: delta per (row, head); dkv zeroed;
-//   bwd_dz:   the logits and dP on the bf16 MFMA (each 32-slot block of rows
-//             gathered into LDS with direct-to-LDS loads, the forward's
-//             layout; q and dout rows in VGPRs), P and dZs rounded to bf16
-//             into a workspace [row][slot][head] (bf16 is also what the
-//             products below take as MFMA operands);
+//   bwd_zero: dkv zeroed;
+//   bwd_dz:   delta per head, then the logits and dP on the bf16 MFMA (each
+//             32-slot block of rows gathered into LDS with direct-to-LDS
+//             loads, the forward's layout; q and dout rows in VGPRs), P and
+//             dZs rounded to bf16 into a workspace [row][slot][head] (bf16 is
+//             also what the products below take as MFMA operands);
 //   bwd_dq:   dq^T = K^T dZs^T: both operands through LDS transpose reads,
 //             the accumulators (a wave's dims x all heads) in registers;
 //   bwd_dkv:  per block [dZs^T | P^T] [q | dout] over the 128 heads, with the
@@ -131,24 +131,6 @@ __device__ __forceinline__ int kt_off(int kr, int d0) {
 
 }  // namespace
 
-// delta[t, h] = <dout[t,h,:], out[t,h,:]>; two threads per head.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
-    const int t = blockIdx.x;
-    const int h = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const uint16_t *g = p.dout + ((int64_t)t * H + h) * DV + 256 * half;
-    const uint16_t *o = p.out + ((int64_t)t * H + h) * DV + 256 * half;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < 256; c += 8) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(g + c);
-        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(o + c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
-    }
-    acc += __shfl_xor(acc, 1, kWave);
-    if (half == 0) p.delta[(int64_t)t * H + h] = acc;
-}
-
 __global__ __launch_bounds__(256) void bwd_zero_kernel(float4 *x, int64_t n4) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
         x[i] = float4{0.f, 0.f, 0.f, 0.f};
@@ -180,7 +162,20 @@ __global__ __launch_bounds__(NT) void bwd_dz_kernel(BwdParams p) {
     }
     const float ls = p.lse[(int64_t)t * H + h];
     const float lse2 = ls > -INFINITY && ls < INFINITY ? ls * LOG2E : INFINITY;   // no finite lse: P = 0
-    const float dl = p.delta[(int64_t)t * H + h];
+    // delta = <dout, out> of the lane's head: its 128 of the 512 dims (the
+    // same chunks as its dout operands), then the sum over the 4 lane groups
+    float dl = 0.f;
+    {
+        const uint16_t *orow = p.out + ((int64_t)t * H + h) * DV + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks) {
+            const bf16x8 o8 = *reinterpret_cast<const bf16x8 *>(orow + 32 * ks);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dl = fmaf((float)gb[ks][e], (float)o8[e], dl);
+        }
+        dl += shfl_xor_f(dl, 16);
+        dl += shfl_xor_f(dl, 32);
+    }
     const uint64_t kvb = seq_base(p.kv, ri.kv0);
 
     const int rr = row16 & 7;
@@ -455,7 +450,6 @@ hipError_t launch_sparse_mla_bwd(const BwdParams &p, int T, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3(T), dim3(256), 0, s, p);
     hipLaunchKernelGGL(bwd_dz_kernel, dim3(T), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(bwd_dq_kernel, dim3(T), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(bwd_dkv_kernel, dim3(T), dim3(NT), 0, s, p);
