@@ -51,20 +51,20 @@ SEED_SHORT = 0xD5A7        # seed of the short-prompt (2048-token) prefill
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     ("prefill_32k", "sparse_mla_kernel"): {
-        "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "1c84730cb82ad104", "fetch_kib": 11618602, "write_kib": 4352330},
+        "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
+        "sha256_16": "4d8eb309aa9735ae", "fetch_kib": 11618602, "write_kib": 4352330},
     ("short_prefill_2k", "sparse_mla_kernel"): {
-        "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "1c84730cb82ad104", "fetch_kib": 192978, "write_kib": 272097},
+        "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
+        "sha256_16": "4d8eb309aa9735ae", "fetch_kib": 192978, "write_kib": 272097},
     ("decode_64k", "indexer_decode_kernel"): {
-        "sources": ("indexer.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "203ed68eb27b3dc4", "fetch_kib": 289241, "write_kib": 17469},
+        "sources": ("indexer.hip", "dsa_device.h", "kernels.h"),
+        "sha256_16": "d700ff06de14d768", "fetch_kib": 289241, "write_kib": 17469},
     ("indexer_kl_32k", "indexer_kl_kernel"): {
-        "sources": ("indexer_kl.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "056372b83dc6dfa0", "fetch_kib": 18370464, "write_kib": 1340},
+        "sources": ("indexer_kl.hip", "dsa_device.h", "kernels.h"),
+        "sha256_16": "7e04a3d781a597b9", "fetch_kib": 18370464, "write_kib": 1340},
     ("quant_append_32k", "quant_groups_kernel<8192,256>"): {
-        "sources": ("quant.hip", "dsa_device.h", "kernels.h", "api.hip"),
-        "sha256_16": "de88c3e3a58f257f", "fetch_kib": 524451, "write_kib": 270336},
+        "sources": ("quant.hip", "dsa_device.h", "kernels.h"),
+        "sha256_16": "a6da93774139246b", "fetch_kib": 524451, "write_kib": 270336},
 }
 
 def measured_traffic(workload, kernel):
