@@ -172,14 +172,17 @@ dsa_status dsa_indexer_kl_fwd(const dsa_batch *batch, const uint16_t *q, const u
  * summed over every row and slot that selects a cache row (a position listed
  * twice counts twice).  out and lse are the forward's outputs for the same
  * inputs.  P and dZ are rounded to bf16 before the products that consume them
- * (the usual precision of attention backward passes); accumulation in fp32.
+ * (the usual precision of attention backward passes), and so is each slot's
+ * dkv contribution before it is summed per cache row; accumulation in fp32.
  *   q [T,H,D] bf16, kv [N,D] bf16, idx [T,k] int32, out [T,H,Dv] bf16,
  *   lse [T,H] fp32, dout [T,H,Dv] bf16
- *   dq [T,H,D] fp32 out (overwritten); dkv [N,D] fp32 out (overwritten: zeroed,
- *   then accumulated with atomics, so its low bits vary from call to call).
+ *   dq [T,H,D] fp32 out (overwritten); dkv [N,D] fp32 out (overwritten; the
+ *   order in which a cache row's contributions are added varies from call to
+ *   call, and so do its low bits).
  * Supported: H = 128, D = 576, Dv = 512, 1 <= k <= 2048, max_kv <= 2^21.
  * Workspace (required when T > 0): dsa_workspace_size(DSA_WS_SPARSE_MLA_BWD,
- * ...), 2 * T * ceil(k/32)*32 * H * 2 bytes. */
+ * ...): the rows are processed in chunks of 4096, and the workspace holds one
+ * chunk (about 1.7 KB per (row, slot) plus 8 bytes per cache row). */
 dsa_status dsa_sparse_mla_bwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                               int k, int H, int D, int Dv, float scale, const uint16_t *out, const float *lse,
                               const uint16_t *dout, float *dq, float *dkv, void *ws, size_t ws_bytes,

@@ -84,10 +84,31 @@ size_t kl_ws(const dsa_batch *b, int k) {
     return up((size_t)b->total_q * s * 5 * 4);
 }
 
-// Backward workspace: P and scale * dZ per (row, slot, head) in bf16, with
-// k rounded up to whole 32-slot blocks.
+// Backward workspace, for one chunk of at most BWD_CHUNK query rows (k
+// rounded up to whole 32-slot blocks): P and scale * dZ per (row, slot, head)
+// in bf16, each slot's 576 sums in bf16, the slot list by cache row, and the
+// counting-sort arrays over the N cache rows.
 int bwd_kpad(int k) { return (k + 31) / 32 * 32; }
-size_t bwd_ws(const dsa_batch *b, int k) { return 2 * up((size_t)b->total_q * bwd_kpad(k) * kH * 2); }
+struct BwdWs {
+    size_t ps, dzs, g, list, cnt, cur, bsum, total;
+};
+BwdWs bwd_layout(const dsa_batch *b, int k) {
+    const size_t tc = (size_t)(b->total_q < BWD_CHUNK ? b->total_q : BWD_CHUNK);
+    const size_t slots = tc * bwd_kpad(k);
+    const size_t n = (size_t)b->total_kv;
+    const size_t nb = (n + 1 + 1023) / 1024;
+    BwdWs w;
+    w.ps = 0;
+    w.dzs = w.ps + up(slots * kH * 2);
+    w.g = w.dzs + up(slots * kH * 2);
+    w.list = w.g + up(slots * kD * 2);
+    w.cnt = w.list + up(slots * 4);
+    w.cur = w.cnt + up((n + 1) * 4);
+    w.bsum = w.cur + up((n + 1) * 4);
+    w.total = w.bsum + up((nb + 1) * 4);
+    return w;
+}
+size_t bwd_ws(const dsa_batch *b, int k) { return b->total_q > 0 ? bwd_layout(b, k).total : 0; }
 
 int64_t score_ld(int max_kv) { return ((int64_t)max_kv + 63) / 64 * 64; }
 
@@ -424,9 +445,16 @@ dsa_status dsa_sparse_mla_bwd(const dsa_batch *batch, const uint16_t *q, const u
     p.dq = dq;
     p.dkv = dkv;
     char *w = static_cast<char *>(ws);
-    const size_t z = up((size_t)batch->total_q * p.kpad * kH * 2);
-    p.ps = reinterpret_cast<uint16_t *>(w);
-    p.dzs = w ? reinterpret_cast<uint16_t *>(w + z) : nullptr;
+    const BwdWs lay = bwd_layout(batch, k);
+    p.t0 = 0;
+    p.tc = 0;
+    p.ps = w ? reinterpret_cast<uint16_t *>(w + lay.ps) : nullptr;
+    p.dzs = w ? reinterpret_cast<uint16_t *>(w + lay.dzs) : nullptr;
+    p.g = w ? reinterpret_cast<uint16_t *>(w + lay.g) : nullptr;
+    p.list = w ? reinterpret_cast<int32_t *>(w + lay.list) : nullptr;
+    p.cnt = w ? reinterpret_cast<int32_t *>(w + lay.cnt) : nullptr;
+    p.cur = w ? reinterpret_cast<int32_t *>(w + lay.cur) : nullptr;
+    p.bsum = w ? reinterpret_cast<int32_t *>(w + lay.bsum) : nullptr;
     return hip_status(launch_sparse_mla_bwd(p, batch->total_q, static_cast<hipStream_t>(stream)));
 }
 

@@ -103,9 +103,18 @@ struct BwdParams {
     const uint16_t *dout;   // [T, 128, 512] bf16 gradient of out
     float *dq;              // [T, 128, 576] out
     float *dkv;             // [N, 576] out (zeroed, then accumulated)
-    uint16_t *ps;           // [T, kpad, 128] bf16 workspace: P
-    uint16_t *dzs;          // [T, kpad, 128] bf16 workspace: scale * dZ
+    int t0, tc;             // the chunk of query rows [t0, t0 + tc) a launch works on
+    // workspace of one chunk (row t at t - t0)
+    uint16_t *ps;           // [tc, kpad, 128] bf16: P
+    uint16_t *dzs;          // [tc, kpad, 128] bf16: scale * dZ
+    uint16_t *g;            // [tc, kpad, 576] bf16: each slot's sum over heads (its dkv contribution)
+    int32_t *cnt;           // [N + 1] slots per cache row, then their exclusive prefix
+    int32_t *cur;           // [N] fill cursors
+    int32_t *list;          // [tc * kpad] the chunk's usable slots ((t - t0) * kpad + j), by cache row
+    int32_t *bsum;          // [scan blocks + 1] scan block totals
 };
+
+constexpr int BWD_CHUNK = 4096;       // query rows per pass of the backward
 
 constexpr int TOPK_CHUNK = 32768;     // columns selected per workgroup in LDS
 constexpr int TOPK_MAX_CHUNKS = 8;    // merge capacity: 8 x 2048 candidates

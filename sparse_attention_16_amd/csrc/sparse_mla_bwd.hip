@@ -11,8 +11,9 @@
 //   dZs[h,j] = scale P[h,j] (dP[h,j] - delta[h])      (the softmax's backward, scaled)
 //   dq[t,h,:]    = sum_j dZs[h,j] kv[s_j,:]
 //   dkv[s_j,:]  += sum_h dZs[h,j] q[t,h,:]   +   [sum_h P[h,j] dout[t,h,:], 0 .. 0]
-// Four launches, each one workgroup per query row (the longest rows first):
-//   bwd_zero: dkv zeroed;
+// In chunks of query rows (the workspace holds one chunk), each kernel one
+// workgroup per row (the longest rows first):
+//   bwd_zero: dkv zeroed (once);
 //   bwd_dz:   delta per head, then the logits and dP on the bf16 MFMA (each
 //             32-slot block of rows gathered into LDS with direct-to-LDS
 //             loads, the forward's layout; q and dout rows in VGPRs), P and
@@ -20,9 +21,15 @@
 //             also what the products below take as MFMA operands);
 //   bwd_dq:   dq^T = K^T dZs^T: both operands through LDS transpose reads,
 //             the accumulators (a wave's dims x all heads) in registers;
-//   bwd_dkv:  per block [dZs^T | P^T] [q | dout] over the 128 heads, with the
-//             row's q and dout resident in VGPRs in head-contraction layout,
-//             added to dkv with fp32 atomics.
+//   bwd_g:    per block [dZs^T | P^T] [q | dout] over the 128 heads, with the
+//             row's q and dout resident in VGPRs in head-contraction layout:
+//             each slot's 576 sums, rounded to bf16 into a workspace;
+//   bwd_count, bwd_scan_*, bwd_scatter: the chunk's usable slots sorted by
+//             cache row (counting sort);
+//   bwd_reduce: per cache row, its listed sums added in fp32 into dkv.
+// (fp32 atomic adds of every slot's sums into dkv were bound by the atomic
+// rate: 3.75e10 adds at 32K take 113 ms; this route moves 2 x 1152 bytes
+// per slot through memory instead.)
 #include "dsa_device.h"
 #include "kernels.h"
 
@@ -45,6 +52,7 @@ constexpr int ZBUF = BK * ZP;             // 8 KB per P / dZs block
 constexpr int MAX_SEL = 2048;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int AHEAD = 3;                  // k-steps of K operands read ahead in bwd_dz
+constexpr int GTP = D + 8;                // pitch (in bf16) of a slot row of bwd_g's LDS tile
 
 typedef DSA_LDS uint8_t lds_u8;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
@@ -106,6 +114,13 @@ __device__ __forceinline__ void gather8(const DSA_LDS int32_t *sel, int blk, int
     }
 }
 
+// A device address made wave-uniform (scalar) for dma16s.
+__device__ __forceinline__ uint64_t uniform_base(const void *ptr) {
+    const uint64_t v = (uint64_t)(uintptr_t)ptr;
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+           (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+}
+
 // One 8 KB block [32 slots][128 heads] of a workspace array into LDS (wave w:
 // slots 4w .. 4w+3, one 1 KB load).
 __device__ __forceinline__ void load_zblock(const uint16_t *src, int wave, int l, lds_u8 *buf) {
@@ -143,7 +158,7 @@ __global__ __launch_bounds__(NT) void bwd_dz_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
     __shared__ __attribute__((aligned(16))) uint16_t tz[NW][2][BK * 16];   // per wave: P, dZs of a block
 
-    const int t = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int t = p.t0 + p.tc - 1 - (int)blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
     const int row16 = l & 15, grp = l >> 4;
     const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
@@ -188,8 +203,8 @@ __global__ __launch_bounds__(NT) void bwd_dz_kernel(BwdParams p) {
     };
     DSA_LDS uint16_t *tp = (DSA_LDS uint16_t *)tz[wave][0];
     DSA_LDS uint16_t *tzd = (DSA_LDS uint16_t *)tz[wave][1];
-    uint16_t *ps_row = p.ps + (int64_t)t * p.kpad * H;
-    uint16_t *dz_row = p.dzs + (int64_t)t * p.kpad * H;
+    uint16_t *ps_row = p.ps + (int64_t)(t - p.t0) * p.kpad * H;
+    uint16_t *dz_row = p.dzs + (int64_t)(t - p.t0) * p.kpad * H;
 
     __syncthreads();   // the slot positions
     if (nblk > 0) gather8((const DSA_LDS int32_t *)sel, 0, wave, l, kvb, (lds_u8 *)kb[0]);
@@ -262,7 +277,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t zb[2][ZBUF];
     __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
 
-    const int t = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int t = p.t0 + p.tc - 1 - (int)blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
     const int row16 = l & 15, grp = l >> 4;
     const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
@@ -270,7 +285,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdParams p) {
     const int nblk = sl.nblk;
     const int nct = wave < 4 ? 5 : 4;
     const uint64_t kvb = seq_base(p.kv, ri.kv0);
-    const uint16_t *dz_row = p.dzs + (int64_t)t * p.kpad * H;
+    const uint16_t *dz_row = p.dzs + (int64_t)(t - p.t0) * p.kpad * H;
 
     // transpose-read addressing: lane row16 of a 16-lane group points at row
     // (4*grp + row16/4) [+16 for the second half], 4 columns 4*(row16%4) ..
@@ -329,16 +344,20 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdParams p) {
             }
 }
 
-// dkv rows of a row's selected slots: per block, D[32 slots x dims] =
-// dZs^T[32 x 128 heads] q[128 x dims] (+ P^T dout on the value dims).
-// Wave w owns latent dim tiles 4w .. 4w+3 and, for w < 4, rope tile w; the
-// row's q and dout for those dims stay in VGPRs as MFMA B operands.
-__global__ __launch_bounds__(NT) void bwd_dkv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t zb[2][ZBUF];
-    __shared__ __attribute__((aligned(1024))) uint8_t pb[2][ZBUF];
+// Each usable slot's dkv contribution, summed over the heads: per block,
+// D[32 slots x dims] = dZs^T[32 x 128 heads] q[128 x dims] (+ P^T dout on the
+// value dims), rounded to bf16 into g[(t - t0) * kpad + slot][576].  Wave w
+// owns latent dim tiles 4w .. 4w+3 and, for w < 4, rope tile w; the row's q
+// and dout for those dims stay in VGPRs as MFMA B operands.
+__global__ __launch_bounds__(NT) void bwd_g_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t zb[3][ZBUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t pb[3][ZBUF];
     __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
+    // two blocks' sums, [32 slots][576 dims] at a 1168-byte pitch (the 4 slots
+    // a wave writes at once then fall in distinct banks)
+    __shared__ __attribute__((aligned(16))) uint16_t gt[2][BK * GTP];
 
-    const int t = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int t = p.t0 + p.tc - 1 - (int)blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
     const int row16 = l & 15, grp = l >> 4;
     const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
@@ -346,74 +365,79 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(BwdParams p) {
     const int nblk = sl.nblk;
     const int nct = wave < 4 ? 5 : 4;
     auto dim_tile = [&](int i) { return i < 4 ? 4 * wave + i : 32 + wave; };
-    const uint16_t *dz_row = p.dzs + (int64_t)t * p.kpad * H;
-    const uint16_t *ps_row = p.ps + (int64_t)t * p.kpad * H;
-    float *dkv0 = p.dkv + ri.kv0 * D;
+    const int64_t lrow = (int64_t)(t - p.t0) * p.kpad;
+    const uint16_t *dz_row = p.dzs + lrow * H;
+    const uint16_t *ps_row = p.ps + lrow * H;
 
     // B operands: lane (dim row16 of a tile, group grp) holds heads
-    // 32*ks + 8*grp .. +7 at that dim.  Each pair of heads is packed into one
-    // word as it arrives (the empty asm keeps the packing here: left alone,
-    // the compiler keeps the 16-bit halves apart and packs them inside the
-    // block loop, spilling them in between).
-    auto gather8h = [&](const uint16_t *src, int64_t stride) {
-        i32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint32_t v = (uint32_t)src[(int64_t)(2 * e) * stride] | ((uint32_t)src[(int64_t)(2 * e + 1) * stride] << 16);
-            asm volatile("" : "+v"(v));
-            w[e] = (int)v;
-        }
-        return __builtin_bit_cast(bf16x8, w);
-    };
+    // 32*ks + 8*grp .. +7 at that dim.  Per k-step, the 32 q rows (36 KB) and
+    // 32 dout rows (32 KB) of those heads are copied contiguously into the
+    // (not yet used) tile buffers with 1 KB direct-to-LDS loads, and the
+    // operands read back with transpose reads (rows = heads, columns = dims:
+    // lane row16 gets 4 heads of its dim per read).
     bf16x8 qb[4][5], gb[4][4];
+    {
+        lds_u8 *stage = (lds_u8 *)gt;
+        constexpr int QB = 32 * D * 2, GB = 32 * DV * 2;   // 36864, 32768 bytes
+        static_assert(QB + GB <= (int)sizeof(gt), "staging fits the tile buffers");
+        const uint64_t qbase = uniform_base(p.q + (int64_t)t * H * D);
+        const uint64_t gbase = uniform_base(p.dout + (int64_t)t * H * DV);
+        const int hr = 8 * grp + (row16 >> 2), dc = 4 * (row16 & 3);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 4; ++ks) {   // (unrolled: qb[ks] and gb[ks] must stay registers)
+            for (int c = wave; c < QB / 1024; c += NW)
+                dma16s(qbase + (uint64_t)ks * QB + 1024u * c, 16u * (uint32_t)l, stage + 1024 * c);
+            for (int c = wave; c < GB / 1024; c += NW)
+                dma16s(gbase + (uint64_t)ks * GB + 1024u * c, 16u * (uint32_t)l, stage + QB + 1024 * c);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            lds_barrier();
 #pragma unroll
-        for (int i = 0; i < 5; ++i)
-            if (i < nct)
-                qb[ks][i] = gather8h(p.q + ((int64_t)t * H + 32 * ks + 8 * grp) * D + 16 * dim_tile(i) + row16, D);
+            for (int i = 0; i < 5; ++i)
+                if (i < nct) {
+                    const lds_u8 *a = stage + hr * (2 * D) + 2 * (16 * dim_tile(i) + dc);
+                    qb[ks][i] = tr_pair(a, a + 4 * (2 * D));
+                }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            gb[ks][i] = gather8h(p.dout + ((int64_t)t * H + 32 * ks + 8 * grp) * DV + 16 * dim_tile(i) + row16, DV);
+            for (int i = 0; i < 4; ++i) {
+                const lds_u8 *a = stage + QB + hr * (2 * DV) + 2 * (16 * dim_tile(i) + dc);
+                gb[ks][i] = tr_pair(a, a + 4 * (2 * DV));
+            }
+            lds_barrier();   // (the next k-step's loads overwrite the stage)
+        }
     }
 
-    f32x4 acc[2][5];
-    // adds block b's results to dkv (slots whose position is -1 are skipped)
-    auto scatter = [&](int b) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int pos = sel[b * BK + 16 * mt + 4 * grp + r];
-                if (pos >= 0) {
-                    float *dst = dkv0 + (int64_t)pos * D + row16;
-#pragma unroll
-                    for (int i = 0; i < 5; ++i)
-                        if (i < nct) atomicAdd(dst + 16 * dim_tile(i), acc[mt][i][r]);
-                }
-            }
+    // block b's 32 g rows (contiguous in g) from the LDS tile, 16-byte pieces
+    auto copy_out = [&](int b) {
+        const DSA_LDS uint16_t *tile = (const DSA_LDS uint16_t *)gt[b & 1];
+        uint16_t *grow = p.g + (lrow + (int64_t)b * BK) * D;
+        for (int c = threadIdx.x; c < BK * D / 8; c += NT) {
+            const int r = c / (D / 8), o = c % (D / 8);
+            *reinterpret_cast<bf16x8 *>(grow + 8 * c) = *reinterpret_cast<const DSA_LDS bf16x8 *>(tile + r * GTP + 8 * o);
+        }
     };
 
+    // Operand blocks are loaded two blocks ahead into three buffers.  The wait
+    // at the end of step b is for block b+1's loads: issued in step b-1, they
+    // were followed only by step b-1's copy-out stores (5 per wave for waves
+    // 0..3, 4 for waves 4..7) and block b+2's two loads; vector memory
+    // operations of a wave complete in issue order.
+    auto load_ops = [&](int blk) {
+        load_zblock(dz_row + (int64_t)blk * BK * H, wave, l, (lds_u8 *)zb[blk % 3]);
+        load_zblock(ps_row + (int64_t)blk * BK * H, wave, l, (lds_u8 *)pb[blk % 3]);
+    };
     __syncthreads();
-    if (nblk > 0) {
-        load_zblock(dz_row, wave, l, (lds_u8 *)zb[0]);
-        load_zblock(ps_row, wave, l, (lds_u8 *)pb[0]);
-    }
+    if (nblk > 0) load_ops(0);
+    if (nblk > 1) load_ops(1);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
 
     for (int b = 0; b < nblk; ++b) {
-        const int cur = b & 1;
-        // the previous block's sums go out first (their atomics complete under
-        // this block's products), then this block's loads of the next one
-        if (b > 0) scatter(b - 1);
-        __builtin_amdgcn_sched_barrier(0);   // (the sums leave their registers before the next block's)
-        if (b + 1 < nblk) {
-            load_zblock(dz_row + (int64_t)(b + 1) * BK * H, wave, l, (lds_u8 *)zb[cur ^ 1]);
-            load_zblock(ps_row + (int64_t)(b + 1) * BK * H, wave, l, (lds_u8 *)pb[cur ^ 1]);
-        }
+        const int cur = b % 3;
+        const bool ld2 = b + 2 < nblk;
+        if (ld2) load_ops(b + 2);
         const lds_u8 *zbuf = (const lds_u8 *)zb[cur];
         const lds_u8 *pbuf = (const lds_u8 *)pb[cur];
+        f32x4 acc[2][5];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -434,26 +458,195 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(BwdParams p) {
             }
             __builtin_amdgcn_sched_barrier(0);   // (keeps the operand reads from all moving up front)
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        lds_barrier();
+        // lane holds slots 16*mt + 4*grp + r of dim 16*tile + row16: into the tile
+        DSA_LDS uint16_t *tile = (DSA_LDS uint16_t *)gt[b & 1];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int i = 0; i < 5; ++i)
+                    if (i < nct)
+                        tile[(16 * mt + 4 * grp + r) * GTP + 16 * dim_tile(i) + row16] =
+                            __builtin_bit_cast(uint16_t, (__bf16)acc[mt][i][r]);
+        // block b+1's loads (see above); step 0's were waited for in the prologue
+        if (b > 0 && b + 1 < nblk) {
+            if (wave < 4) {
+                if (ld2)
+                    __builtin_amdgcn_s_waitcnt(0x0F77);   // vmcnt(7) = 5 stores + 2 loads
+                else
+                    __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
+            } else {
+                if (ld2)
+                    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6) = 4 stores + 2 loads
+                else
+                    __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+            }
+        }
+        lds_barrier();   // publishes block b's tile and block b+1's operands
+        copy_out(b);     // (its stores complete under the next block's products)
     }
-    if (nblk > 0) scatter(nblk - 1);
 }
 
-hipError_t launch_sparse_mla_bwd(const BwdParams &p, int T, hipStream_t s) {
-    const int64_t n4 = p.total_kv * D / 4;
+// Slots per cache row over the chunk's usable slots (one workgroup per row).
+__global__ __launch_bounds__(256) void bwd_count_kernel(BwdParams p) {
+    const int t = p.t0 + (int)blockIdx.x;
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    const int32_t *idx_row = p.idx + (int64_t)t * p.k;
+    for (int j = threadIdx.x; j < p.k; j += 256) {
+        const int v = idx_row[j];
+        if (v >= 0 && v < ri.ctx) atomicAdd(p.cnt + ri.kv0 + v, 1);
+    }
+}
+
+// Exclusive prefix of cnt[0 .. n) in place, in three launches: per 1024
+// elements (256 threads x 4), the block totals, then their prefixes added.
+__global__ __launch_bounds__(256) void bwd_scan_blocks_kernel(int32_t *x, int64_t n, int32_t *bsum) {
+    __shared__ int32_t wsum[4];
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    int32_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = i0 + e < n ? x[i0 + e] : 0;
+    const int32_t s = v[0] + v[1] + v[2] + v[3];
+    int32_t inc = s;
+    const int l = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t o = __shfl_up(inc, d, kWave);
+        if (l >= d) inc += o;
+    }
+    if (l == kWave - 1) wsum[w] = inc;
+    __syncthreads();
+    int32_t base = 0;
+    for (int u = 0; u < w; ++u) base += wsum[u];
+    int32_t e = base + inc - s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (i0 + k < n) x[i0 + k] = e;
+        e += v[k];
+    }
+    if (threadIdx.x == 255) bsum[blockIdx.x] = base + inc;
+}
+
+__global__ __launch_bounds__(1024) void bwd_scan_totals_kernel(int32_t *bsum, int nb) {
+    __shared__ int32_t wsum[16];
+    __shared__ int32_t carry;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    const int l = lane_id(), w = threadIdx.x >> 6;
+    for (int c0 = 0; c0 < nb; c0 += 1024) {
+        const int i = c0 + (int)threadIdx.x;
+        const int32_t s = i < nb ? bsum[i] : 0;
+        int32_t inc = s;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int32_t o = __shfl_up(inc, d, kWave);
+            if (l >= d) inc += o;
+        }
+        if (l == kWave - 1) wsum[w] = inc;
+        __syncthreads();
+        int32_t base = carry;
+        for (int u = 0; u < w; ++u) base += wsum[u];
+        if (i < nb) bsum[i] = base + inc - s;
+        __syncthreads();
+        if (threadIdx.x == 1023) carry = base + inc;
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void bwd_scan_add_kernel(int32_t *x, int64_t n, const int32_t *bsum, int32_t *cur,
+                                                          int64_t ncur) {
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int32_t add = bsum[blockIdx.x];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (i0 + e < n) {
+            const int32_t v = x[i0 + e] + add;
+            x[i0 + e] = v;
+            if (i0 + e < ncur) cur[i0 + e] = v;
+        }
+}
+
+// The chunk's usable slots listed by cache row (order within a row is the
+// order the atomics land in).
+__global__ __launch_bounds__(256) void bwd_scatter_kernel(BwdParams p) {
+    const int t = p.t0 + (int)blockIdx.x;
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    const int32_t *idx_row = p.idx + (int64_t)t * p.k;
+    for (int j = threadIdx.x; j < p.k; j += 256) {
+        const int v = idx_row[j];
+        if (v >= 0 && v < ri.ctx) {
+            const int32_t at = atomicAdd(p.cur + ri.kv0 + v, 1);
+            p.list[at] = (int32_t)blockIdx.x * p.kpad + j;
+        }
+    }
+}
+
+// dkv[s, :] += the chunk's listed contributions to cache row s, summed in
+// fp32 (one workgroup per cache row; threads 0..71 own 8 dims each).
+__global__ __launch_bounds__(128) void bwd_reduce_kernel(BwdParams p) {
+    const int64_t s = blockIdx.x;
+    const int32_t beg = p.cnt[s], end = p.cnt[s + 1];
+    if (beg == end || threadIdx.x >= D / 8) return;
+    const int d0 = 8 * (int)threadIdx.x;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int32_t i = beg;
+    for (; i + 4 <= end; i += 4) {
+        bf16x8 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = *reinterpret_cast<const bf16x8 *>(p.g + (int64_t)p.list[i + u] * D + d0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e];
+    }
+    for (; i < end; ++i) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p.g + (int64_t)p.list[i] * D + d0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+    }
+    f32x4 *o = reinterpret_cast<f32x4 *>(p.dkv + s * D + d0);
+    o[0] += f32x4{acc[0], acc[1], acc[2], acc[3]};
+    o[1] += f32x4{acc[4], acc[5], acc[6], acc[7]};
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_i32_kernel(int32_t *x, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) x[i] = 0;
+}
+
+hipError_t launch_sparse_mla_bwd(const BwdParams &p0, int T, hipStream_t s) {
+    const int64_t N = p0.total_kv;
+    const int64_t n4 = N * D / 4;
+    auto grid_for = [](int64_t n) { const int64_t g = (n + 255) / 256; return (unsigned)(g < 4096 ? g : 4096); };
     if (n4 > 0) {
-        const int64_t want = (n4 + 255) / 256;
-        const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
-        hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<float4 *>(p.dkv), n4);
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid_for(n4)), dim3(256), 0, s, reinterpret_cast<float4 *>(p0.dkv),
+                           n4);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_dz_kernel, dim3(T), dim3(NT), 0, s, p);
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(T), dim3(NT), 0, s, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel, dim3(T), dim3(NT), 0, s, p);
-    return hipGetLastError();
+    const int64_t nscan = N + 1;                          // the last entry becomes the total
+    const unsigned nb = (unsigned)((nscan + 1023) / 1024);
+    for (int t0 = 0; t0 < T; t0 += BWD_CHUNK) {
+        BwdParams p = p0;
+        p.t0 = t0;
+        p.tc = T - t0 < BWD_CHUNK ? T - t0 : BWD_CHUNK;
+        hipLaunchKernelGGL(bwd_zero_i32_kernel, dim3(grid_for(nscan)), dim3(256), 0, s, p.cnt, nscan);
+        hipLaunchKernelGGL(bwd_dz_kernel, dim3(p.tc), dim3(NT), 0, s, p);
+        hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.tc), dim3(NT), 0, s, p);
+        hipLaunchKernelGGL(bwd_g_kernel, dim3(p.tc), dim3(NT), 0, s, p);
+        if (N > 0) {
+            hipLaunchKernelGGL(bwd_count_kernel, dim3(p.tc), dim3(256), 0, s, p);
+            hipLaunchKernelGGL(bwd_scan_blocks_kernel, dim3(nb), dim3(256), 0, s, p.cnt, nscan, p.bsum);
+            hipLaunchKernelGGL(bwd_scan_totals_kernel, dim3(1), dim3(1024), 0, s, p.bsum, (int)nb);
+            hipLaunchKernelGGL(bwd_scan_add_kernel, dim3(nb), dim3(256), 0, s, p.cnt, nscan, p.bsum, p.cur, N);
+            hipLaunchKernelGGL(bwd_scatter_kernel, dim3(p.tc), dim3(256), 0, s, p);
+            hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)N), dim3(128), 0, s, p);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace dsa
