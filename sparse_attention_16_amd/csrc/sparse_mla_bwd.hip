@@ -350,8 +350,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdParams p) {
 // owns latent dim tiles 4w .. 4w+3 and, for w < 4, rope tile w; the row's q
 // and dout for those dims stay in VGPRs as MFMA B operands.
 __global__ __launch_bounds__(NT) void bwd_g_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t zb[3][ZBUF];
-    __shared__ __attribute__((aligned(1024))) uint8_t pb[3][ZBUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t zb[2][ZBUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t pb[2][ZBUF];
     __shared__ __attribute__((aligned(16))) int32_t sel[MAX_SEL];
     // two blocks' sums, [32 slots][576 dims] at a 1168-byte pitch (the 4 slots
     // a wave writes at once then fall in distinct banks)
@@ -416,25 +416,19 @@ __global__ __launch_bounds__(NT) void bwd_g_kernel(BwdParams p) {
         }
     };
 
-    // Operand blocks are loaded two blocks ahead into three buffers.  The wait
-    // at the end of step b is for block b+1's loads: issued in step b-1, they
-    // were followed only by step b-1's copy-out stores (5 per wave for waves
-    // 0..3, 4 for waves 4..7) and block b+2's two loads; vector memory
-    // operations of a wave complete in issue order.
+    // Operand blocks are loaded one block ahead into two buffers.
     auto load_ops = [&](int blk) {
-        load_zblock(dz_row + (int64_t)blk * BK * H, wave, l, (lds_u8 *)zb[blk % 3]);
-        load_zblock(ps_row + (int64_t)blk * BK * H, wave, l, (lds_u8 *)pb[blk % 3]);
+        load_zblock(dz_row + (int64_t)blk * BK * H, wave, l, (lds_u8 *)zb[blk & 1]);
+        load_zblock(ps_row + (int64_t)blk * BK * H, wave, l, (lds_u8 *)pb[blk & 1]);
     };
     __syncthreads();
     if (nblk > 0) load_ops(0);
-    if (nblk > 1) load_ops(1);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
 
     for (int b = 0; b < nblk; ++b) {
-        const int cur = b % 3;
-        const bool ld2 = b + 2 < nblk;
-        if (ld2) load_ops(b + 2);
+        const int cur = b & 1;
+        if (b + 1 < nblk) load_ops(b + 1);
         const lds_u8 *zbuf = (const lds_u8 *)zb[cur];
         const lds_u8 *pbuf = (const lds_u8 *)pb[cur];
         f32x4 acc[2][5];
@@ -469,20 +463,9 @@ __global__ __launch_bounds__(NT) void bwd_g_kernel(BwdParams p) {
                     if (i < nct)
                         tile[(16 * mt + 4 * grp + r) * GTP + 16 * dim_tile(i) + row16] =
                             __builtin_bit_cast(uint16_t, (__bf16)acc[mt][i][r]);
-        // block b+1's loads (see above); step 0's were waited for in the prologue
-        if (b > 0 && b + 1 < nblk) {
-            if (wave < 4) {
-                if (ld2)
-                    __builtin_amdgcn_s_waitcnt(0x0F77);   // vmcnt(7) = 5 stores + 2 loads
-                else
-                    __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
-            } else {
-                if (ld2)
-                    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6) = 4 stores + 2 loads
-                else
-                    __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
-            }
-        }
+        // block b+1's loads, and the previous block's copy-out stores (issued a
+        // whole block ago, so normally done)
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         lds_barrier();   // publishes block b's tile and block b+1's operands
         copy_out(b);     // (its stores complete under the next block's products)
     }
