@@ -62,6 +62,10 @@ COUNTERS = {
     ("indexer_kl_32k", "indexer_kl_kernel"): {
         "sources": ("indexer_kl.hip", "dsa_device.h", "kernels.h"),
         "sha256_16": "7e04a3d781a597b9", "fetch_kib": 18370464, "write_kib": 1340},
+    # the whole backward (its 10 kernels, 8 row chunks), summed per call
+    ("sparse_bwd_32k", "dsa_sparse_mla_bwd"): {
+        "sources": ("sparse_mla_bwd.hip", "dsa_device.h", "kernels.h"),
+        "sha256_16": "b63a5d5b42ec31b1", "fetch_kib": 93422305, "write_kib": 120081451},
     ("quant_append_32k", "quant_groups_kernel<8192,256>"): {
         "sources": ("quant.hip", "dsa_device.h", "kernels.h"),
         "sha256_16": "a6da93774139246b", "fetch_kib": 524451, "write_kib": 270336},
@@ -343,10 +347,15 @@ def bwd_bench(args, dsa):
     torch.cuda.synchronize()
     kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     achieved = flops / (kms * 1e-3) / 1e12
-    roof = {"kernel": "dsa_sparse_mla_bwd (bwd_prep, bwd_dz, bwd_dq, bwd_dkv launches)", "bound": "mfma",
+    roof = {"kernel": "dsa_sparse_mla_bwd (all launches)", "bound": "mfma",
             "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "avg_ms": round(kms, 4),
             "algorithmic_flops": flops}
+    tr = measured_traffic("sparse_bwd_32k", "dsa_sparse_mla_bwd")
+    if tr is not None:
+        roof["traffic"] = round(tr["fetch"] + tr["write"])
+        roof["traffic_unit"] = "bytes/call, all kernels of the backward (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
+        roof["traffic_fetch"], roof["traffic_write"] = round(tr["fetch"]), round(tr["write"])
     say(f"[bench] backward: {kms:.3f} ms/launch, {achieved:.1f} TFLOP/s ({100 * roof['frac']:.1f}% of peak)")
 
     cpu = None
