@@ -8,24 +8,28 @@
 // columns in ascending order, -1 padded.
 //
 // Method (one 512-thread workgroup per row chunk of up to 32768 columns; the
-// chunk's scores stay in registers, 64 per thread, as order-preserving uint32
-// keys):
+// chunk's scores stay in registers as order-preserving uint32 keys, thread t
+// holding the 4G consecutive columns 4Gt .. 4Gt + 4G - 1):
 //   1. range   : block minimum and maximum of the chunk's scores.
 //   2. bin     : a 2048-bin histogram of the scores, binned by value over
 //                [min, max] (a non-decreasing map, so bins keep the order);
 //                a scan from the top names the bin b1 holding the k-th
-//                largest key and how many of its keys are taken.
-//   3. kappa   : the keys of bin b1 (a handful on spread-out scores) are
-//                collected in LDS and each is ranked against the others: the
-//                k-th largest key kappa and the number of keys equal to kappa
-//                to take follow directly.  If the bins cannot be formed or bin
-//                b1 is too full (e.g. many equal scores), three exact radix
-//                passes (11, 11, 10 key bits) over the register keys give
-//                kappa instead.
-//   4. emit    : each thread counts, per 4-column group, its keys > kappa and
-//                == kappa; one block prefix over the groups in column order
-//                gives every selected key its output slot.  The output is
-//                ascending with no sort.
+//                largest key.
+//   3. classify: two key thresholds a quarter bin outside b1, each checked
+//                with the histogram's own bin arithmetic, split the keys:
+//                those above the upper one are selected outright, those
+//                below the lower one are not, and the few in between (b1
+//                and its edges, about 20 keys on spread-out scores) are
+//                collected in LDS and ranked (key descending, then column);
+//                the first k - #outright of them are selected.  Each thread
+//                ends with a bit mask of its selected keys.  If the scores
+//                cannot be binned or too many keys fall in between (e.g.
+//                many equal scores), three exact radix passes (11, 11, 10
+//                key bits) give the k-th key kappa, and the masks take the
+//                keys > kappa plus the first keys == kappa in column order.
+//   4. emit    : one block scan of the masks' popcounts gives every thread
+//                its first output slot; each thread writes only its selected
+//                columns.  The output is ascending with no sort.
 // Rows longer than one chunk: each chunk selects its exact local top-k
 // candidates (key, column) into workspace; a merge workgroup runs the same
 // select over the candidates.  The union of the chunk-local top-k sets
@@ -44,19 +48,18 @@ constexpr int BPT = NBIN / TPB;                            // bins scanned per t
 constexpr int CCAP = TPB;                                  // candidates ranked directly (one per thread)
 constexpr int CH_V4 = TOPK_CHUNK / (4 * TPB);              // 4-key groups per thread, chunk kernel
 constexpr int MG_V4 = TOPK_MAX_CHUNKS * 2048 / (4 * TPB);  // 4-key groups per thread, merge kernel
-constexpr int MAX_V4 = CH_V4 > MG_V4 ? CH_V4 : MG_V4;
 static_assert(NBIN % TPB == 0 && CH_V4 * 4 * TPB == TOPK_CHUNK && MG_V4 * 4 * TPB == TOPK_MAX_CHUNKS * 2048,
               "register layout");
-static_assert(NWAVE * MAX_V4 <= 2 * kWave, "one wave scans the group totals, two per lane");
 
 struct SelectShared {
-    // each array has one spare entry per lane after its end: writes that
-    // must not count go there (a spare per lane, so that they do not collide)
-    uint32_t hist[NBIN + kWave];
-    uint32_t ckey[CCAP + kWave];
-    int32_t ocol[2048 + kWave];      // selected columns by slot
-    uint32_t okey[2048 + kWave];     // their keys
-    uint32_t gsum[MAX_V4 * NWAVE];   // per (group, wave) packed counts, then their prefix
+    union {
+        uint32_t hist[NBIN + kWave];  // histogram, one spare entry per lane after it
+        uint32_t okey[2048];          // selected keys by slot (written once the histogram is done)
+    };
+    uint32_t ckey[CCAP];             // uncertain keys ...
+    uint32_t cpos[CCAP];             // ... and their positions (thread << 6 | register index)
+    uint32_t tbits[TPB][2];          // uncertain keys taken, as bits of their owner's key mask
+    int32_t ocol[2048];              // selected columns by slot
     uint32_t wtot[NWAVE];            // scan and reduction scratch
     uint32_t wmin[NWAVE], wmax[NWAVE];
     uint32_t ncand;
@@ -175,40 +178,60 @@ __device__ __forceinline__ void radix_kappa(uint32_t (&kr)[4 * NV4], int ngroups
     lds_barrier();
 }
 
-// Steps 1-4 over the register keys kr (key 0 = no key; key i of group u sits
-// at column 4 * (u * TPB + tid) + i), at least k + 1 of them real, groups >=
-// ngroups empty.  tz is the thread index, passed in so that a caller's loop
-// can keep the per-key column arithmetic from being hoisted out of it and
-// held in registers.  On return (after a barrier) sh.ocol[slot], slot < k,
-// holds the columns of the k selected keys, slot = rank in column order, and
-// sh.okey[slot] their keys when want_keys.
-template <int NV4>
-__device__ __forceinline__ void select_regs(uint32_t (&kr)[4 * NV4], int ngroups, int k, SelectShared &sh, int tz,
-                                            bool want_keys) {
+// Block sum of one value per thread (every thread gets the total).
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *wtot) {
+    const int l = lane_id(), w = threadIdx.x >> 6;
+    const uint32_t x = wave_scan_add(v);
+    if (l == 63) wtot[w] = x;
+    lds_barrier();
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVE; ++i) s += wtot[i];
+    lds_barrier();
+    return s;
+}
+
+// Steps 1-4 over the register keys kr (key 0 = no key).  Thread tz holds the
+// G * 4 consecutive columns 4 * G * tz + j in kr[j], j < 4 * G (G <= NV4), at
+// least k + 1 of all keys real; lmin / lmax are the thread's smallest nonzero
+// and largest key (0xFFFFFFFF / 0 when it has none).  tz is the thread index,
+// passed in so that a caller's loop can keep the column arithmetic from being
+// hoisted out of it and held in registers.  On return (after a barrier)
+// sh.ocol[slot], slot < k, holds the columns of the k selected keys, slot =
+// rank in column order, and sh.okey[slot] their keys when want_keys.
+//
+// Every thread ends with a mask of its selected keys (bit j = kr[j]):
+//   * keys at or above khi, a key whose value bin is known to lie above the
+//     bin b1 of the k-th largest key, are selected outright;
+//   * keys in [klo, khi), a few bins' worth around b1, are collected in LDS
+//     and ranked (key descending, then column): the first k - #outright are
+//     selected and set their bits in their owner's mask;
+//   * keys below klo are not selected.
+// The masks' popcounts give each thread its first slot (one block scan), and
+// each thread writes only its selected columns.
+template <int NV4, class Hook>
+__device__ __forceinline__ void select_regs(uint32_t (&kr)[4 * NV4], int G, uint32_t lmin, uint32_t lmax, int k,
+                                            SelectShared &sh, int tz, bool want_keys, Hook &&hook) {
+    static_assert(4 * NV4 <= 64, "key masks hold 64 bits");
     const int tid = threadIdx.x, l = lane_id(), w = tid >> 6;
-    launder(kr);
 
     // 1. range (keys order like scores: min/max over keys)
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < 4 * NV4; ++i) {
-        const uint32_t key = kr[i];
-        kmin = key != 0u && key < kmin ? key : kmin;
-        kmax = key > kmax ? key : kmax;
-    }
-    kmin = wave_scan(kmin, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
-    kmax = wave_scan(kmax, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+    uint32_t kmin = wave_scan(lmin, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+    uint32_t kmax = wave_scan(lmax, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
     if (l == 63) {   // the inclusive scan's last lane holds the wave's result
         sh.wmin[w] = kmin;
         sh.wmax[w] = kmax;
     }
     clear_hist(sh);
+    sh.tbits[tid][0] = 0u;
+    sh.tbits[tid][1] = 0u;
     if (tid == 0) {
         sh.ncand = 0;
         sh.prefix = 0;
         sh.rem = (uint32_t)k;
     }
     lds_barrier();
+    hook(2);
 #pragma unroll
     for (int x = 0; x < NWAVE; ++x) {
         kmin = sh.wmin[x] < kmin ? sh.wmin[x] : kmin;
@@ -220,7 +243,8 @@ __device__ __forceinline__ void select_regs(uint32_t (&kr)[4 * NV4], int ngroups
     // value bins need a finite, positive range with a finite scale
     const bool binned = range > 0.f && range < INFINITY && inv < INFINITY;
 
-    bool exact_done = false;
+    uint32_t m0 = 0u, m1 = 0u;   // selected keys: bit j of (m1:m0) = kr[j]
+    bool done = false;
     if (binned) {
         // 2. value histogram, bin b1
         auto bin_of = [&](uint32_t key) {
@@ -230,110 +254,159 @@ __device__ __forceinline__ void select_regs(uint32_t (&kr)[4 * NV4], int ngroups
         launder(kr);
 #pragma unroll
         for (int i = 0; i < 4 * NV4; ++i) {
-            if (i / 4 < ngroups) atomicAdd(&sh.hist[kr[i] != 0u ? bin_of(kr[i]) : NBIN + l], 1u);
+            if (i / 4 < G) atomicAdd(&sh.hist[kr[i] != 0u ? bin_of(kr[i]) : NBIN + l], 1u);
             if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // one 4-key group at a time
         }
         lds_barrier();
-        pick_bin(0, sh);   // prefix = b1, rem = rank inside b1
-        const uint32_t b1 = sh.prefix, rem = sh.rem;
-        // the bins are recomputed below, not kept from the histogram pass
-        // (64 live bin values would not fit in the registers)
+        hook(3);
+        pick_bin(0, sh);   // prefix = b1
+        const uint32_t b1 = sh.prefix;
+        // 3. key thresholds around b1, each checked with the histogram's own
+        // bin arithmetic (bins are non-decreasing in the key): keys >= khi lie
+        // in bins above b1, keys < klo in bins below it.  A quarter bin of
+        // margin; when a check fails the threshold falls back to the range's end.
+        const float bw = range / (float)NBIN;
+        uint32_t klo = kmin, khi = kmax + 1u;
+        if (b1 > 0u) {
+            const uint32_t c = score_key(vmin + ((float)b1 - 0.25f) * bw);
+            if (c > kmin && c <= kmax && bin_of(c - 1u) < b1) klo = c;
+        }
+        if (b1 < (uint32_t)(NBIN - 1)) {
+            const uint32_t c = score_key(vmin + ((float)b1 + 1.25f) * bw);
+            if (c > kmin && c <= kmax && bin_of(c) > b1) khi = c;
+        }
+        const uint32_t span = khi - klo;
+        hook(4);
         launder(kr);
-        float vmin2 = vmin, inv2 = inv;
-        asm volatile("" : "+v"(vmin2), "+v"(inv2));
-        auto bin2_of = [&](uint32_t key) {
-            const float t = (key_value(key) - vmin2) * inv2;
-            return (uint32_t)fminf(t, (float)(NBIN - 1));
-        };
-        // 3. candidates of bin b1, ranked
+        uint32_t nunc = 0;
 #pragma unroll
         for (int i = 0; i < 4 * NV4; ++i) {
-            if (i / 4 >= ngroups) continue;
-            const bool m = kr[i] != 0u && bin2_of(kr[i]) == b1;
-            const uint64_t bal = __ballot(m);
-            if (bal != 0ull) {   // wave-uniform; rare
-                uint32_t base = 0;
-                if (l == 0) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(bal));
-                base = __builtin_amdgcn_readlane(base, 0);
-                const uint32_t pos = base + (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-                sh.ckey[m && pos < CCAP ? pos : CCAP + l] = kr[i];
+            if (i / 4 < G) {
+                const uint32_t key = kr[i];
+                const uint32_t bit = key >= khi ? 1u << (i & 31) : 0u;
+                if (i < 32) m0 |= bit; else m1 |= bit;
+                nunc += key - klo < span ? 1u : 0u;   // (key 0 wraps past span: klo >= 1)
             }
-            if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+        hook(5);
+        // outright count per wave (summed after the barrier below)
+        const uint32_t ns = wave_scan_add((uint32_t)(__builtin_popcount(m0) + __builtin_popcount(m1)));
+        if (l == 63) sh.wtot[w] = ns;
+        if (__ballot(nunc != 0u) != 0ull) {   // a wave holding uncertain keys: one atomic per wave
+            const uint32_t x = wave_scan_add(nunc);
+            uint32_t base = 0;
+            if (l == 63) base = atomicAdd(&sh.ncand, x);
+            uint32_t p = (uint32_t)__builtin_amdgcn_readlane((int)base, 63) + x - nunc;
+            if (nunc != 0u) {
+#pragma unroll
+                for (int i = 0; i < 4 * NV4; ++i) {
+                    if (i / 4 < G) {
+                        const uint32_t key = kr[i];
+                        if (key - klo < span) {
+                            if (p < (uint32_t)CCAP) {
+                                sh.ckey[p] = key;
+                                sh.cpos[p] = ((uint32_t)tz << 6) | (uint32_t)i;
+                            }
+                            ++p;
+                        }
+                    }
+                }
+            }
         }
         lds_barrier();
+        hook(6);
         const uint32_t nc = sh.ncand;
-        if (nc <= CCAP) {
-            if ((uint32_t)tid < nc) {
-                const uint32_t key = sh.ckey[tid];
-                uint32_t gt = 0, eq = 0;
+        uint32_t sure = 0;
+#pragma unroll
+        for (int i = 0; i < NWAVE; ++i) sure += sh.wtot[i];
+        if (nc <= (uint32_t)CCAP) {
+            // sure < k <= sure + nc: the outright keys are all in bins above
+            // b1, and the uncertain ones include every key of b1.  Uncertain
+            // key c is selected when fewer than k - sure uncertain keys come
+            // before it (larger, or equal at a lower column).
+            const uint32_t need = (uint32_t)k - sure;
+            if (nc <= (uint32_t)kWave) {
+                if (w == 0) {   // one wave, the keys in its lanes
+                    const uint32_t key = (uint32_t)l < nc ? sh.ckey[l] : 0u;
+                    const uint32_t pos = (uint32_t)l < nc ? sh.cpos[l] : 0u;
+                    uint32_t before = 0;
+                    for (uint32_t j = 0; j < nc; ++j) {
+                        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)key, (int)j);
+                        const uint32_t op = (uint32_t)__builtin_amdgcn_readlane((int)pos, (int)j);
+                        before += (o > key || (o == key && op < pos)) ? 1u : 0u;
+                    }
+                    if ((uint32_t)l < nc && before < need)
+                        atomicOr(&sh.tbits[pos >> 6][(pos >> 5) & 1u], 1u << (pos & 31u));
+                }
+            } else if ((uint32_t)tid < nc) {
+                const uint32_t key = sh.ckey[tid], pos = sh.cpos[tid];
+                uint32_t before = 0;
                 for (uint32_t j = 0; j < nc; ++j) {
                     const uint32_t o = sh.ckey[j];
-                    gt += o > key ? 1u : 0u;
-                    eq += o == key ? 1u : 0u;
+                    before += (o > key || (o == key && sh.cpos[j] < pos)) ? 1u : 0u;
                 }
-                // every thread holding kappa writes the same two values
-                if (gt < rem && rem <= gt + eq) {
-                    sh.kappa = key;
-                    sh.need_eq = rem - gt;
-                }
+                if (before < need) atomicOr(&sh.tbits[pos >> 6][(pos >> 5) & 1u], 1u << (pos & 31u));
             }
             lds_barrier();
-            exact_done = true;
+            m0 |= sh.tbits[tid][0];
+            m1 |= sh.tbits[tid][1];
+            done = true;
         }
     }
-    if (!exact_done) radix_kappa<NV4>(kr, ngroups, k, sh);
-    const uint32_t kappa = sh.kappa, need_eq = sh.need_eq;
+    if (!done) {
+        // exact kappa by radix passes; then keys > kappa, and the first
+        // need_eq keys == kappa in column order
+        radix_kappa<NV4>(kr, G, k, sh);
+        const uint32_t kappa = sh.kappa, need_eq = sh.need_eq;
+        launder(kr);
+        m0 = m1 = 0u;
+        uint32_t eqc = 0;
+#pragma unroll
+        for (int i = 0; i < 4 * NV4; ++i) {
+            if (i / 4 < G) {
+                const uint32_t bit = kr[i] > kappa ? 1u << (i & 31) : 0u;
+                if (i < 32) m0 |= bit; else m1 |= bit;
+                eqc += kr[i] == kappa ? 1u : 0u;
+            }
+        }
+        const uint32_t eqb = block_excl_scan(eqc, sh.wtot);
+        uint32_t quota = need_eq > eqb ? need_eq - eqb : 0u;
+#pragma unroll
+        for (int i = 0; i < 4 * NV4; ++i) {
+            if (i / 4 < G && kr[i] == kappa && quota != 0u) {
+                if (i < 32) m0 |= 1u << (i & 31); else m1 |= 1u << (i & 31);
+                --quota;
+            }
+        }
+    }
 
-    launder(kr);
-    // 4. emit: packed counts (keys > kappa in the low half, == kappa in the
-    // high half; each at most 32768) per 4-key group, prefix in column order
-    uint32_t incl[NV4];
+    // 4. emit: each thread's selected keys take consecutive slots from the
+    // count of selected keys in the threads before it (column order)
+    uint32_t slot = block_excl_scan((uint32_t)(__builtin_popcount(m0) + __builtin_popcount(m1)), sh.wtot);
+    const int colbase = 4 * G * tz;
+    if (want_keys) {
+        launder(kr);
 #pragma unroll
-    for (int u = 0; u < NV4; ++u) {
-        if (u < ngroups) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t key = kr[4 * u + i];
-                c += key > kappa ? 1u : (key == kappa ? 0x10000u : 0u);
-            }
-            const uint32_t x = wave_scan_add(c);
-            incl[u] = x - c;   // exclusive within the wave
-            if (l == 63) sh.gsum[u * NWAVE + w] = x;
-        }
-    }
-    lds_barrier();
-    if (w == 0) {   // exclusive prefix over (group, wave) in column order
-        const int n2 = ngroups * NWAVE;
-        const uint32_t a = 2 * l < n2 ? sh.gsum[2 * l] : 0u;
-        const uint32_t b = 2 * l + 1 < n2 ? sh.gsum[2 * l + 1] : 0u;
-        const uint32_t s = a + b;
-        const uint32_t x = wave_scan_add(s);
-        if (2 * l < n2) sh.gsum[2 * l] = x - s;
-        if (2 * l + 1 < n2) sh.gsum[2 * l + 1] = x - s + a;
-    }
-    lds_barrier();
-    launder(kr);
-#pragma unroll
-    for (int u = 0; u < NV4; ++u) {
-        if (u < ngroups) {
-            const uint32_t base = sh.gsum[u * NWAVE + w] + incl[u];
-            uint32_t g = base & 0xFFFFu, e = base >> 16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t key = kr[4 * u + i];
-                const bool fg = key > kappa, fe = key == kappa;
-                const uint32_t slot = g + (e < need_eq ? e : need_eq);
-                const bool take = (fg || (fe && e < need_eq)) && slot < (uint32_t)k;
-                const uint32_t at = take ? slot : 2048u + (uint32_t)l;   // this lane's spare slot
-                sh.ocol[at] = 4 * (u * TPB + tz) + i;
-                if (want_keys) sh.okey[at] = key;
-                g += fg ? 1u : 0u;
-                e += fe ? 1u : 0u;
+        for (int i = 0; i < 4 * NV4; ++i) {
+            if (i / 4 < G && (((i < 32 ? m0 : m1) >> (i & 31)) & 1u)) {
+                if (slot < (uint32_t)k) {   // (exactly k keys are selected)
+                    sh.ocol[slot] = colbase + i;
+                    sh.okey[slot] = kr[i];
+                }
+                ++slot;
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        while (m0 != 0u) {
+            if (slot < (uint32_t)k) sh.ocol[slot] = colbase + __builtin_ctz(m0);   // (exactly k keys are selected)
+            ++slot;
+            m0 &= m0 - 1u;
+        }
+        while (m1 != 0u) {
+            if (slot < (uint32_t)k) sh.ocol[slot] = colbase + 32 + __builtin_ctz(m1);
+            ++slot;
+            m1 &= m1 - 1u;
+        }
     }
     lds_barrier();   // selection in sh.ocol / sh.okey
 }
@@ -366,8 +439,9 @@ __device__ __forceinline__ ChunkItem chunk_item(const TopkParams &p, int item) {
 // 16-byte direct-to-LDS loads when rows allow them, else plain loads and LDS
 // stores.  Columns past len are left unwritten (and dropped when the keys are
 // formed); a 16-byte load may read up to 3 of them, still inside the row.
-__device__ __forceinline__ void stage_chunk(const ChunkItem &it, float *stage, int tid) {
+__device__ __forceinline__ void stage_chunk(const ChunkItem &it, float *stage, int tid, int u0, int u1) {
     const int w = tid >> 6, l = tid & 63;
+    if (it.len <= 0) return;
     if (it.vec) {
         uint64_t base = (uint64_t)(uintptr_t)it.row;
         // (readfirstlane returns int: widen through uint32_t)
@@ -376,10 +450,10 @@ __device__ __forceinline__ void stage_chunk(const ChunkItem &it, float *stage, i
 #pragma unroll
         for (int u = 0; u < CH_V4; ++u) {
             const int c = 4 * (u * TPB + 64 * w + l);
-            if (c < it.len)
+            if (u >= u0 && u < u1 && c < it.len)
                 dma16s(base, 4u * (uint32_t)c, (const DSA_LDS void *)(stage + 4 * (u * TPB + 64 * w)));
         }
-    } else {
+    } else if (u0 == 0) {
         for (int c = tid; c < it.len; c += TPB) stage[c] = it.row[c];
     }
 }
@@ -394,72 +468,113 @@ __device__ __forceinline__ void stage_chunk(const ChunkItem &it, float *stage, i
 __global__ __launch_bounds__(TPB, 2) void topk_chunk_kernel(TopkParams p, int nitems) {
     __shared__ __attribute__((aligned(16))) float stage[TOPK_CHUNK];
     __shared__ SelectShared sh;
-    const int tid = threadIdx.x, k = p.k;
+    const int tid = threadIdx.x, k = p.k, grid = (int)gridDim.x;
     int item = blockIdx.x;
     if (item >= nitems) return;
     ChunkItem nxt = chunk_item(p, item);
-    if (nxt.len > 0) stage_chunk(nxt, stage, tid);
-    for (; item < nitems; item += gridDim.x) {
+    stage_chunk(nxt, stage, tid, 0, CH_V4);
+    // the next item's row bounds (scalar loads) are fetched one item ahead
+    ChunkItem nn{};
+    if (item + grid < nitems) nn = chunk_item(p, item + grid);
+    for (; item < nitems; item += grid) {
         // the thread index rebuilt from an opaque zero (item < 2^30): per-key
         // column arithmetic then stays inside the loop instead of being held
         // in registers across it
         const int tz = tid + (item >> 30);
         const ChunkItem it = nxt;
+        const bool has_next = item + grid < nitems;
+        nxt = nn;
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's part of the stage
         lds_barrier();
-        uint32_t kr[4 * CH_V4];
+        // thread tz takes the G 4-column groups tz * G + u: consecutive
+        // columns, and with G odd the 16-byte LDS reads of a wave fall in
+        // distinct banks.  (Reads of groups u >= G stay inside the stage and
+        // are dropped.)
+        const int ngroups = (it.len + 4 * TPB - 1) / (4 * TPB);
+        const int G = ngroups < CH_V4 ? (ngroups | 1) : CH_V4;
+        float4 f4[CH_V4];
+        if (G > CH_V4 / 2) {
+#pragma unroll
+            for (int u = 0; u < CH_V4; ++u) f4[u] = *reinterpret_cast<const float4 *>(stage + 4 * (tz * G + u));
+        } else {
+#pragma unroll
+            for (int u = 0; u < CH_V4 / 2; ++u) f4[u] = *reinterpret_cast<const float4 *>(stage + 4 * (tz * G + u));
+#pragma unroll
+            for (int u = CH_V4 / 2; u < CH_V4; ++u) f4[u] = float4{0.f, 0.f, 0.f, 0.f};
+        }
+        // this thread's columns end at lim (its G groups, cut at the chunk's end)
+        const int lim = 4 * G * (tz + 1) < it.len ? 4 * G * (tz + 1) : it.len;
+        uint32_t kr[4 * CH_V4], lmin = 0xFFFFFFFFu, lmax = 0u;
 #pragma unroll
         for (int u = 0; u < CH_V4; ++u) {
-            const int c = 4 * (u * TPB + tz);
-            const float4 f4 = c < it.len ? *reinterpret_cast<const float4 *>(stage + c) : float4{0.f, 0.f, 0.f, 0.f};
-            const float f[4] = {f4.x, f4.y, f4.z, f4.w};
+            const int c = 4 * (tz * G + u);
+            const float f[4] = {f4[u].x, f4[u].y, f4[u].z, f4[u].w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kr[4 * u + i] = c + i < it.len ? score_key(f[i]) : 0u;
+            for (int i = 0; i < 4; ++i) {
+                // (a mask, not a branch around the conversion)
+                const uint32_t key = score_key(f[i]) & (0u - (uint32_t)(c + i < lim));
+                kr[4 * u + i] = key;
+                lmin = key != 0u && key < lmin ? key : lmin;
+                lmax = key > lmax ? key : lmax;
+            }
         }
         lds_barrier();   // stage read by every thread: the next item may land in it
-        if (item + (int)gridDim.x < nitems) {
-            nxt = chunk_item(p, item + gridDim.x);
-            if (nxt.len > 0) stage_chunk(nxt, stage, tz);
-        }
+        // the next item's scores, 1 KB loads per wave issued in seven parts
+        // spread over the select (hook(part) issues the parts up to part), so
+        // that the stage refills at a steady rate instead of in one burst that
+        // stalls the issuing waves
+        int issued = 0;
+        auto hook = [&](int part) {
+            constexpr int PART[8] = {0, 2, 4, 6, 8, 10, 13, CH_V4};
+            if (has_next && part > issued) {
+                stage_chunk(nxt, stage, tz, PART[issued], PART[part]);
+                issued = part;
+            }
+        };
+        hook(1);
+        if (item + 2 * grid < nitems) nn = chunk_item(p, item + 2 * grid);
         int32_t *out = p.idx + (int64_t)it.t * k;
-        if (it.n <= k) {  // everything visible is selected
-            if (it.c == 0)
-                for (int j = tz; j < k; j += TPB) out[j] = j < it.n ? j : -1;
-            continue;
-        }
-        if (it.len == 0) continue;  // chunk past the visible end
-        const int c0 = it.c0, len = it.len;
-        const int ngroups = (len + 4 * TPB - 1) / (4 * TPB);
+        const int c0 = it.c0;
+        int len = it.len;
         // multi-chunk row: local top-min(k, len) candidates of this chunk
         const bool multi = it.n > TOPK_CHUNK;
-        uint32_t *ck = p.cand_key + ((int64_t)it.t * p.nchunk + it.c) * k;
-        int32_t *cp = p.cand_pos + ((int64_t)it.t * p.nchunk + it.c) * k;
-        if (multi && len <= k) {   // the whole chunk, in column order, padded
+        if (it.n <= k || len == 0 || (multi && len <= k)) {
+            hook(7);
+            if (it.n <= k) {  // everything visible is selected
+                if (it.c == 0)
+                    for (int j = tz; j < k; j += TPB) out[j] = j < it.n ? j : -1;
+            } else if (len > 0) {   // the whole chunk, in column order, padded
+                uint32_t *ck = p.cand_key + ((int64_t)it.t * p.nchunk + it.c) * k;
+                int32_t *cp = p.cand_pos + ((int64_t)it.t * p.nchunk + it.c) * k;
+                asm volatile("" : "+s"(len));   // fresh compares below, not the ones of the key loop
 #pragma unroll
-            for (int u = 0; u < CH_V4; ++u)
+                for (int u = 0; u < CH_V4; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int c = 4 * (u * TPB + tz) + i;
-                    if (c < len) {
-                        ck[c] = kr[4 * u + i];
-                        cp[c] = c0 + c;
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = 4 * (tz * G + u) + i;
+                        if (u < G && c < len) {
+                            ck[c] = kr[4 * u + i];
+                            cp[c] = c0 + c;
+                        }
                     }
+                for (int j = len + tz; j < k; j += TPB) {
+                    ck[j] = 0u;
+                    cp[j] = -1;
                 }
-            for (int j = len + tz; j < k; j += TPB) {
-                ck[j] = 0u;
-                cp[j] = -1;
             }
             continue;
         }
-        select_regs<CH_V4>(kr, ngroups, k, sh, tz, multi);
-        for (int j = tz; j < k; j += TPB) {
-            const int col = c0 + sh.ocol[j];
-            if (multi) {
+        select_regs<CH_V4>(kr, G, lmin, lmax, k, sh, tz, multi, hook);
+        hook(7);
+        if (multi) {
+            uint32_t *ck = p.cand_key + ((int64_t)it.t * p.nchunk + it.c) * k;
+            int32_t *cp = p.cand_pos + ((int64_t)it.t * p.nchunk + it.c) * k;
+            for (int j = tz; j < k; j += TPB) {
                 ck[j] = sh.okey[j];
-                cp[j] = col;
-            } else {
-                out[j] = col;
+                cp[j] = c0 + sh.ocol[j];
             }
+        } else {
+            for (int j = tz; j < k; j += TPB) out[j] = c0 + sh.ocol[j];
         }
         lds_barrier();   // sh free for the next select
     }
@@ -478,18 +593,39 @@ __global__ __launch_bounds__(TPB, 2) void topk_merge_kernel(TopkParams p) {
     const int m = nch * k;
     const uint32_t *ck = p.cand_key + (int64_t)t * p.nchunk * k;
     const int32_t *cp = p.cand_pos + (int64_t)t * p.nchunk * k;
-    uint32_t kr[4 * MG_V4];
+    // thread tid takes the candidates 4 * G * tid + j, j < 4 * G
+    const int G = (m + 4 * TPB - 1) / (4 * TPB);
+    uint32_t kr[4 * MG_V4], lmin = 0xFFFFFFFFu, lmax = 0u;
+    if ((k & 3) == 0) {   // m and every row's block are multiples of 4 keys: 16-byte loads
 #pragma unroll
-    for (int u = 0; u < MG_V4; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = 4 * (u * TPB + tid) + i;
-            kr[4 * u + i] = c < m ? ck[c] : 0u;
+        for (int u = 0; u < MG_V4; ++u) {
+            const int c = 4 * (tid * G + u);
+            const uint4 v = u < G && c < m ? *reinterpret_cast<const uint4 *>(ck + c) : uint4{0u, 0u, 0u, 0u};
+            kr[4 * u] = v.x;
+            kr[4 * u + 1] = v.y;
+            kr[4 * u + 2] = v.z;
+            kr[4 * u + 3] = v.w;
         }
-    const int ngroups = (m + 4 * TPB - 1) / (4 * TPB);
+    } else {
+#pragma unroll
+        for (int u = 0; u < MG_V4; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 4 * (tid * G + u) + i;
+                kr[4 * u + i] = u < G && c < m ? ck[c] : 0u;
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * MG_V4; ++i) {
+        lmin = kr[i] != 0u && kr[i] < lmin ? kr[i] : lmin;
+        lmax = kr[i] > lmax ? kr[i] : lmax;
+    }
     int32_t *out = p.idx + (int64_t)t * k;
-    select_regs<MG_V4>(kr, ngroups, k, sh, tid, false);
-    for (int j = tid; j < k; j += TPB) out[j] = cp[sh.ocol[j]];
+    select_regs<MG_V4>(kr, G, lmin, lmax, k, sh, tid, false, [](int) {});
+    for (int j = tid; j < k; j += TPB) {
+        const int c = sh.ocol[j];   // a candidate index below m (checked: it addresses cp)
+        out[j] = (unsigned)c < (unsigned)m ? cp[c] : -1;
+    }
 }
 
 // The selection of a row that sees no more than k keys: every visible key,

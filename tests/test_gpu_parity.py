@@ -141,6 +141,55 @@ def test_topk_all_equal_rows(dsa):
     assert np.array_equal(g[0], np.arange(2048)) and np.array_equal(g[1], np.arange(2048))
 
 
+def _finite_topk_case(name):
+    """Finite scores (the value-binned path; -inf among the visible columns
+    sends a row to the radix path instead)."""
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    k = 2048
+    if name == "finite_prefill_2100":
+        b = synth.Batch.prefill(2100, 2100, 0)
+    elif name == "finite_long_rows":
+        b = synth.Batch.decode([32768, 32769, 40000, 70001, 131072, 2049])
+    else:
+        b = synth.Batch.decode([3000, 17000, 30721, 32768, 50000])
+    _, _, ctx, _, nvis = oracle.visible(b.cu_q, b.cu_kv, b.pos0)
+    s = rng.standard_normal((b.T, int(b.max_kv))).astype(np.float32)
+    if name.startswith("finite"):
+        s[:, ::17] = np.float32(0.75)
+        s[:, 5::23] = np.float32(-0.0)
+        s[:, 7::29] = np.float32(0.0)
+    elif name.startswith("kappa_ties"):
+        # 2t keys around rank k share the k-th value: the tie at the boundary
+        # is broken by column, across the whole row (and across chunks)
+        t = int(name.rsplit("_", 1)[1]) // 2
+        for r in range(b.T):
+            n = int(nvis[r])
+            order = np.argsort(-s[r, :n], kind="stable")
+            s[r, order[k - 1 - t:k - 1 + t]] = s[r, order[k - 1]]
+    elif name == "sub_ulp_bins":
+        # a range of a few float ulps: value bins narrower than the spacing of
+        # the scores, most scores tied
+        s = (np.float32(1000.0) + np.float32(2e-4) * s).astype(np.float32)
+    else:
+        raise KeyError(name)
+    for r in range(b.T):
+        s[r, nvis[r]:] = -np.inf
+    return b, k, s
+
+
+@pytest.mark.parametrize("name", ["finite_prefill_2100", "finite_long_rows", "kappa_ties_300", "kappa_ties_900",
+                                  "sub_ulp_bins"])
+def test_topk_bit_exact_finite_scores(dsa, name):
+    say(f"[topk] {name}")
+    b, k, s = _finite_topk_case(name)
+    ref = oracle.topk(b.cu_q, b.cu_kv, b.pos0, s, k)
+    batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0)
+    idx = torch.full((b.T, k), -7, dtype=torch.int32, device="cuda")
+    dsa.topk(batch, dev(s), k, idx)
+    g = idx.cpu().numpy()
+    assert np.array_equal(g, ref), f"{name}: {np.sum(np.any(g != ref, axis=1))} rows differ"
+
+
 # ---------------------------------------------------------------- attention
 
 def _attn_case(name):
