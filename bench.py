@@ -52,23 +52,23 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     ("prefill_32k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "4d8eb309aa9735ae", "fetch_kib": 11618602, "write_kib": 4352330},
+        "sha256_16": "d2c03ab62fc0b1a3", "fetch_kib": 11617984, "write_kib": 4352233},
     ("short_prefill_2k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "4d8eb309aa9735ae", "fetch_kib": 192978, "write_kib": 272097},
+        "sha256_16": "d2c03ab62fc0b1a3", "fetch_kib": 192977, "write_kib": 272100},
     ("decode_64k", "indexer_decode_kernel"): {
         "sources": ("indexer.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "d700ff06de14d768", "fetch_kib": 289241, "write_kib": 17469},
+        "sha256_16": "2413eb3049fc7b19", "fetch_kib": 289220, "write_kib": 17469},
     ("indexer_kl_32k", "indexer_kl_kernel"): {
         "sources": ("indexer_kl.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "7e04a3d781a597b9", "fetch_kib": 18370464, "write_kib": 1340},
+        "sha256_16": "9b7feb36ad51a4c0", "fetch_kib": 18264248, "write_kib": 1335},
     # the whole backward (its 10 kernels, 8 row chunks), summed per call
     ("sparse_bwd_32k", "dsa_sparse_mla_bwd"): {
         "sources": ("sparse_mla_bwd.hip", "dsa_device.h", "kernels.h"),
         "sha256_16": "b63a5d5b42ec31b1", "fetch_kib": 93422305, "write_kib": 120081451},
     ("quant_append_32k", "quant_groups_kernel<8192,256>"): {
         "sources": ("quant.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "a6da93774139246b", "fetch_kib": 524451, "write_kib": 270336},
+        "sha256_16": "9bfd0fd924bee994", "fetch_kib": 524449, "write_kib": 270336},
 }
 
 def measured_traffic(workload, kernel):
