@@ -146,7 +146,9 @@ def _finite_topk_case(name):
     sends a row to the radix path instead)."""
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     k = 2048
-    if name == "finite_prefill_2100":
+    if name == "finite_small_k":
+        b, k = synth.Batch.prefill(300, 300, 0), 7   # the k-th key sits in the top bin
+    elif name == "finite_prefill_2100":
         b = synth.Batch.prefill(2100, 2100, 0)
     elif name == "finite_long_rows":
         b = synth.Batch.decode([32768, 32769, 40000, 70001, 131072, 2049])
@@ -177,17 +179,18 @@ def _finite_topk_case(name):
     return b, k, s
 
 
-@pytest.mark.parametrize("name", ["finite_prefill_2100", "finite_long_rows", "kappa_ties_300", "kappa_ties_900",
-                                  "sub_ulp_bins"])
+@pytest.mark.parametrize("name", ["finite_small_k", "finite_prefill_2100", "finite_long_rows", "kappa_ties_300",
+                                  "kappa_ties_900", "sub_ulp_bins"])
 def test_topk_bit_exact_finite_scores(dsa, name):
     say(f"[topk] {name}")
     b, k, s = _finite_topk_case(name)
-    ref = oracle.topk(b.cu_q, b.cu_kv, b.pos0, s, k)
-    batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0)
-    idx = torch.full((b.T, k), -7, dtype=torch.int32, device="cuda")
-    dsa.topk(batch, dev(s), k, idx)
-    g = idx.cpu().numpy()
-    assert np.array_equal(g, ref), f"{name}: {np.sum(np.any(g != ref, axis=1))} rows differ"
+    for kk in ([1, k] if name == "finite_small_k" else [k]):
+        ref = oracle.topk(b.cu_q, b.cu_kv, b.pos0, s, kk)
+        batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0)
+        idx = torch.full((b.T, kk), -7, dtype=torch.int32, device="cuda")
+        dsa.topk(batch, dev(s), kk, idx)
+        g = idx.cpu().numpy()
+        assert np.array_equal(g, ref), f"{name} k={kk}: {np.sum(np.any(g != ref, axis=1))} rows differ"
 
 
 # ---------------------------------------------------------------- attention
