@@ -178,19 +178,6 @@ __device__ __forceinline__ void radix_kappa(uint32_t (&kr)[4 * NV4], int ngroups
     lds_barrier();
 }
 
-// Block sum of one value per thread (every thread gets the total).
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *wtot) {
-    const int l = lane_id(), w = threadIdx.x >> 6;
-    const uint32_t x = wave_scan_add(v);
-    if (l == 63) wtot[w] = x;
-    lds_barrier();
-    uint32_t s = 0;
-#pragma unroll
-    for (int i = 0; i < NWAVE; ++i) s += wtot[i];
-    lds_barrier();
-    return s;
-}
-
 // Steps 1-4 over the register keys kr (key 0 = no key).  Thread tz holds the
 // G * 4 consecutive columns 4 * G * tz + j in kr[j], j < 4 * G (G <= NV4), at
 // least k + 1 of all keys real; lmin / lmax are the thread's smallest nonzero
