@@ -7,7 +7,7 @@
 // column; all visible columns when there are at most k.  Output: the selected
 // columns in ascending order, -1 padded.
 //
-// Method (one 512-thread workgroup per row chunk of up to 32768 columns; the
+// Method (one 1024-thread workgroup per row chunk of up to 32768 columns; the
 // chunk's scores stay in registers as order-preserving uint32 keys, thread t
 // holding the 4G consecutive columns 4Gt .. 4Gt + 4G - 1):
 //   1. range   : block minimum and maximum of the chunk's scores.
@@ -41,11 +41,11 @@ namespace dsa {
 
 namespace {
 
-constexpr int TPB = 512;                                   // threads per workgroup
+constexpr int TPB = 1024;                                  // threads per workgroup (16 waves, 4 per SIMD)
 constexpr int NWAVE = TPB / kWave;                         // 8
 constexpr int NBIN = 2048;                                 // histogram bins
 constexpr int BPT = NBIN / TPB;                            // bins scanned per thread
-constexpr int CCAP = TPB;                                  // candidates ranked directly (one per thread)
+constexpr int CCAP = 512;                                  // candidates ranked directly (one per thread)
 constexpr int CH_V4 = TOPK_CHUNK / (4 * TPB);              // 4-key groups per thread, chunk kernel
 constexpr int MG_V4 = TOPK_MAX_CHUNKS * 2048 / (4 * TPB);  // 4-key groups per thread, merge kernel
 static_assert(NBIN % TPB == 0 && CH_V4 * 4 * TPB == TOPK_CHUNK && MG_V4 * 4 * TPB == TOPK_MAX_CHUNKS * 2048,
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(TPB, 2) void topk_chunk_kernel(TopkParams p, int ni
         // stalls the issuing waves
         int issued = 0;
         auto hook = [&](int part) {
-            constexpr int PART[8] = {0, 2, 4, 6, 8, 10, 13, CH_V4};
+            constexpr int PART[8] = {0, 1, 2, 3, 4, 5, 6, CH_V4};
             if (has_next && part > issued) {
                 stage_chunk(nxt, stage, tz, PART[issued], PART[part]);
                 issued = part;
