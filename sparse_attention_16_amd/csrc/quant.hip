@@ -9,14 +9,14 @@
 //   code = E4M3FN(x / s): the nearest code to the binary32 quotient, ties to
 //          the even mantissa, magnitudes above 448 saturate to 448, the sign
 //          bit follows the quotient.
-// The quotient is the correctly rounded binary32 division; the rounding to
-// E4M3FN is done in software (exact power-of-two scaling, then round to
-// nearest even on the scaled value), so the codes do not depend on the
-// hardware conversion's saturation mode.  The code only depends on which side
-// of an E4M3FN rounding midpoint the quotient lies, so it is first taken from
-// x * RN(1/s), which is within 2 ulp of the correctly rounded quotient; a
-// value whose product lies within 2^-16 (scaled units, far more than 2 ulp)
-// of a midpoint is redone with the correctly rounded division.
+// The code only depends on which side of an E4M3FN rounding midpoint the
+// quotient lies, so it is taken from y = x * RN(1/s), within 2 ulp of the
+// correctly rounded quotient, by the hardware conversion (round to nearest
+// even; it gives the same code as e4m3_rne below for every binary32 of
+// magnitude under 460, and |y| stays below 449, so its saturation mode never
+// matters).  When y - 4 ulp and y + 4 ulp round to different codes (a
+// midpoint within a few ulps: about one value in 10^5), the correctly rounded
+// division is rounded in software instead.
 //
 // HBM-bound: 4 bytes read and 1 byte written per value, one group per 32 (key)
 // or 256 (query) threads, 16-byte loads.
@@ -27,23 +27,19 @@ namespace dsa {
 
 namespace {
 
-// E4M3FN code of a binary32 value (round to nearest even, saturating).  When
-// near is given, it is set if y lies within 2^-16 of a rounding midpoint in
-// the scaled units (value / code step).
-__device__ __forceinline__ uint32_t e4m3_rne(float y, bool *near = nullptr) {
+// E4M3FN code of a binary32 value (round to nearest even, saturating):
+// exact power-of-two scaling, then rounding to an integer number of steps.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
     const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
     const float a = fabsf(y);
     uint32_t code;
-    float t = 0.f;                                       // value in code steps
     if (a >= 448.f) {
         code = 0x7Eu;                                    // largest finite value
     } else if (a < 0.015625f) {                          // below 2^-6: steps of 2^-9
-        t = a * 512.f;
-        code = (uint32_t)rintf(t);                       // 0..8; 8 is 2^-6, code 0x08
+        code = (uint32_t)rintf(a * 512.f);               // 0..8; 8 is 2^-6, code 0x08
     } else {
         int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // -6 .. 8
-        t = ldexpf(a, 3 - e);                                      // [8, 16)
-        uint32_t m = (uint32_t)rintf(t);                           // 8 .. 16
+        uint32_t m = (uint32_t)rintf(ldexpf(a, 3 - e));            // 8 .. 16
         if (m == 16u) {
             m = 8u;
             e += 1;
@@ -51,14 +47,9 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y, bool *near = nullptr) {
         code = ((uint32_t)(e + 7) << 3) | (m - 8u);
         code = code > 0x7Eu ? 0x7Eu : code;
     }
-    if (near) *near = fabsf(t - truncf(t) - 0.5f) < 1.52587890625e-5f;   // 2^-16 (saturated: t = 0, false)
     return code | sign;
 }
 
-// Groups of COLS values, NT threads per group (VPT = COLS / NT values each,
-// a multiple of 4), 256 threads per workgroup.  Group r of x goes to row
-// dst[r] of codes / scale (dst null: row r; rows outside [0, nout) are
-// skipped).  The scale is written rep times (rep consecutive entries).
 template <int COLS, int NT>
 __global__ __launch_bounds__(256) void quant_groups_kernel(const float *__restrict__ x, int64_t rows,
                                                           uint8_t *__restrict__ codes,
@@ -103,13 +94,26 @@ __global__ __launch_bounds__(256) void quant_groups_kernel(const float *__restri
     uint8_t *cr = codes + orow * COLS;
 #pragma unroll
     for (int u = 0; u < VPT / 4; ++u) {
-        uint32_t packed = 0;
+        // y = v * (1/s) is within 2 ulps of the exact quotient v / s.  The
+        // hardware conversion rounds to nearest even exactly like e4m3_rne
+        // (checked on every fp32 of magnitude below 460) and is monotone, so
+        // when y +- 4 ulps give the same code, so does v / s; otherwise (a
+        // rounding boundary within a few ulps, rare) the exact quotient is
+        // rounded in software.
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = v[4 * u + j] * rs;
+        uint32_t packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)packed, true);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            bool near;
-            uint32_t c = e4m3_rne(v[4 * u + j] * rs, &near);
-            if (near) c = e4m3_rne(v[4 * u + j] / s);   // rare: the exact quotient decides
-            packed |= c << (8 * j);
+            const uint32_t a = __float_as_uint(y[j]) & 0x7FFFFFFFu;
+            const uint32_t lh = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                __uint_as_float(a - (a < 4u ? a : 4u)), __uint_as_float(a + 4u), 0, false);
+            if (((lh ^ (lh >> 8)) & 0xFFu) != 0u) {
+                const uint32_t c = e4m3_rne(v[4 * u + j] / s);
+                packed = (packed & ~(0xFFu << (8 * j))) | (c << (8 * j));
+            }
         }
         *reinterpret_cast<uint32_t *>(cr + 4 * (i + NT * u)) = packed;
     }
