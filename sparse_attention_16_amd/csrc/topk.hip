@@ -152,6 +152,7 @@ __device__ __forceinline__ void radix_kappa(uint32_t (&kr)[4 * NV4], int ngroups
         sh.rem = (uint32_t)k;
     }
     constexpr int SHIFT[3] = {21, 10, 0}, WIDTH[3] = {11, 11, 10};
+    static_assert(NBIN >= (1 << 11), "the radix digits index the histogram");
 #pragma unroll
     for (int ps = 0; ps < 3; ++ps) {
         clear_hist(sh);
