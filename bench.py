@@ -1,18 +1,26 @@
 """DSA hot-path benchmark on one MI355X: indexer + top-2048 + sparse MQA MLA.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_32k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
 
 A step is one call of the fused C-ABI entry (dsa_prefill_fwd, or dsa_decode_fwd
 for the decode workload) over one batch of synthetic inputs already resident
-in HBM.  Prints one JSON line: tokens/s over the K timed steps, the roofline of
-the dominant kernel (timed with HIP events around its own launches, on the
-stream it runs on), and the CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+in HBM.  Prints one JSON line: tokens/s over the K timed steps, every kernel
+of the step timed with HIP events recorded around its own launches on the
+stream it runs on (dsa_fwd_profile; mean and median over >= 20 calls), the
+roofline of the kernel with the largest time, the step's event median with
+and without an Infinity Cache flush, and the CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
+
+The default workload, headline, is the metric's pair: `value` is the 32K
+prefill (one sequence of 32768 tokens), and the line nests the same figures
+for the decode batch (64 sequences, one new token each) under "decode_64k".
 
 Workloads (synthetic, seeded; the shapes and distributions of the DSA
-configurations): prefill_32k (default), prefill_4k, decode_64k (64 sequences,
+configurations): prefill_32k, prefill_4k, decode_64k (64 sequences,
 contexts uniform in 16384..131072, one new token each), chunked_128k (4096 new
-tokens at the end of a 131072-entry context).
+tokens at the end of a 131072-entry context), short_prefill_2k (the
+short-sequence mode), and the neighbours of the path: quant_append_32k,
+indexer_kl_32k, sparse_bwd_32k.
 """
 from __future__ import annotations
 
@@ -498,9 +506,14 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_32k",
-                    choices=["prefill_32k", "prefill_4k", "decode_64k", "chunked_128k", "quant_append_32k",
-                             "short_prefill_2k", "indexer_kl_32k", "sparse_bwd_32k"])
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "prefill_32k", "prefill_4k", "decode_64k", "chunked_128k",
+                             "quant_append_32k", "short_prefill_2k", "indexer_kl_32k", "sparse_bwd_32k"],
+                    help="headline (default): prefill_32k with the decode_64k figures nested in the same line")
+    ap.add_argument("--decode-steps", type=int, default=200,
+                    help="timed steps of the nested decode_64k figures (at least --steps)")
+    ap.add_argument("--profile-reps", type=int, default=20,
+                    help="calls timed per kernel with HIP events (at least 20)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=5,
@@ -534,10 +547,154 @@ def main(argv=None):
         return kl_bench(args, dsa)
     if args.workload == "sparse_bwd_32k":
         return bwd_bench(args, dsa)
-    wl, entry = make_workload(args.workload)
+    if args.workload == "headline":
+        line = fwd_bench(args, dsa, "prefill_32k", args.steps, args.warmup)
+        dec_steps = max(args.steps, args.decode_steps)
+        dec = fwd_bench(args, dsa, "decode_64k", dec_steps, max(args.warmup, 10))
+        line["decode_64k"] = {k: dec[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step", "timing",
+                                                  "config", "roofline", "kernels", "cpu_baseline") if k in dec}
+        line["decode_64k"]["tokens_per_s"] = dec["value"]
+    else:
+        line = fwd_bench(args, dsa, args.workload, args.steps, args.warmup)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+# ------------------------------------------------------ fused forward (A1-A9)
+
+def cpu_info():
+    """The host the CPU baseline ran on: model, logical CPUs, affinity, OpenMP setting."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": aff,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def sampled_pairs(batch, k):
+    """(query, key) pairs the threshold sample scores: per block of 16 query
+    rows of a sequence whose longest row sees n > 4096 (and > k) keys, the keys
+    o + i * (n // m), i < m = clamp(n // 32, 512, 1024), that each row sees
+    (the sample kernel's grid, offset hashed from the block and the sequence)."""
+    cu_q, cu_kv, pos0 = np.asarray(batch.cu_q), np.asarray(batch.cu_kv), np.asarray(batch.pos0)
+    total = 0
+    for sq in range(len(pos0)):
+        nq = int(cu_q[sq + 1] - cu_q[sq])
+        ctx = int(cu_kv[sq + 1] - cu_kv[sq])
+        nv = np.clip(np.minimum(int(pos0[sq]) + np.arange(nq) + 1, ctx), 0, None)
+        for blk in range(0, nq, 16):
+            rows = nv[blk:blk + 16]
+            n_hi = int(rows.max())
+            if n_hi <= 4096 or n_hi <= k:
+                continue
+            m = min(max(n_hi // 32, 512), 1024)
+            stride = n_hi // m
+            o = (((blk // 16) * 2654435761 + sq * 40503) & 0xFFFFFFFF) % stride
+            total += int(np.sum(np.clip(-(-(rows - o) // stride), 0, m)))
+    return total
+
+
+def scored_rows(batch, k):
+    """Visible counts of the rows the candidate indexer scores: every row of a
+    16-row block whose longest row sees more than k keys (blocks that see at
+    most k keys need no scores; prefill layout)."""
+    cu_q, cu_kv, pos0 = np.asarray(batch.cu_q), np.asarray(batch.cu_kv), np.asarray(batch.pos0)
+    out = []
+    for sq in range(len(pos0)):
+        nq = int(cu_q[sq + 1] - cu_q[sq])
+        ctx = int(cu_kv[sq + 1] - cu_kv[sq])
+        nv = np.clip(np.minimum(int(pos0[sq]) + np.arange(nq) + 1, ctx), 0, None)
+        for blk in range(0, nq, 16):
+            rows = nv[blk:blk + 16]
+            if rows.max() > k:
+                out.append(rows)
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def kernel_roof(name, wl, entry, nvis, ms_mean, ms_median, splits=1, items=-1):
+    """Roofline of one kernel of the fused forward: its bound, algorithmic work
+    per launch (flops or HBM bytes, as stated per kernel below), achieved rate
+    on the mean launch time, fraction of the MI355X peak and the target."""
     b = wl.batch
+    k, T = wl.k, b.T
+    long_rows = nvis > k
+    if name == "indexer_sample_kernel":
+        bound, work = "mfma", 2.0 * HI * DI * sampled_pairs(b, k)   # fp8 flops of the sampled pairs
+        peak, unit, target = PEAK_FP8_TFLOPS, "TFLOP/s", 0.5
+    elif name == "indexer_prefill_kernel<cand>":
+        bound, work = "mfma", indexer_flops(scored_rows(b, k))     # 2*64*128 fp8 flops per scored visible pair
+        peak, unit, target = PEAK_FP8_TFLOPS, "TFLOP/s", 0.5
+    elif name == "indexer_decode_kernel<cand>":
+        # keys (128 code bytes + 4 scale bytes) of rows that see more than k, their query rows
+        work = (DI + 4) * float(np.sum(nvis[long_rows])) + float(np.sum(long_rows)) * (HI * DI + HI * 8)
+        bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.5
+    elif name == "cand_select_kernel":
+        # candidate keys read, the selected positions read, idx written
+        work = 4.0 * max(items, 0) + 8.0 * k * T
+        bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.6
+    elif name == "indexer_prefill_kernel":
+        bound, work = "mfma", indexer_flops(nvis)            # 2*64*128 fp8 flops per visible pair
+        peak, unit, target = PEAK_FP8_TFLOPS, "TFLOP/s", 0.5
+    elif name == "indexer_decode_kernel":
+        bound, work = "hbm", indexer_bytes(nvis, b.N, T)     # keys + scales + queries read, scores written
+        peak, unit, target = PEAK_HBM_GBS, "GB/s", 0.5
+    elif name == "topk_chunk_kernel":
+        nch = np.ceil(nvis / 32768.0)
+        # scores of rows longer than k read once, idx written; chunked rows write (key, position) candidates
+        work = 4.0 * float(np.sum(nvis[long_rows])) + 4.0 * k * T + 8.0 * k * float(np.sum(nch[nvis > 32768]))
+        bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.6
+    elif name == "topk_merge_kernel":
+        nch = np.ceil(nvis / 32768.0)
+        work = 8.0 * k * float(np.sum(nch[nvis > 32768])) + 4.0 * k * float(np.sum(nvis > 32768))
+        bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.6
+    elif name == "sparse_mla_kernel" and splits == 1:
+        bound, work = "mfma", mla_flops(nvis, k)              # 128 heads x 2 x (576 + 512) per selected pair
+        peak, unit, target = PEAK_BF16_TFLOPS, "TFLOP/s", 0.5
+    elif name == "sparse_mla_kernel":
+        # split-KV (few rows): every selected latent row gathered from HBM, q read, partials written
+        work = mla_bytes(nvis, k, T) - T * H * DV * 2 + T * splits * H * (DV * 2 + 4)
+        bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.6
+    elif name == "mla_merge_kernel":
+        work = T * splits * H * (DV * 2 + 4) + T * H * (DV * 2 + 4)
+        bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.6
+    elif name == "select_all_visible_kernel":
+        work = 4.0 * k * T
+        bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.6
+    else:
+        r = {"kernel": name, "avg_ms": round(ms_mean, 4), "median_ms": round(ms_median, 4)}
+        if items >= 0:
+            r["items"] = items
+        return r
+    rate = work / (ms_mean * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+    r = {"kernel": name, "bound": bound, "achieved": round(rate, 2), "peak": peak, "unit": unit,
+         "frac": round(rate / peak, 4), "target_frac": target, "avg_ms": round(ms_mean, 4),
+         "median_ms": round(ms_median, 4)}
+    if items >= 0:
+        r["items"] = items
+    r["algorithmic_flops" if bound == "mfma" else "algorithmic_bytes"] = float(work)
+    return r
+
+
+def fwd_bench(args, dsa, workload, steps, warmup):
+    """One fused-forward workload: K timed steps (wall clock, synchronised on
+    both sides), then per-kernel HIP-event times over --profile-reps calls of
+    the same entry, and the step's event median with and without an Infinity
+    Cache flush (a 512 MB write) before each call.  Returns the JSON object."""
+    import torch
     say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
-    say(f"[bench] workload {args.workload}: T={b.T} N={b.N} B={b.B} max_kv={b.max_kv}")
+    wl, entry = make_workload(workload)
+    b = wl.batch
+    say(f"[bench] workload {workload}: T={b.T} N={b.N} B={b.B} max_kv={b.max_kv}")
     t0 = time.time()
     dev = wl.device("cuda")
     torch.cuda.synchronize()
@@ -550,93 +707,89 @@ def main(argv=None):
     lse = torch.empty((b.T, H), dtype=torch.float32, device="cuda")
     idx = torch.empty((b.T, wl.k), dtype=torch.int32, device="cuda")
     ws_entry = dsa.WS_PREFILL if entry == "prefill" else dsa.WS_DECODE
-    ws = torch.empty(max(1, dsa.workspace_size(ws_entry, batch, wl.k)), dtype=torch.uint8,
-                     device="cuda")
+    ws_bytes = dsa.workspace_size(ws_entry, batch, wl.k)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
     fwd = dsa.prefill_fwd if entry == "prefill" else dsa.decode_fwd
+    stream = torch.cuda.current_stream()
 
     def step():
         fwd(fargs, batch, out, lse, idx, ws)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = b.T * args.steps / elapsed
-    say(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, {tokens_per_s:,.0f} tokens/s")
+    ms_per_step = elapsed * 1e3 / steps
+    tokens_per_s = b.T * steps / elapsed
+    say(f"[bench] {steps} steps: {ms_per_step:.4f} ms/step, {tokens_per_s:,.0f} tokens/s")
 
-    # ---- dominant kernel, timed alone with HIP events on its stream
+    # ---- per-kernel times: HIP events around each launch of the same entry, on its stream
+    reps = max(20, args.profile_reps)
+    per = {}
+    items = {}
+    order = []
+    step_ev = []
+    for _ in range(reps):
+        tl = dsa.fwd_profile(fargs, batch, out, lse, idx, ws, decode=(entry == "decode"), stream=stream)
+        step_ev.append(sum(ms for _, ms, _ in tl))
+        for kname, ms, it in tl:
+            if kname not in per:
+                per[kname] = []
+                order.append(kname)
+            per[kname].append(ms)
+            items[kname] = it
+    # the same, each call after a 512 MB write that evicts the Infinity Cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    step_cold = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        torch.cuda.synchronize()
+        tl = dsa.fwd_profile(fargs, batch, out, lse, idx, ws, decode=(entry == "decode"), stream=stream)
+        step_cold.append(sum(ms for _, ms, _ in tl))
+    del flush
     nvis = visible_counts(b.cu_q, b.cu_kv, b.pos0)
-    stream = torch.cuda.current_stream()
-    short = b.max_kv <= wl.k
-    if short:
-        # short-sequence mode: the attention kernel over every visible key
-        name = "sparse_mla_kernel"
-        flops = dense_mla_flops(nvis)
-        mws = torch.empty(max(1, dsa.workspace_size(dsa.WS_DENSE_MLA, batch, 1)),
-                          dtype=torch.uint8, device="cuda")
-        out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
-
-        def kernel():
-            dsa.dense_mla_fwd(batch, dev["q"], dev["kv"], wl.scale, out2, lse2, ws=mws)
-    elif entry == "prefill":
-        name = "sparse_mla_kernel"
-        flops = mla_flops(nvis, wl.k)
-        mws = torch.empty(max(1, dsa.workspace_size(dsa.WS_SPARSE_MLA, batch, wl.k)),
-                          dtype=torch.uint8, device="cuda")
-        out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
-
-        def kernel():
-            dsa.sparse_mla_fwd(batch, dev["q"], dev["kv"], idx, wl.scale, out2, lse2, ws=mws)
-    else:
-        name = "indexer_decode_kernel"
-        ld = ((b.max_kv + 63) // 64) * 64
-        scores = torch.empty((b.T, ld), dtype=torch.float32, device="cuda")
-        nbytes = indexer_bytes(nvis, b.N, b.T)
-
-        def kernel():
-            dsa.indexer_scores(batch, dev["qi"], dev["qs"], dev["w"], dev["ki"], dev["ks"], scores)
-    kernel()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.kernel_reps)]
-    for e0, e1 in evs:
-        e0.record(stream)
-        kernel()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-    traffic = measured_traffic(args.workload, name)
-    if entry == "prefill":
-        achieved = flops / (kms * 1e-3) / 1e12
-        roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "avg_ms": round(kms, 4), "algorithmic_flops": flops,
-                "algorithmic_bytes": mla_bytes(nvis, wl.k, b.T, b.N)}
-    else:
-        achieved = nbytes / (kms * 1e-3) / 1e9
-        roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": None, "avg_ms": round(kms, 4), "algorithmic_bytes": nbytes}
-    if traffic is not None:
-        roof["traffic"] = round(traffic["fetch"] + traffic["write"])
+    splits = 1
+    if entry == "decode" or b.T < 256:
+        # split-KV factor the library takes for few rows: one workgroup per compute unit
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        splits = 1 if b.T >= ncu else min(-(-ncu // b.T), -(-wl.k // 32))
+    kernels = [kernel_roof(kn, wl, entry, nvis, float(np.mean(per[kn])), float(np.median(per[kn])), splits,
+                           items.get(kn, -1))
+               for kn in order]
+    dom = max(kernels, key=lambda r: r["avg_ms"])
+    roof = dict(dom)
+    roof["traffic"] = None
+    tr = measured_traffic(workload, dom["kernel"])
+    if tr is not None:
+        roof["traffic"] = round(tr["fetch"] + tr["write"])
         roof["traffic_unit"] = "bytes/launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
-        roof["traffic_fetch"] = round(traffic["fetch"])
-        roof["traffic_write"] = round(traffic["write"])
-    say(f"[bench] {name}: {kms:.3f} ms/launch, {roof['achieved']} {roof['unit']} "
-        f"({100 * roof['frac']:.1f}% of peak)")
+        roof["traffic_fetch"], roof["traffic_write"] = round(tr["fetch"]), round(tr["write"])
+    roof["chosen_by"] = "largest mean HIP-event time among the step's kernels"
+    for r in kernels:
+        tgt = f", target {100 * r['target_frac']:.0f}%" if "frac" in r else ""
+        rate = f"{r['achieved']} {r['unit']} ({100 * r['frac']:.1f}% of peak{tgt})" if "frac" in r else ""
+        if "items" in r:
+            rate += f" [{r['items']} items]"
+        say(f"[bench]   {r['kernel']}: {r['avg_ms']:.4f} ms mean, {r['median_ms']:.4f} median  {rate}")
+    timing = {"events_reps": reps, "step_ms_median": round(float(np.median(step_ev)), 4),
+              "step_ms_median_mall_flushed": round(float(np.median(step_cold)), 4),
+              "note": "value uses the wall clock over the K steps; the medians are sums of the per-kernel "
+                      "HIP-event intervals of single calls (the flushed one writes 512 MB before each call)"}
+    say(f"[bench] event median per step {timing['step_ms_median']} ms, "
+        f"after a cache flush {timing['step_ms_median_mall_flushed']} ms")
 
     three = None
-    if short:
-        # the same forward through the three separate steps (indexer -> top-k ->
-        # sparse attention over the -1 padded selection), for comparison
+    if b.max_kv <= wl.k:
+        # short-sequence mode: the same forward through the three separate steps
+        # (indexer -> top-k -> sparse attention over the -1 padded selection)
         ld = ((b.max_kv + 63) // 64) * 64
         scores = torch.empty((b.T, ld), dtype=torch.float32, device="cuda")
         idx3 = torch.empty_like(idx)
+        out3, lse3 = torch.empty_like(out), torch.empty_like(lse)
         tws = torch.empty(max(1, dsa.workspace_size(dsa.WS_TOPK, batch, wl.k)), dtype=torch.uint8, device="cuda")
         sws = torch.empty(max(1, dsa.workspace_size(dsa.WS_SPARSE_MLA, batch, wl.k)), dtype=torch.uint8,
                           device="cuda")
@@ -644,16 +797,16 @@ def main(argv=None):
         def three_step():
             dsa.indexer_scores(batch, dev["qi"], dev["qs"], dev["w"], dev["ki"], dev["ks"], scores)
             dsa.topk(batch, scores, wl.k, idx3, ws=tws)
-            dsa.sparse_mla_fwd(batch, dev["q"], dev["kv"], idx3, wl.scale, out2, lse2, ws=sws)
+            dsa.sparse_mla_fwd(batch, dev["q"], dev["kv"], idx3, wl.scale, out3, lse3, ws=sws)
         three_step()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             three_step()
         e1.record(stream)
         torch.cuda.synchronize()
-        t3 = e0.elapsed_time(e1) / args.steps
+        t3 = e0.elapsed_time(e1) / steps
         three = {"three_step_ms": round(t3, 4), "short_mode_ms": round(ms_per_step, 4),
                  "speedup": round(t3 / ms_per_step, 3)}
         say(f"[bench] indexer -> top-k -> sparse attention on the same inputs: {t3:.3f} ms/step "
@@ -663,23 +816,24 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         say("[bench] timing the CPU oracle on a sample of the workload ...")
         cpu = cpu_baseline(wl, args.cpu_seconds)
-        say(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
+        cpu.update(cpu_info())
+        say(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} threads ({cpu['cpu_model']})")
 
-    cfg = {"workload": args.workload, "batch": b.B, "query_tokens": b.T, "cache_rows": b.N,
+    cfg = {"workload": workload, "batch": b.B, "query_tokens": b.T, "cache_rows": b.N,
            "max_context": b.max_kv, "topk": wl.k, "indexer_heads": HI, "indexer_dim": DI,
-           "heads": H, "d_qk": D, "d_v": DV, "entry": f"dsa_{entry}_fwd"}
-    if args.workload == "decode_64k":
+           "heads": H, "d_qk": D, "d_v": DV, "entry": f"dsa_{entry}_fwd", "workspace_bytes": ws_bytes}
+    if workload == "decode_64k":
         cfg["mean_context"] = round(float(np.mean(np.diff(b.cu_kv))), 1)
+    if b.max_kv <= wl.k:
+        cfg["entry"] += " (short-sequence mode: no indexer, no select)"
     line = {"metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "fp8+bf16", "data": "synthetic", "config": cfg, "roofline": roof,
-            "cpu_baseline": cpu}
+            "kernels": kernels, "timing": timing, "cpu_baseline": cpu}
     if three is not None:
-        cfg["entry"] += " (short-sequence mode: no indexer, no select)"
         line["short_mode"] = three
-    print(json.dumps(line), flush=True)
-    return 0
+    return line
 
 
 if __name__ == "__main__":

@@ -31,6 +31,8 @@
  *    OCP format, max 448); query heads H = 128 over D = 576 bf16 dims
  *    (512 latent + 64 rope), value = the first Dv = 512 dims; 1 <= k <= 2048.
  *    Anything else returns DSA_ERR_UNSUPPORTED.
+ *  * Every `scale` argument (the softmax scale of the attention) must be
+ *    finite and > 0, else DSA_ERR_INVALID_ARG.
  *  * Positions: score columns and idx entries are positions local to their
  *    sequence (0 = the sequence's first cache row).  Query row cu_q[b]+i sits
  *    at absolute position pos0[b]+i and sees the keys 0..min(pos, ctx_b-1)
@@ -97,6 +99,29 @@ dsa_status dsa_indexer_scores(const dsa_batch *batch,
  * when that size is 0. */
 dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld, int k,
                     int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/* Index scores and top-k selection in one call, with the scores kept on chip
+ * ([R] "Молниеносный индексатор" for I[t,s], "Отбор и основное внимание"
+ * for Top-k(I[t,:]) and its data flow: the cheap selection feeds the
+ * attention; the T x N score matrix is never written).  The result equals
+ * dsa_indexer_scores followed by dsa_topk on the same inputs, bit for bit:
+ * the same fp32 scores (same arithmetic), the same exact selection (k largest
+ * visible scores, -0 == +0, ties to the lower position, ascending, -1 padded).
+ * How: a strided sample of each row's keys sets a score threshold; the
+ * indexer keeps only the keys at or above it (with their positions) as
+ * candidates, and an exact select over them is checked to be complete (at
+ * least k candidates, no region overflow).  Rows that fail the check (rare:
+ * a threshold drawn too high, many equal scores) are recomputed on chip,
+ * 32768 columns at a time, still without writing scores.
+ *   inputs as dsa_indexer_scores; idx [T, k] int32 out.
+ * Workspace (required): dsa_workspace_size(DSA_WS_INDEXER_TOPK, ...): the
+ * candidate lists, about 8 bytes x min(8192, columns) per query row for
+ * prefill-shaped batches (max_q >= 16), 8 bytes per cached column for
+ * decode-shaped ones.  Supported: max_kv <= 262144, 1 <= k <= 2048. */
+dsa_status dsa_indexer_topk(const dsa_batch *batch,
+                            const uint8_t *q_fp8, const float *q_scale, const float *w,
+                            const uint8_t *k_fp8, const float *k_scale, int HI, int DI,
+                            int k, int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 
 /* Sparse attention in MLA's MQA mode, [R] "Отбор и основное внимание", eq. u,
  * and [N]: for each query row t and head h,
@@ -199,13 +224,14 @@ typedef struct {
     const uint16_t *q;       /* [T, H, D] bf16 */
     const uint16_t *kv;      /* [N, D] bf16 latent cache */
     int32_t HI, DI, H, D, Dv, k;
-    float scale;             /* softmax scale, e.g. 1/sqrt(D) */
+    float scale;             /* softmax scale, finite and > 0, e.g. 1/sqrt(D) */
 } dsa_fwd_args;
 
 /* The whole hot path in one call, following the data flow of [R]
  * "Отбор и основное внимание" (cheap selection first, then attention over the
- * k selected rows): index scores -> top-k -> sparse MQA attention.  Results
- * equal dsa_indexer_scores + dsa_topk + dsa_sparse_mla_fwd on the same inputs.
+ * k selected rows): index scores -> top-k -> sparse MQA attention, the first
+ * two as dsa_indexer_topk (no score matrix in memory).  Results equal
+ * dsa_indexer_scores + dsa_topk + dsa_sparse_mla_fwd on the same inputs.
  * dsa_prefill_fwd is tuned for many query rows per sequence (prefill, chunked
  * prefill); dsa_decode_fwd for one or a few query rows per sequence over long
  * contexts (split-KV).  Both accept any batch.
@@ -221,6 +247,27 @@ dsa_status dsa_prefill_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse,
                            int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 dsa_status dsa_decode_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse,
                           int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Measurement helper (not part of the hot path's data flow): runs the same
+ * launches as dsa_prefill_fwd (decode = 0) or dsa_decode_fwd (decode != 0)
+ * with a HIP event recorded on `stream` before the first launch and after
+ * each one, then WAITS for the last event (a host synchronisation, unlike
+ * every other entry point) and reports, per launch in order, the kernel's
+ * name and the time between its two events in ms (launch gaps included).
+ * Outputs, workspace and errors are those of the entry it runs; `times`
+ * [max_times] and `n_times` are host memory; kernel names are static
+ * strings.  Events are created and destroyed inside the call.  `items`
+ * counts what the library itself tallies for a kernel: for the fused
+ * select, the candidates it selected over (all rows); for the on-chip
+ * recompute, the rows it recomputed; -1 for the others. */
+typedef struct {
+    const char *kernel;
+    float ms;
+    int64_t items;
+} dsa_kernel_time;
+dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, float *lse,
+                           int32_t *idx_out, void *ws, size_t ws_bytes, void *stream,
+                           dsa_kernel_time *times, int max_times, int *n_times);
 
 /* FP8 quantisation of the indexer queries, the step before the index score
  * ([R] "Молниеносный индексатор": the indexer runs on FP8 values).  Per
@@ -257,7 +304,8 @@ typedef enum {
     DSA_WS_DECODE = 3,
     DSA_WS_DENSE_MLA = 4,      /* k is ignored (pass any 1..2048) */
     DSA_WS_INDEXER_KL = 5,
-    DSA_WS_SPARSE_MLA_BWD = 6
+    DSA_WS_SPARSE_MLA_BWD = 6,
+    DSA_WS_INDEXER_TOPK = 7     /* the layout depends on max_q (>= 16: prefill-shaped) */
 } dsa_ws_entry;
 
 /* Workspace bytes the given entry point needs for this batch (host only; reads

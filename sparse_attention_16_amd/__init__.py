@@ -7,8 +7,8 @@ memory and streams only.  Importing this package fails loudly when the built
 library is missing: there is no fallback implementation.
 
 Entry points (same names as the C ABI, without the ``dsa_`` prefix):
-    indexer_scores, topk, sparse_mla_fwd, dense_mla_fwd, indexer_kl_fwd, sparse_mla_bwd, prefill_fwd,
-    decode_fwd,
+    indexer_scores, indexer_topk, topk, sparse_mla_fwd, dense_mla_fwd, indexer_kl_fwd, sparse_mla_bwd, prefill_fwd,
+    decode_fwd, fwd_profile (measurement helper),
     quantize_queries, append_cache,
     workspace_size, status_string, version
 """
@@ -30,11 +30,12 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
-WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE, WS_DENSE_MLA, WS_INDEXER_KL, WS_SPARSE_MLA_BWD = range(7)
+(WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE, WS_DENSE_MLA, WS_INDEXER_KL, WS_SPARSE_MLA_BWD,
+ WS_INDEXER_TOPK) = range(8)
 
-EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_dense_mla_fwd", "dsa_indexer_kl_fwd",
+EXPORTS = ("dsa_indexer_scores", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_dense_mla_fwd", "dsa_indexer_kl_fwd",
            "dsa_sparse_mla_bwd", "dsa_prefill_fwd",
-           "dsa_decode_fwd", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
+           "dsa_decode_fwd", "dsa_fwd_profile", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
            "dsa_status_string", "dsa_version")
 
 
@@ -60,16 +61,23 @@ class dsa_fwd_args(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
+class dsa_kernel_time(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("ms", ctypes.c_float), ("items", ctypes.c_int64)]
+
+
 _P, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 _BP = ctypes.POINTER(dsa_batch)
 _lib.dsa_indexer_scores.argtypes = [_BP, _P, _P, _P, _P, _P, _I, _I, _P, _I64, _P]
 _lib.dsa_topk.argtypes = [_BP, _P, _I64, _I, _P, _P, _SZ, _P]
+_lib.dsa_indexer_topk.argtypes = [_BP, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _SZ, _P]
 _lib.dsa_sparse_mla_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
 _lib.dsa_dense_mla_fwd.argtypes = [_BP, _P, _P, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
 _lib.dsa_indexer_kl_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _F, _P, _I64, _P, _I, _P, _P, _P, _SZ, _P]
 _lib.dsa_sparse_mla_bwd.argtypes = [_BP, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_prefill_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_decode_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
+_lib.dsa_fwd_profile.argtypes = [ctypes.POINTER(dsa_fwd_args), _I, _P, _P, _P, _P, _SZ, _P,
+                                 ctypes.POINTER(dsa_kernel_time), _I, ctypes.POINTER(ctypes.c_int)]
 _lib.dsa_workspace_size.argtypes = [_I, _BP, _I, _I, _I]
 _lib.dsa_quantize_queries.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
 _lib.dsa_append_cache.argtypes = [_P, _P, _I64, _I, _I, _P, _P, _P, _P, _I64, _P]
@@ -77,8 +85,8 @@ _lib.dsa_workspace_size.restype = _SZ
 _lib.dsa_status_string.argtypes = [_I]
 _lib.dsa_status_string.restype = ctypes.c_char_p
 _lib.dsa_version.restype = ctypes.c_char_p
-for _name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_fwd",
-              "dsa_decode_fwd"):
+for _name in ("dsa_indexer_scores", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_fwd",
+              "dsa_decode_fwd", "dsa_fwd_profile"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -154,6 +162,17 @@ def indexer_scores(batch: Batch, q_fp8, q_scale, w, k_fp8, k_scale, scores, ld=N
                                  _ptr(scores), int(ld), _stream(stream))
     _check(st, "dsa_indexer_scores")
     return scores
+
+
+def indexer_topk(batch: Batch, q_fp8, q_scale, w, k_fp8, k_scale, k: int, idx, ws=None, stream=None):
+    """Top-k positions per row into ``idx`` [T, k] int32 straight from the
+    indexer inputs, without a score matrix (see dsa_indexer_topk)."""
+    ws, nbytes = _workspace(WS_INDEXER_TOPK, batch, k, ws, q_fp8.device)
+    st = _lib.dsa_indexer_topk(ctypes.byref(batch.c), _ptr(q_fp8), _ptr(q_scale), _ptr(w), _ptr(k_fp8),
+                               _ptr(k_scale), q_fp8.shape[1], q_fp8.shape[2], int(k), _ptr(idx), _ptr(ws), nbytes,
+                               _stream(stream))
+    _check(st, "dsa_indexer_topk")
+    return idx
 
 
 def quantize_queries(q, q_fp8, q_scale, stream=None):
@@ -261,6 +280,21 @@ def decode_fwd(args: dsa_fwd_args, batch: Batch, out, lse, idx_out=None, ws=None
     """Whole hot path (indexer -> top-k -> sparse MLA), decode-tuned (split-KV)."""
     return _fwd(_lib.dsa_decode_fwd, WS_DECODE, "dsa_decode_fwd", args, batch, out, lse,
                 idx_out, ws, stream)
+
+
+def fwd_profile(args: dsa_fwd_args, batch: Batch, out, lse, idx_out=None, ws=None, decode=False, stream=None):
+    """Runs the prefill (or decode) entry with a HIP event after each launch,
+    waits for it, and returns [(kernel name, ms, items)] in launch order (see
+    dsa_fwd_profile; items: candidates for the fused select, recomputed rows
+    for the recompute, else -1)."""
+    entry = WS_DECODE if decode else WS_PREFILL
+    ws, nbytes = _workspace(entry, batch, args.k, ws, out.device)
+    times = (dsa_kernel_time * 16)()
+    n = ctypes.c_int(0)
+    st = _lib.dsa_fwd_profile(ctypes.byref(args), int(bool(decode)), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws),
+                              nbytes, _stream(stream), times, 16, ctypes.byref(n))
+    _check(st, "dsa_fwd_profile")
+    return [(times[i].kernel.decode(), float(times[i].ms), int(times[i].items)) for i in range(n.value)]
 
 
 def raw_lib():

@@ -110,14 +110,57 @@ BwdWs bwd_layout(const dsa_batch *b, int k) {
 }
 size_t bwd_ws(const dsa_batch *b, int k) { return b->total_q > 0 ? bwd_layout(b, k).total : 0; }
 
-int64_t score_ld(int max_kv) { return ((int64_t)max_kv + 63) / 64 * 64; }
-
 // Slot budget of the dense attention: the longest context (at least 1).
 int dense_slots(const dsa_batch *b) { return b->max_kv < 1 ? 1 : b->max_kv; }
 
-size_t fwd_ws(const dsa_batch *b, int k) {
-    return up((size_t)b->total_q * score_ld(b->max_kv) * 4) + up((size_t)b->total_q * k * 4) +
-           topk_ws(b, k) + mla_ws(b, k);
+// Candidate regions of the fused indexer + select.  Region width: the decode
+// indexer's per-wave range (512 columns); for prefill, the widest power-of-two
+// key range per indexer workgroup (up to the whole row) that still gives at
+// least 8 workgroups per compute unit.  Slots per region: every column for
+// decode; at most 8192 for prefill (a row's candidates are ~1.3k..2.5k when
+// the sampled threshold is right; more overflow, and the row is recomputed
+// on chip).  A row's area also holds the recompute's per-chunk candidates,
+// k per 32768 columns.
+struct CandLayout {
+    int seg_w = 0, nseg = 0, cap = 0;
+    size_t tau = 0, cnt = 0, key = 0, pos = 0, fb = 0, total = 0;
+};
+CandLayout cand_layout(const dsa_batch *b, int k, bool decode) {
+    CandLayout c;
+    if (decode) {
+        c.seg_w = CAND_DECODE_SEG;
+    } else {
+        const int64_t rowblocks = (int64_t)((b->max_q + 15) / 16) * b->batch;
+        int full = 2048;
+        while (full < b->max_kv) full <<= 1;
+        c.seg_w = 2048;
+        for (int w = full; w > 2048; w >>= 1)
+            if (rowblocks * ((b->max_kv + w - 1) / w) >= 8LL * device_cus()) {
+                c.seg_w = w;
+                break;
+            }
+    }
+    c.nseg = b->max_kv <= 0 ? 1 : (b->max_kv + c.seg_w - 1) / c.seg_w;
+    c.cap = decode ? CAND_DECODE_SEG : (c.seg_w < CAND_CAP ? c.seg_w : CAND_CAP);
+    const int64_t need = (int64_t)k * topk_chunks(b->max_kv);
+    if ((int64_t)c.nseg * c.cap < need) c.cap = (int)((need + c.nseg - 1) / c.nseg);
+    const size_t T = (size_t)b->total_q, slots = T * c.nseg * c.cap;
+    c.tau = 0;
+    c.cnt = c.tau + up(T * 4);
+    c.key = c.cnt + up(T * c.nseg * 4);
+    c.pos = c.key + up(slots * 4);
+    c.fb = c.pos + up(slots * 4);
+    c.total = c.fb + up((FB_LIST + T) * 4);
+    return c;
+}
+
+size_t idxtopk_ws(const dsa_batch *b, int k, bool decode) { return b->total_q > 0 ? cand_layout(b, k, decode).total : 0; }
+
+// Fused entries: candidates (none for short sequences, which skip the select),
+// the selection when the caller does not take it, split-KV partials.
+size_t fwd_cand_ws(const dsa_batch *b, int k, bool decode) { return b->max_kv <= k ? 0 : idxtopk_ws(b, k, decode); }
+size_t fwd_ws(const dsa_batch *b, int k, bool decode) {
+    return fwd_cand_ws(b, k, decode) + up((size_t)b->total_q * k * 4) + mla_ws(b, k);
 }
 
 // Keys per indexer workgroup.  Prefill takes the widest chunk of 8192, 4096
@@ -151,7 +194,34 @@ IndexerParams make_indexer(const dsa_batch *b, const uint8_t *q, const float *qs
     p.ld = ld;
     p.key_chunk = chunk;
     p.fill_masked = fill;
+    p.tau = nullptr;
+    p.cand_key = nullptr;
+    p.cand_pos = nullptr;
+    p.cand_cnt = nullptr;
+    p.seg_w = p.nseg = p.cap = p.topk_k = 0;
     return p;
+}
+
+// The fused indexer + select over the candidate layout at ws.
+IdxTopkParams make_idxtopk(const dsa_batch *b, const uint8_t *q, const float *qs, const float *w, const uint8_t *kk,
+                           const float *ks, int k, int32_t *idx, void *ws, bool decode) {
+    const CandLayout c = cand_layout(b, k, decode);
+    char *base = static_cast<char *>(ws);
+    IdxTopkParams tp;
+    tp.ix = make_indexer(b, q, qs, w, kk, ks, nullptr, 0, decode ? 4 * CAND_DECODE_SEG : c.seg_w, 0);
+    tp.tau = reinterpret_cast<uint32_t *>(base + c.tau);
+    tp.ix.tau = tp.tau;
+    tp.ix.cand_cnt = reinterpret_cast<int32_t *>(base + c.cnt);
+    tp.ix.cand_key = reinterpret_cast<uint32_t *>(base + c.key);
+    tp.ix.cand_pos = reinterpret_cast<int32_t *>(base + c.pos);
+    tp.ix.seg_w = c.seg_w;
+    tp.ix.nseg = c.nseg;
+    tp.ix.cap = c.cap;
+    tp.ix.topk_k = k;
+    tp.k = k;
+    tp.idx = idx;
+    tp.fb = reinterpret_cast<int32_t *>(base + c.fb);
+    return tp;
 }
 
 TopkParams make_topk(const dsa_batch *b, const float *scores, int64_t ld, int k, int32_t *idx,
@@ -206,13 +276,35 @@ MlaParams make_mla(const dsa_batch *b, const uint16_t *q, const uint16_t *kv, co
 
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+// Per-launch timing of the fused entries: an event is recorded on the stream
+// before the first launch and after each one, so consecutive events bracket
+// one kernel each (the profiling entry point passes one; null elsewhere).
+struct Timeline final : LaunchMarks {
+    static constexpr int kMax = 16;
+    hipEvent_t ev[kMax + 1] = {};
+    const char *name[kMax] = {};
+    int n = 0;        // kernels recorded
+    bool ok = true;   // every event recorded
+    void after(const char *kernel, hipStream_t s) override {
+        if (n >= kMax) return;
+        name[n] = kernel;
+        if (hipEventRecord(ev[n + 1], s) != hipSuccess) ok = false;
+        ++n;
+    }
+};
+
+// Softmax scales must be positive and finite: the attention kernels take the
+// maximum of the scaled logits as the maximum of the raw ones, and a masked
+// slot's -inf logit times a scale <= 0 is NaN or +inf.
+bool valid_scale(float scale) { return std::isfinite(scale) && scale > 0.f; }
+
 dsa_status check_k(int k) {
     if (k < 1 || k > kKMax) return DSA_ERR_UNSUPPORTED;
     return DSA_OK;
 }
 
 dsa_status run_fwd(const dsa_fwd_args *a, uint16_t *out, float *lse, int32_t *idx_out, void *ws,
-                   size_t ws_bytes, void *stream, bool decode) {
+                   size_t ws_bytes, void *stream, bool decode, Timeline *tl = nullptr) {
     if (!a) return DSA_ERR_INVALID_ARG;
     dsa_status st = check_batch(&a->batch);
     if (st != DSA_OK) return st;
@@ -220,7 +312,7 @@ dsa_status run_fwd(const dsa_fwd_args *a, uint16_t *out, float *lse, int32_t *id
         return DSA_ERR_UNSUPPORTED;
     if ((st = check_k(a->k)) != DSA_OK) return st;
     if (a->batch.max_kv > kMaxKvTopk) return DSA_ERR_UNSUPPORTED;
-    if (!std::isfinite(a->scale)) return DSA_ERR_INVALID_ARG;
+    if (!valid_scale(a->scale)) return DSA_ERR_INVALID_ARG;
     const dsa_batch *b = &a->batch;
     if (b->total_q == 0) return DSA_OK;
     if (!a->q_fp8 || !a->q_scale || !a->w || !a->q || !out || !lse) return DSA_ERR_INVALID_ARG;
@@ -231,19 +323,16 @@ dsa_status run_fwd(const dsa_fwd_args *a, uint16_t *out, float *lse, int32_t *id
     if (b->total_kv > 0 && (!al16(a->k_fp8) || !al16(a->k_scale) || !al16(a->kv)))
         return DSA_ERR_INVALID_ARG;
     if (idx_out && !al16(idx_out)) return DSA_ERR_INVALID_ARG;
-    const size_t need = fwd_ws(b, a->k);
+    const size_t need = fwd_ws(b, a->k, decode);
     if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t ld = score_ld(b->max_kv);
     char *w = static_cast<char *>(ws);
-    float *scores = reinterpret_cast<float *>(w);
-    w += up((size_t)b->total_q * ld * 4);
+    void *cws = w;
+    w += fwd_cand_ws(b, a->k, decode);
     int32_t *idx = reinterpret_cast<int32_t *>(w);
     w += up((size_t)b->total_q * a->k * 4);
     if (idx_out) idx = idx_out;
-    void *tws = w;
-    w += topk_ws(b, a->k);
     void *mws = w;
 
     // Short sequences (every context within k): the select keeps every visible
@@ -254,21 +343,17 @@ dsa_status run_fwd(const dsa_fwd_args *a, uint16_t *out, float *lse, int32_t *id
         if (idx_out) {
             TopkParams tp = make_topk(b, nullptr, 0, a->k, idx_out, nullptr);
             if ((st = hip_status(launch_select_all_visible(tp, b->total_q, s))) != DSA_OK) return st;
+            if (tl) tl->after("select_all_visible_kernel", s);
         }
         MlaParams mp = make_mla(b, a->q, a->kv, nullptr, a->k, a->scale, out, lse, mws, 1);
-        return hip_status(launch_sparse_mla(mp, b->total_q, s));
+        return hip_status(launch_sparse_mla(mp, b->total_q, s, tl));
     }
 
-    if (b->max_kv > 0) {
-        IndexerParams ip = make_indexer(b, a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, scores,
-                                        ld, indexer_chunk(b, decode), 0);
-        if ((st = hip_status(launch_indexer(ip, b->total_q, b->max_q, decode, s))) != DSA_OK)
-            return st;
-    }
-    TopkParams tp = make_topk(b, scores, ld, a->k, idx, tws);
-    if ((st = hip_status(launch_topk(tp, b->total_q, s))) != DSA_OK) return st;
+    // indexer -> top-k with the scores kept on chip (candidates only)
+    IdxTopkParams tp = make_idxtopk(b, a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, a->k, idx, cws, decode);
+    if ((st = hip_status(launch_indexer_topk(tp, b->total_q, b->max_q, decode, s, tl))) != DSA_OK) return st;
     MlaParams mp = make_mla(b, a->q, a->kv, idx, a->k, a->scale, out, lse, mws);
-    return hip_status(launch_sparse_mla(mp, b->total_q, s));
+    return hip_status(launch_sparse_mla(mp, b->total_q, s, tl));
 }
 
 }  // namespace
@@ -337,6 +422,28 @@ dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld, int
     return hip_status(launch_topk(p, batch->total_q, static_cast<hipStream_t>(stream)));
 }
 
+dsa_status dsa_indexer_topk(const dsa_batch *batch, const uint8_t *q_fp8, const float *q_scale, const float *w,
+                            const uint8_t *k_fp8, const float *k_scale, int HI, int DI, int k, int32_t *idx, void *ws,
+                            size_t ws_bytes, void *stream) {
+    dsa_status st = check_batch(batch);
+    if (st != DSA_OK) return st;
+    if (HI != kHI || DI != kDI) return DSA_ERR_UNSUPPORTED;
+    if ((st = check_k(k)) != DSA_OK) return st;
+    if (batch->max_kv > kMaxKvTopk) return DSA_ERR_UNSUPPORTED;
+    if (batch->total_q == 0) return DSA_OK;
+    if (!q_fp8 || !q_scale || !w || !idx) return DSA_ERR_INVALID_ARG;
+    if (batch->total_kv > 0 && (!k_fp8 || !k_scale)) return DSA_ERR_INVALID_ARG;
+    const void *ptrs[] = {q_fp8, q_scale, w, idx};
+    for (const void *p : ptrs)
+        if (!al16(p)) return DSA_ERR_INVALID_ARG;
+    if (batch->total_kv > 0 && (!al16(k_fp8) || !al16(k_scale))) return DSA_ERR_INVALID_ARG;
+    const bool decode = batch->max_q < 16;
+    const size_t need = idxtopk_ws(batch, k, decode);
+    if (!ws || ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
+    IdxTopkParams tp = make_idxtopk(batch, q_fp8, q_scale, w, k_fp8, k_scale, k, idx, ws, decode);
+    return hip_status(launch_indexer_topk(tp, batch->total_q, batch->max_q, decode, static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv,
                               const int32_t *idx, int k, int H, int D, int Dv, float scale,
                               uint16_t *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
@@ -345,7 +452,7 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const uint16_t *q, const u
     if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
     if ((st = check_k(k)) != DSA_OK) return st;
     if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
-    if (!std::isfinite(scale)) return DSA_ERR_INVALID_ARG;
+    if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
     if (batch->total_q == 0) return DSA_OK;
     if (!q || !idx || !out || !lse) return DSA_ERR_INVALID_ARG;
     if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
@@ -364,7 +471,7 @@ dsa_status dsa_dense_mla_fwd(const dsa_batch *batch, const uint16_t *q, const ui
     if (st != DSA_OK) return st;
     if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
     if (batch->max_kv > kKMax) return DSA_ERR_UNSUPPORTED;
-    if (!std::isfinite(scale)) return DSA_ERR_INVALID_ARG;
+    if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
     if (batch->total_q == 0) return DSA_OK;
     if (!q || !out || !lse) return DSA_ERR_INVALID_ARG;
     if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
@@ -384,7 +491,7 @@ dsa_status dsa_indexer_kl_fwd(const dsa_batch *batch, const uint16_t *q, const u
     if (H != kH || D != kD) return DSA_ERR_UNSUPPORTED;
     if (idx && (st = check_k(k)) != DSA_OK) return st;
     if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
-    if (!std::isfinite(scale)) return DSA_ERR_INVALID_ARG;
+    if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
     if (batch->total_q == 0) return DSA_OK;
     if (!q || !lse || !scores || !kl) return DSA_ERR_INVALID_ARG;
     if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
@@ -429,7 +536,7 @@ dsa_status dsa_sparse_mla_bwd(const dsa_batch *batch, const uint16_t *q, const u
     if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
     if ((st = check_k(k)) != DSA_OK) return st;
     if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
-    if (!std::isfinite(scale)) return DSA_ERR_INVALID_ARG;
+    if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
     if (batch->total_q == 0 && batch->total_kv == 0) return DSA_OK;
     if (batch->total_kv > 0 && (!kv || !dkv)) return DSA_ERR_INVALID_ARG;
     if (batch->total_q > 0 && (!q || !idx || !out || !lse || !dout || !dq)) return DSA_ERR_INVALID_ARG;
@@ -481,6 +588,47 @@ dsa_status dsa_decode_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse, i
     return run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, true);
 }
 
+dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, float *lse, int32_t *idx_out,
+                           void *ws, size_t ws_bytes, void *stream, dsa_kernel_time *times, int max_times,
+                           int *n_times) {
+    if (!times || !n_times || max_times < 1) return DSA_ERR_INVALID_ARG;
+    *n_times = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Timeline tl;
+    int made = 0;
+    dsa_status st = DSA_OK;
+    for (; made <= Timeline::kMax; ++made)
+        if (hipEventCreate(&tl.ev[made]) != hipSuccess) {
+            st = DSA_ERR_HIP;
+            break;
+        }
+    if (st == DSA_OK && hipEventRecord(tl.ev[0], s) != hipSuccess) st = DSA_ERR_HIP;
+    if (st == DSA_OK) st = run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, decode != 0, &tl);
+    if (st == DSA_OK && tl.n > 0) {
+        if (!tl.ok || hipEventSynchronize(tl.ev[tl.n]) != hipSuccess) st = DSA_ERR_HIP;
+        // the fused select's counts: queued rows and candidates (its queue header)
+        int32_t fb[3] = {-1, -1, -1};
+        const dsa_batch *b = &args->batch;
+        if (st == DSA_OK && b->max_kv > args->k && b->total_q > 0) {
+            const CandLayout c = cand_layout(b, args->k, decode != 0);
+            if (hipMemcpy(fb, static_cast<char *>(ws) + c.fb, sizeof(fb), hipMemcpyDeviceToHost) != hipSuccess)
+                st = DSA_ERR_HIP;
+        }
+        for (int i = 0; st == DSA_OK && i < tl.n && i < max_times; ++i) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, tl.ev[i], tl.ev[i + 1]) != hipSuccess) st = DSA_ERR_HIP;
+            times[i].kernel = tl.name[i];
+            times[i].ms = ms;
+            times[i].items = -1;
+            if (std::strcmp(tl.name[i], "cand_select_kernel") == 0) times[i].items = fb[2];
+            if (std::strcmp(tl.name[i], "idx_fallback_kernel") == 0) times[i].items = fb[0];
+            *n_times = i + 1;
+        }
+    }
+    for (int i = 0; i < made; ++i) (void)hipEventDestroy(tl.ev[i]);
+    return st;
+}
+
 size_t dsa_workspace_size(dsa_ws_entry entry, const dsa_batch *batch, int k, int H, int Dv) {
     if (!batch || batch->batch < 1 || batch->total_q < 0 || batch->max_kv < 0 || k < 1 ||
         k > kKMax || H != kH || Dv != kDv)
@@ -488,8 +636,10 @@ size_t dsa_workspace_size(dsa_ws_entry entry, const dsa_batch *batch, int k, int
     switch (entry) {
         case DSA_WS_TOPK: return topk_ws(batch, k);
         case DSA_WS_SPARSE_MLA: return mla_ws(batch, k);
-        case DSA_WS_PREFILL:
-        case DSA_WS_DECODE: return fwd_ws(batch, k);
+        case DSA_WS_PREFILL: return fwd_ws(batch, k, false);
+        case DSA_WS_DECODE: return fwd_ws(batch, k, true);
+        case DSA_WS_INDEXER_TOPK:
+            return batch->max_kv > kMaxKvTopk ? 0 : idxtopk_ws(batch, k, batch->max_q < 16);
         case DSA_WS_DENSE_MLA: return batch->max_kv > kKMax ? 0 : mla_ws(batch, dense_slots(batch));
         case DSA_WS_INDEXER_KL: return batch->max_kv > MAX_KV_ATTN ? 0 : kl_ws(batch, k);
         case DSA_WS_SPARSE_MLA_BWD: return batch->max_kv > MAX_KV_ATTN ? 0 : bwd_ws(batch, k);

@@ -16,71 +16,10 @@
 // four 16-key blocks at once with two rounds of VALU lane swaps (a reduce-
 // scatter that leaves key l of the 64 in lane l).  Only the final fp32 score
 // leaves the registers.
-#include "dsa_device.h"
-#include "kernels.h"
+#include "indexer_core.h"
 
 namespace dsa {
 
-namespace {
-
-constexpr int HI = 64;
-constexpr int DI = 128;
-constexpr int ROW_BYTES = HI * DI;  // one query row of FP8 indexer queries
-
-// Loads the A operands (4 head groups) and folded weights of one query row.
-// Branch-free: an invalid row reads row t anyway (the caller passes a valid
-// row index) and gets zero weights, so its scores are zero.
-__device__ __forceinline__ void load_query(const IndexerParams &p, int64_t t, bool valid,
-                                           i32x8 (&qa)[4], float (&wq)[4][4]) {
-    const int l = lane_id();
-    const int row = l & 15, grp = l >> 4;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const uint8_t *src = p.q + t * ROW_BYTES + (16 * m + row) * DI + 32 * grp;
-        const i32x4 *s4 = reinterpret_cast<const i32x4 *>(src);
-        const i32x4 lo = s4[0], hi = s4[1];
-        qa[m] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = 16 * m + 4 * grp + i;
-            wq[m][i] = (valid ? 1.0f : 0.0f) * (p.w[t * HI + j] * p.q_scale[t * HI + j]);
-        }
-    }
-}
-
-// The 16 head partials of one lane for one 16-key block: 4 MFMAs (one per
-// group of 16 heads), kept in separate accumulators so that they can be in
-// flight while the previous block's epilogue runs.
-__device__ __forceinline__ void block_mfma(const i32x8 (&qa)[4], const i32x8 &kb, f32x4 (&c)[4]) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) c[m] = mfma_f8_16x16x128(qa[m], kb, zero);
-}
-
-// ReLU + weighted sum over this lane's 16 heads (4 per MFMA tile).
-__device__ __forceinline__ float block_epilogue(const f32x4 (&c)[4], const float (&wq)[4][4]) {
-    float part = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part = fmaf(wq[m][i], fmaxf(c[m][i], 0.f), part);
-    return part;
-}
-
-// Sum over the four 16-lane groups of four 16-key blocks at once: p[b] holds,
-// in lane l, the partial (over the heads of group l/16) of key 16*b + l%16.
-// Returns, in lane l, the total of key l of the 64-key group.  Two exchanges
-// of the lane halves, then of the 16-lane rows (VALU lane swaps, no LDS).
-__device__ __forceinline__ float reduce_scatter4(const float (&p)[4]) {
-    const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
-    const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
-    const float a = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);   // blocks 0 | 2, halves summed
-    const float b = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);   // blocks 1 | 3
-    const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(y[0]) + __uint_as_float(y[1]);
-}
-
-}  // namespace
 
 // ---------------------------------------------------------------------------
 // Prefill variant: one workgroup = 16 consecutive query rows of one sequence
@@ -88,11 +27,19 @@ __device__ __forceinline__ float reduce_scatter4(const float (&p)[4]) {
 // once per workgroup in LDS (row pitch 144 B so that the 16 rows read by one
 // B operand land on disjoint banks) and shared by all 16 query rows.
 // Grid: x = row block, y = key chunk, z = sequence.
+//
+// Candidate mode (CAND): the score is not stored; a visible key whose score
+// is >= the row's threshold is appended, in column order, to the row's
+// candidate region of this key chunk (the region's running count is wave-
+// uniform: one ballot and one mbcnt per 64 keys), and the region's count is
+// written at the end.  Row blocks run longest first (causal rows grow with
+// the block index), so the short blocks fill the tail.
 // ---------------------------------------------------------------------------
 constexpr int PF_ROWS = 16;
 constexpr int PF_KT = 128;
 constexpr int PF_PITCH = 144;
 
+template <bool CAND>
 __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t ktile[PF_KT * PF_PITCH];
     __shared__ float kscale[PF_KT];
@@ -100,7 +47,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
     const int b = blockIdx.z;
     const int q0 = p.cu_q[b];
     const int nq = p.cu_q[b + 1] - q0;
-    const int tb = blockIdx.x * PF_ROWS;
+    const int tb = (CAND ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x) * PF_ROWS;
     if (tb >= nq) return;
     int64_t kv0 = p.cu_kv[b], kv1 = p.cu_kv[b + 1];
     kv0 = kv0 < 0 ? 0 : (kv0 > p.total_kv ? p.total_kv : kv0);
@@ -113,8 +60,9 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
     const int c0 = blockIdx.y * p.key_chunk;
     const int c_end = c0 + p.key_chunk;
     const int comp_end = c_end < vis_max ? c_end : vis_max;      // keys needing the MFMA
-    const int fill_end = p.fill_masked ? (c_end < ctx ? c_end : ctx) : comp_end;
+    const int fill_end = (!CAND && p.fill_masked) ? (c_end < ctx ? c_end : ctx) : comp_end;
     if (c0 >= fill_end) return;
+    if (CAND && vis_max <= p.topk_k) return;   // every row of the block selects all it sees
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -125,12 +73,20 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
     float wq[2][4][4];
     int pos[2];
     bool valid[2];
+    float thr[2];        // candidate mode: the rows' score thresholds
+    int cnt[2] = {0, 0};  // candidate mode: candidates found so far (wave-uniform)
+    int64_t rbase[2];    // candidate mode: first slot of the rows' regions
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int tl = tb + 2 * wave + r;
         valid[r] = tl < nq;
         pos[r] = p.pos0[b] + tl;
         load_query(p, (int64_t)(q0 + (valid[r] ? tl : tb)), valid[r], qa[r], wq[r]);
+        if constexpr (CAND) {
+            const int64_t t = q0 + (valid[r] ? tl : tb);
+            thr[r] = threshold_value(p.tau[t]);
+            rbase[r] = (t * p.nseg + blockIdx.y) * (int64_t)p.cap;
+        }
     }
 
     // register staging of the next key tile: 1024 16-byte chunks over 512 threads
@@ -202,15 +158,27 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const float v = reduce_scatter4(part[r]);
-                    if (valid[r] && key < fill_end)
+                    if constexpr (CAND) {
+                        const float sc = v * ks;
+                        const bool c = valid[r] && key <= pos[r] && key < comp_end && sc >= thr[r];
+                        emit_candidate(p, c, sc, key, rbase[r], cnt[r]);
+                    } else if (valid[r] && key < fill_end) {
                         p.scores[(int64_t)(q0 + tb + 2 * wave + r) * p.ld + key] =
                             key <= pos[r] && key < comp_end ? v * ks : -INFINITY;
+                    }
                 }
             }
             // one pipeline stage per region: left free, the scheduler hoists
             // every block's MFMAs to the front and runs out of registers
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+
+    if constexpr (CAND) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            if (valid[r] && l == 0) p.cand_cnt[(int64_t)(q0 + tb + 2 * wave + r) * p.nseg + blockIdx.y] = cnt[r];
+        return;
     }
 
     // keys of this chunk that no row of the block can see: -inf when requested
@@ -244,27 +212,11 @@ constexpr int DC_NBUF = 1;
 constexpr int DC_GROUP = 64 * DI;           // bytes of one 64-key group
 constexpr int DC_LOADS = 9;                 // loads per group: 8 x 1 KB of keys + the scales
 
-// Direct-to-LDS loads (16 or 4 bytes per lane) from sbase + voff (scalar base,
-// 32-bit lane offset) to LDS lds + size * lane.  Issued from asm: the
-// compiler's wait insertion does not track them; the kernel waits with
-// explicit vmcnt.  M0 must be written one instruction ahead of the load.
-__device__ __forceinline__ void dma_b128(uint64_t sbase, uint32_t voff, const DSA_LDS void *lds) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-                 : "m0");
-}
-__device__ __forceinline__ void dma_b32(uint64_t sbase, uint32_t voff, const DSA_LDS void *lds) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-                 : "m0");
-}
-// A wave-uniform 64-bit pointer value in scalar registers.  (readfirstlane
-// returns int: widen through uint32_t, or the low word is sign-extended.)
-__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
-    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
-           (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-}
-
+// Candidate mode (CAND): wave w takes the contiguous 512 columns
+// [c0 + 512w, c0 + 512w + 512) instead of every fourth group, so that its
+// candidates (the visible keys whose score is >= the row's threshold) fill
+// one region in column order; the region holds all of them (cap 512).
+template <bool CAND>
 __global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t kst[DC_WAVES][DC_NBUF][DC_GROUP];
     __shared__ __attribute__((aligned(16))) float sst[DC_WAVES][DC_NBUF][64];
@@ -273,8 +225,9 @@ __global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerPa
     const int c0 = blockIdx.y * p.key_chunk;
     const int c_end = c0 + p.key_chunk;
     const int comp_end = c_end < ri.nvis ? c_end : ri.nvis;
-    const int fill_end = p.fill_masked ? (c_end < ri.ctx ? c_end : ri.ctx) : comp_end;
+    const int fill_end = (!CAND && p.fill_masked) ? (c_end < ri.ctx ? c_end : ri.ctx) : comp_end;
     if (c0 >= fill_end) return;
+    if (CAND && ri.nvis <= p.topk_k) return;   // the row selects every key it sees
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = lane_id();
@@ -282,6 +235,18 @@ __global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerPa
     float wq[4][4];
     load_query(p, t, true, qa, wq);
 
+    // this wave's groups: g0 = gstart, gstart + STRIDE, ... below gend
+    const int STRIDE = CAND ? 64 : 64 * DC_WAVES;
+    const int gstart = CAND ? c0 + CAND_DECODE_SEG * wave : c0 + 64 * wave;
+    const int gend = CAND ? (gstart + CAND_DECODE_SEG < fill_end ? gstart + CAND_DECODE_SEG : fill_end) : fill_end;
+    float thr = 0.f;
+    int cnt = 0;
+    int64_t rbase = 0;
+    const int seg = gstart / CAND_DECODE_SEG;
+    if constexpr (CAND) {
+        thr = threshold_value(p.tau[t]);
+        rbase = ((int64_t)t * p.nseg + seg) * p.cap;
+    }
     const int row = l & 15, grp = l >> 4;
     const uint64_t kbase = uniform_u64((uint64_t)(uintptr_t)(p.k + ri.kv0 * DI));
     const uint64_t sbase = uniform_u64((uint64_t)(uintptr_t)(p.k_scale + ri.kv0));
@@ -315,18 +280,22 @@ __global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerPa
         const float v = reduce_scatter4(part);
         const float ks = sst[wave][b][l];
         const int key = g0 + l;
-        if (key < fill_end) p.scores[(int64_t)t * p.ld + key] = key < comp_end ? v * ks : -INFINITY;
+        if constexpr (CAND) {
+            const float sc = v * ks;
+            emit_candidate(p, key < comp_end && sc >= thr, sc, key, rbase, cnt);
+        } else if (key < fill_end) {
+            p.scores[(int64_t)t * p.ld + key] = key < comp_end ? v * ks : -INFINITY;
+        }
     };
-    constexpr int STRIDE = 64 * DC_WAVES;
-    int g0 = c0 + 64 * wave;
+    int g0 = gstart;
 #pragma unroll
     for (int j = 0; j < DC_NBUF; ++j)
-        if (g0 + j * STRIDE < fill_end) issue(g0 + j * STRIDE, j);
-    for (int i = 0; g0 < fill_end; g0 += STRIDE, ++i) {
+        if (g0 + j * STRIDE < gend) issue(g0 + j * STRIDE, j);
+    for (int i = 0; g0 < gend; g0 += STRIDE, ++i) {
         // wait for this group's loads; the later groups' loads (at most
         // DC_NBUF - 1 groups, issued after this one) may still fly
         static_assert(DC_NBUF >= 1 && DC_NBUF <= 3, "vmcnt waits written for a ring of 1 to 3 groups");
-        const int ahead = (fill_end - 1 - g0) / STRIDE;   // groups after this one
+        const int ahead = (gend - 1 - g0) / STRIDE;   // groups after this one
         const int fly = ahead < DC_NBUF - 1 ? ahead : DC_NBUF - 1;   // of them already issued
         if (fly >= 2)
             __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DC_LOADS - 16) | (1 << 14));   // vmcnt(2 * DC_LOADS) = 18
@@ -336,7 +305,10 @@ __global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerPa
             __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
         const int b = i % DC_NBUF;
         compute(g0, b);
-        if (g0 + DC_NBUF * STRIDE < fill_end) issue(g0 + DC_NBUF * STRIDE, b);
+        if (g0 + DC_NBUF * STRIDE < gend) issue(g0 + DC_NBUF * STRIDE, b);
+    }
+    if constexpr (CAND) {
+        if (l == 0 && seg < p.nseg) p.cand_cnt[(int64_t)t * p.nseg + seg] = cnt;
     }
 }
 
@@ -345,10 +317,25 @@ hipError_t launch_indexer(const IndexerParams &p, int T, int max_q, bool decode_
     if (T <= 0 || p.max_kv <= 0) return hipSuccess;
     const int nchunk = (p.max_kv + p.key_chunk - 1) / p.key_chunk;
     if (decode_variant) {
-        hipLaunchKernelGGL(indexer_decode_kernel, dim3(T, nchunk), dim3(64 * DC_WAVES), 0, s, p);
+        hipLaunchKernelGGL(indexer_decode_kernel<false>, dim3(T, nchunk), dim3(64 * DC_WAVES), 0, s, p);
     } else {
         const dim3 g((max_q + PF_ROWS - 1) / PF_ROWS, nchunk, p.B);
-        hipLaunchKernelGGL(indexer_prefill_kernel, g, dim3(512), 0, s, p);
+        hipLaunchKernelGGL(indexer_prefill_kernel<false>, g, dim3(512), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer_cand(const IndexerParams &p, int T, int max_q, bool decode_variant, hipStream_t s) {
+    if (T <= 0 || p.max_kv <= 0) return hipSuccess;
+    const int nchunk = (p.max_kv + p.key_chunk - 1) / p.key_chunk;
+    if (decode_variant) {
+        if (p.key_chunk != DC_WAVES * CAND_DECODE_SEG || p.seg_w != CAND_DECODE_SEG || p.cap < CAND_DECODE_SEG)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(indexer_decode_kernel<true>, dim3(T, nchunk), dim3(64 * DC_WAVES), 0, s, p);
+    } else {
+        if (p.seg_w != p.key_chunk || p.nseg != nchunk) return hipErrorInvalidValue;
+        const dim3 g((max_q + PF_ROWS - 1) / PF_ROWS, nchunk, p.B);
+        hipLaunchKernelGGL(indexer_prefill_kernel<true>, g, dim3(512), 0, s, p);
     }
     return hipGetLastError();
 }

@@ -1,0 +1,449 @@
+// indexer_topk.hip — the fused indexer + top-k select of the DSA hot path:
+// the index scores of a query row are never written to HBM.
+//
+// Page "Техотчёт DeepSeek-V3.2 (2025): разреженное внимание DSA и
+// масштабирование RL": section "Молниеносный индексатор" defines the score
+// I[t,s] (computed here by the same FP8 matrix-core code as indexer.hip, so the
+// values are bit-identical), section "Отбор и основное внимание" the selection
+// Top-k(I[t,:]) that feeds the attention (the k largest scores of the row,
+// ties to the lower position; every visible key when there are at most k).
+//
+// An exact top-k of a row is only known once every score of the row is, so
+// the kernels keep each row's *candidates* instead of its scores:
+//   1. indexer_sample_kernel: the scores of an evenly strided sample of the
+//      row's keys (512..1024 of them), and from them a threshold tau[t]: the
+//      r-th largest sample score, with r = mu + 5 sqrt(mu) + 1 for the mu =
+//      k * m / n sampled keys expected above the row's k-th largest score.
+//      Rows that see at most 4096 keys get no threshold (every visible key).
+//   2. the indexer in candidate mode (indexer.hip): every visible key with
+//      score >= tau[t] goes, in column order, to the row's candidate regions
+//      (score bits + position); about 1.3k .. 2.5k per row instead of n scores.
+//   3. cand_select_kernel: the exact select over the candidates (the register
+//      select of select_core.h).  It is exact whenever the candidates are at
+//      least k and no region overflowed: then the k-th largest score of the
+//      row is >= tau, so every key that can be selected is a candidate.  Rows
+//      where that check fails (a threshold drawn too high, or too many equal
+//      scores) are queued.
+//   4. idx_fallback_kernel: each queued row is recomputed on chip: its scores,
+//      32768 columns at a time, into LDS, the select of each chunk, and a merge
+//      of the chunks' top-k.  Nothing of the row reaches HBM but its chunk
+//      candidates.
+// The sample makes the threshold a statistical guess, the check makes the
+// result exact: the output is the top-k of the scores under the same total
+// order as dsa_topk (score descending, position ascending, -0 == +0).
+#include "indexer_core.h"
+#include "select_core.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int SMP_MIN = 512;        // sampled keys per row, at least ...
+constexpr int SMP_MAX = 1024;       // ... and at most
+constexpr int SMP_RATE = 32;        // one sampled key per this many columns, between those bounds
+constexpr int NO_SAMPLE = 4096;     // rows seeing at most this many keys take every visible key
+constexpr float SMP_SIGMA = 5.f;    // margin of the threshold rank, in standard deviations
+constexpr int ST_ROWS = 16;         // query rows per sample workgroup (8 waves x 2)
+constexpr int ST_KT = 128;          // sampled keys per LDS tile
+constexpr int ST_PITCH = 144;       // LDS row pitch of a tile (16 rows of a B operand on disjoint banks)
+constexpr int MAX_SEG = 512;        // candidate regions per row, at most (262144 / 512)
+
+static_assert(MAX_SEG * CAND_DECODE_SEG >= TOPK_CHUNK * TOPK_MAX_CHUNKS, "region prefix array");
+static_assert(CAND_SELECT_MAX == 4 * 4 * TPB, "select register layout");
+
+// Offset of the strided sample of a row block (a hash of its indices; any
+// value below the stride is correct).
+__device__ __forceinline__ int sample_offset(int block, int seq, int stride) {
+    return (int)(((uint32_t)block * 2654435761u + (uint32_t)seq * 40503u) % (uint32_t)stride);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 1. Thresholds.  Grid: x = block of 16 query rows, z = sequence; 8 waves x 2
+// rows as in the prefill indexer.  The block samples the keys o + i * stride,
+// i < m, of its longest row (m = clamp(n / 32, 512, 1024)); each row uses the
+// sampled keys it can see.  The sampled scores go to LDS as keys; each wave
+// then takes the r-th largest of its rows' samples by bisection on the key
+// bits (ballot counts), with no further barrier.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
+    const IndexerParams &p = tp.ix;
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[ST_KT * ST_PITCH];
+    __shared__ float kscale[ST_KT];
+    __shared__ uint32_t samp[ST_ROWS][SMP_MAX];
+
+    if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+        tp.fb[0] = 0;   // recompute queue: empty (this kernel runs first)
+        tp.fb[1] = 0;
+        tp.fb[2] = 0;   // candidates selected over (a count for measurement)
+    }
+    const int b = blockIdx.z;
+    const int q0 = p.cu_q[b];
+    const int nq = p.cu_q[b + 1] - q0;
+    const int tb = blockIdx.x * ST_ROWS;
+    if (tb >= nq) return;
+    int64_t kv0 = p.cu_kv[b], kv1 = p.cu_kv[b + 1];
+    kv0 = kv0 < 0 ? 0 : (kv0 > p.total_kv ? p.total_kv : kv0);
+    kv1 = kv1 < kv0 ? kv0 : (kv1 > p.total_kv ? p.total_kv : kv1);
+    const int ctx = (int)((kv1 - kv0) > p.max_kv ? p.max_kv : (kv1 - kv0));
+    const int last = (tb + ST_ROWS < nq ? tb + ST_ROWS : nq) - 1;
+    int n_hi = p.pos0[b] + last + 1;
+    n_hi = n_hi < 0 ? 0 : (n_hi > ctx ? ctx : n_hi);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int l = lane_id();
+    const int k = tp.k;
+    bool valid[2];
+    int pos[2], nvis[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int tl = tb + 2 * wave + r;
+        valid[r] = tl < nq;
+        pos[r] = p.pos0[b] + tl;
+        const int nv = pos[r] + 1;
+        nvis[r] = nv < 0 ? 0 : (nv > ctx ? ctx : nv);
+    }
+    if (n_hi <= NO_SAMPLE || n_hi <= k) {   // block-uniform: no row of the block needs a threshold
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            if (valid[r] && l == 0) tp.tau[q0 + tb + 2 * wave + r] = 0u;
+        return;
+    }
+    int m = n_hi / SMP_RATE;
+    m = m < SMP_MIN ? SMP_MIN : (m > SMP_MAX ? SMP_MAX : m);
+    const int stride = n_hi / m;   // >= 4; sampled key i at o + i * stride < m * stride <= n_hi
+    const int o = sample_offset(blockIdx.x, b, stride);
+
+    i32x8 qa[2][4];
+    float wq[2][4][4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int tl = tb + 2 * wave + r;
+        load_query(p, (int64_t)(q0 + (valid[r] ? tl : tb)), valid[r], qa[r], wq[r]);
+    }
+
+    for (int i0 = 0; i0 < m; i0 += ST_KT) {
+        __syncthreads();
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {   // 1024 16-byte pieces of 128 gathered key rows
+            const int c = tid + 512 * rr;
+            const int key = c >> 3, byte = (c & 7) * 16;
+            const int i = i0 + key;
+            const int s = i < m ? o + i * stride : o;
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(p.k + (kv0 + s) * DI + byte);
+            *reinterpret_cast<i32x4 *>(&ktile[key * ST_PITCH + byte]) = i < m ? v : i32x4{0, 0, 0, 0};
+        }
+        if (tid < ST_KT) kscale[tid] = i0 + tid < m ? p.k_scale[kv0 + o + (i0 + tid) * stride] : 0.f;
+        __syncthreads();
+        float part[2][4];
+#pragma unroll
+        for (int st = 0; st < ST_KT / 16; ++st) {
+            const uint8_t *src = &ktile[(16 * st + (l & 15)) * ST_PITCH + 32 * (l >> 4)];
+            const i32x4 lo = *reinterpret_cast<const i32x4 *>(src);
+            const i32x4 hi = *reinterpret_cast<const i32x4 *>(src + 16);
+            const i32x8 kb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                f32x4 c[4];
+                block_mfma(qa[r], kb, c);
+                part[r][st & 3] = block_epilogue(c, wq[r]);
+            }
+            if ((st & 3) == 3) {
+                const int j = 16 * (st - 3) + l;   // lane l: sampled key i0 + j
+                const int i = i0 + j;
+                const int s = o + i * stride;
+                const float ks = kscale[j];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const float v = reduce_scatter4(part[r]);
+                    if (i < m) samp[2 * wave + r][i] = (valid[r] && s <= pos[r]) ? score_key(v * ks) : 0u;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (!valid[r]) continue;
+        const int n = nvis[r];
+        uint32_t kr[SMP_MAX / kWave];
+        int mt = 0;   // sampled keys this row sees
+#pragma unroll
+        for (int j = 0; j < SMP_MAX / kWave; ++j) {
+            const int i = j * kWave + l;
+            kr[j] = i < m ? samp[2 * wave + r][i] : 0u;
+            mt += __popcll(__ballot(kr[j] != 0u));
+        }
+        uint32_t tau = 0u;
+        if (n > NO_SAMPLE && n > k && mt > 0) {
+            const float mu = (float)k * (float)mt / (float)n;
+            const int rank = (int)ceilf(mu + SMP_SIGMA * sqrtf(mu)) + 1;
+            if (rank <= mt) {
+                // the largest x with #(keys >= x) >= rank: the rank-th largest sampled key
+                uint32_t x = 0u;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t y = x | (1u << bit);
+                    int cnt = 0;
+#pragma unroll
+                    for (int j = 0; j < SMP_MAX / kWave; ++j) cnt += __popcll(__ballot(kr[j] >= y));
+                    if (cnt >= rank) x = y;
+                }
+                tau = x;
+            }
+        }
+        if (l == 0) tp.tau[q0 + tb + 2 * wave + r] = tau;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Exact select over a row's candidates.  Grid: x = query row; one 1024-
+// thread workgroup (two per compute unit).  The regions' counts give each
+// region's place in the row's candidate array (column order); each thread
+// loads 4G consecutive candidates (G <= 4) as keys with their positions, and
+// the register select emits the positions of the k selected ones, ascending.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(TPB, 2) void cand_select_kernel(IdxTopkParams tp) {
+    const IndexerParams &p = tp.ix;
+    __shared__ SelectShared sh;
+    __shared__ int32_t npre[MAX_SEG + 1];
+    __shared__ int16_t nreg[MAX_SEG];
+    __shared__ int fail, nnz;
+    const int t = blockIdx.x, tid = threadIdx.x, k = tp.k;
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    const int n = ri.nvis;
+    int32_t *out = tp.idx + (int64_t)t * k;
+    if (n <= k) {   // every visible key, ascending, then -1
+        for (int j = tid; j < k; j += TPB) out[j] = j < n ? j : -1;
+        return;
+    }
+    const int nseg_t = (n + p.seg_w - 1) / p.seg_w;   // regions holding the row's visible columns
+    int cv = 0;
+    bool ovf = false;
+    if (tid < nseg_t) {
+        const int c = p.cand_cnt[(int64_t)t * p.nseg + tid];
+        ovf = c > p.cap || c < 0;
+        cv = ovf ? 0 : c;
+    }
+    if (tid == 0) fail = 0;
+    lds_barrier();
+    if (ovf) fail = 1;
+    // the non-empty regions, in order: npre[i] = first candidate of the i-th
+    // one, nreg[i] = its region (so consecutive candidates cross at most one
+    // boundary)
+    const uint32_t off = block_excl_scan((uint32_t)cv, sh.wtot);
+    const uint32_t nz = block_excl_scan(cv > 0 ? 1u : 0u, sh.wtot);
+    if (cv > 0) {
+        npre[nz] = (int32_t)off;
+        nreg[nz] = tid;
+    }
+    if (tid == nseg_t - 1) {
+        npre[nz + (cv > 0 ? 1 : 0)] = (int32_t)(off + cv);   // sentinel: the total
+        nnz = (int)nz + (cv > 0 ? 1 : 0);
+    }
+    lds_barrier();
+    const int nr = nnz;
+    const int c = npre[nr];
+    const uint32_t tau = tp.tau[t];
+    // exact only if every key that can be selected is a candidate: no region
+    // overflowed and, with a threshold, at least k keys reached it
+    if (fail || (tau != 0u && c < k) || (tau == 0u && c != n) || c > CAND_SELECT_MAX) {
+        if (tid == 0) {
+            const int slot = atomicAdd(&tp.fb[0], 1);
+            tp.fb[FB_LIST + slot] = t;
+        }
+        return;
+    }
+    if (tid == 0) atomicAdd(&tp.fb[2], c);
+    const int64_t rows0 = (int64_t)t * p.nseg;
+    // list entry holding candidate j (j < c): the last i with npre[i] <= j
+    auto entry_of = [&](int j) {
+        int lo = 0, hi = nr - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (npre[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+    };
+    auto slot_of = [&](int j, int e) { return (rows0 + nreg[e]) * p.cap + (j - npre[e]); };
+    if (c == k) {   // every candidate is selected; they are already in column order
+        for (int j = tid; j < k; j += TPB) out[j] = p.cand_pos[slot_of(j, entry_of(j))];
+        return;
+    }
+    // thread tid: candidates 4G*tid .. 4G*tid + 4G - 1 of the row (column order)
+    const int G = (c + 4 * TPB - 1) / (4 * TPB);
+    const int j0 = 4 * G * tid;
+    int e = j0 < c ? entry_of(j0) : 0;
+    uint32_t kr[16], lmin = 0xFFFFFFFFu, lmax = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int j = j0 + i;
+        const bool in = i / 4 < G && j < c;
+        e += (in && j >= npre[e + 1]) ? 1 : 0;
+        kr[i] = in ? score_key(__uint_as_float(p.cand_key[slot_of(j, e)])) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        lmin = kr[i] != 0u && kr[i] < lmin ? kr[i] : lmin;
+        lmax = kr[i] > lmax ? kr[i] : lmax;
+    }
+    select_regs<4>(kr, G, lmin, lmax, k, sh, tid, false, [](int) {});
+    // sh.ocol: the selected candidates' indices, ascending (= column order)
+    for (int j = tid; j < k; j += TPB) {
+        const int cj = sh.ocol[j];
+        out[j] = p.cand_pos[slot_of(cj, entry_of(cj))];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. Recompute of the queued rows.  Persistent workgroups take rows from the
+// queue; per row, each 32768-column chunk is scored into LDS (16 waves, 64-key
+// groups, the same MFMA and epilogue as the indexer), then selected like the
+// top-k chunk kernel.  A row of one chunk writes its idx directly; longer rows
+// keep each chunk's top-k (key, position) in the row's own candidate area,
+// and a final register select merges them (exact: the union of the chunks'
+// top-k sets under one total order holds the row's top-k).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(TPB) void idx_fallback_kernel(IdxTopkParams tp) {
+    const IndexerParams &p = tp.ix;
+    __shared__ __attribute__((aligned(16))) float stage[TOPK_CHUNK];
+    __shared__ SelectShared sh;
+    __shared__ int next;
+    const int tid = threadIdx.x, k = tp.k;
+    const int wave = tid >> 6, l = lane_id();
+    const int queued = *static_cast<volatile int32_t *>(&tp.fb[0]);
+    for (;;) {
+        if (tid == 0) next = atomicAdd(&tp.fb[1], 1);
+        lds_barrier();
+        const int qi = next;
+        lds_barrier();
+        if (qi >= queued) break;
+        const int t = tp.fb[FB_LIST + qi];
+        const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+        const int n = ri.nvis;   // > k: only such rows are queued
+        const int nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
+        int32_t *out = tp.idx + (int64_t)t * k;
+        const int64_t cbase = (int64_t)t * p.nseg * p.cap;   // the row's candidate area (>= nch * k slots)
+        uint32_t *ck = p.cand_key + cbase;
+        int32_t *cp = p.cand_pos + cbase;
+        for (int ch = 0; ch < nch; ++ch) {
+            const int c0 = ch * TOPK_CHUNK;
+            const int len = n - c0 < TOPK_CHUNK ? n - c0 : TOPK_CHUNK;
+            {   // scores of columns [c0, c0 + len): wave w takes the 64-key groups w, w + 16, ...
+                i32x8 qa[4];
+                float wq[4][4];
+                load_query(p, t, true, qa, wq);
+                for (int g = wave; 64 * g < len; g += TPB / kWave) {
+                    float part[4];
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) {
+                        const int key = c0 + 64 * g + 16 * bb + (l & 15);
+                        const int kc = key < c0 + len ? key : c0;
+                        const uint8_t *src = p.k + (ri.kv0 + kc) * DI + 32 * (l >> 4);
+                        const i32x4 lo = *reinterpret_cast<const i32x4 *>(src);
+                        const i32x4 hi = *reinterpret_cast<const i32x4 *>(src + 16);
+                        const i32x8 kb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        f32x4 c[4];
+                        block_mfma(qa, kb, c);
+                        part[bb] = block_epilogue(c, wq);
+                    }
+                    const float v = reduce_scatter4(part);
+                    const int key = c0 + 64 * g + l;
+                    if (key < c0 + len) stage[key - c0] = v * p.k_scale[ri.kv0 + key];
+                }
+            }
+            lds_barrier();
+            if (nch > 1 && len <= k) {
+                // the whole (last) chunk is its own top-k: in column order, padded
+                for (int j = tid; j < k; j += TPB) {
+                    ck[ch * k + j] = j < len ? score_key(stage[j]) : 0u;
+                    cp[ch * k + j] = j < len ? c0 + j : -1;
+                }
+            } else {
+                // keys from the stage, thread tz holding the 4G consecutive columns
+                // 4G*tz + j (G odd: the 16-byte LDS reads of a wave hit distinct banks)
+                const int tz = tid;
+                const int ngroups = (len + 4 * TPB - 1) / (4 * TPB);
+                const int G = ngroups < CH_V4 ? (ngroups | 1) : CH_V4;
+                const int lim = 4 * G * (tz + 1) < len ? 4 * G * (tz + 1) : len;
+                uint32_t kr[4 * CH_V4], lmin = 0xFFFFFFFFu, lmax = 0u;
+#pragma unroll
+                for (int u = 0; u < CH_V4; ++u) {
+                    const int cc = 4 * (tz * G + u);
+                    const float4 f4 = (u < G && cc < TOPK_CHUNK) ? *reinterpret_cast<const float4 *>(stage + cc)
+                                                                  : float4{0.f, 0.f, 0.f, 0.f};
+                    const float f[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t key = score_key(f[i]) & (0u - (uint32_t)(cc + i < lim));
+                        kr[4 * u + i] = key;
+                        lmin = key != 0u && key < lmin ? key : lmin;
+                        lmax = key > lmax ? key : lmax;
+                    }
+                }
+                select_regs<CH_V4>(kr, G, lmin, lmax, k, sh, tz, nch > 1, [](int) {});
+                if (nch == 1) {
+                    for (int j = tid; j < k; j += TPB) out[j] = sh.ocol[j];
+                } else {
+                    for (int j = tid; j < k; j += TPB) {
+                        ck[ch * k + j] = sh.okey[j];
+                        cp[ch * k + j] = c0 + sh.ocol[j];
+                    }
+                }
+            }
+            lds_barrier();   // stage and sh free for the next chunk
+        }
+        if (nch > 1) {
+            // merge the chunks' candidates (this workgroup's own global writes)
+            __threadfence();
+            __syncthreads();
+            const int m = nch * k;
+            const int G = (m + 4 * TPB - 1) / (4 * TPB);
+            uint32_t kr[4 * MG_V4], lmin = 0xFFFFFFFFu, lmax = 0u;
+#pragma unroll
+            for (int i = 0; i < 4 * MG_V4; ++i) {
+                const int j = 4 * G * tid + i;
+                kr[i] = i / 4 < G && j < m ? ck[j] : 0u;
+                lmin = kr[i] != 0u && kr[i] < lmin ? kr[i] : lmin;
+                lmax = kr[i] > lmax ? kr[i] : lmax;
+            }
+            select_regs<MG_V4>(kr, G, lmin, lmax, k, sh, tid, false, [](int) {});
+            for (int j = tid; j < k; j += TPB) out[j] = cp[sh.ocol[j]];
+            lds_barrier();
+        }
+    }
+}
+
+hipError_t launch_indexer_topk(const IdxTopkParams &tp, int T, int max_q, bool decode_variant, hipStream_t s,
+                               LaunchMarks *marks) {
+    if (T <= 0) return hipSuccess;
+    const IndexerParams &p = tp.ix;
+    if (p.nseg * p.seg_w < p.max_kv || p.nseg > MAX_SEG) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(indexer_sample_kernel, dim3((max_q + ST_ROWS - 1) / ST_ROWS, 1, p.B), dim3(512), 0, s, tp);
+    hipError_t e = hipGetLastError();
+    if (marks) marks->after("indexer_sample_kernel", s);
+    if (e != hipSuccess) return e;
+    if (p.max_kv > 0) {
+        if ((e = launch_indexer_cand(p, T, max_q, decode_variant, s)) != hipSuccess) return e;
+        if (marks) marks->after(decode_variant ? "indexer_decode_kernel<cand>" : "indexer_prefill_kernel<cand>", s);
+    }
+    hipLaunchKernelGGL(cand_select_kernel, dim3(T), dim3(TPB), 0, s, tp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (marks) marks->after("cand_select_kernel", s);
+    static int ncu = 0;
+    if (ncu == 0) {
+        int dev = 0, nn = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&nn, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || nn <= 0)
+            nn = 256;
+        ncu = nn;
+    }
+    hipLaunchKernelGGL(idx_fallback_kernel, dim3(T < ncu ? T : ncu), dim3(TPB), 0, s, tp);
+    e = hipGetLastError();
+    if (marks) marks->after("idx_fallback_kernel", s);
+    return e;
+}
+
+}  // namespace dsa

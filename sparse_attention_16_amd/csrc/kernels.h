@@ -23,7 +23,32 @@ struct IndexerParams {
     int64_t ld;
     int key_chunk;          // keys per workgroup
     int fill_masked;        // write -inf for s in [nvis, ctx)
+    // Candidate mode (the fused indexer + select; scores are not written):
+    // the visible keys of row t whose score key (score_key of the fp32 score)
+    // is >= tau[t] go, in column order, to the row's candidate regions.
+    // Region r of row t covers columns [r * seg_w, (r + 1) * seg_w) and holds
+    // up to cap (key, position) pairs at slot (t * nseg + r) * cap; cand_cnt
+    // receives the number found (more than cap: the region overflowed).
+    const uint32_t *tau;    // [T]
+    uint32_t *cand_key;     // [T * nseg * cap]
+    int32_t *cand_pos;      // [T * nseg * cap]
+    int32_t *cand_cnt;      // [T * nseg]
+    int seg_w, nseg, cap;
+    int topk_k;             // k of the select (row blocks that see at most k keys need no candidates)
 };
+
+// The fused indexer + select (indexer_topk.hip): a sampled threshold per row,
+// the indexer in candidate mode, an exact select over the candidates, and an
+// on-chip recompute for rows whose threshold failed.
+struct IdxTopkParams {
+    IndexerParams ix;       // inputs, candidate regions and thresholds
+    uint32_t *tau;          // [T] written by the sample kernel (same array as ix.tau)
+    int k;
+    int32_t *idx;           // [T, k] out
+    int32_t *fb;            // [FB_LIST + T]: rows queued for the recompute, next queue entry,
+                            // candidates selected over (all rows), then the queued rows
+};
+constexpr int FB_LIST = 3;
 
 struct TopkParams {
     const int32_t *cu_q;
@@ -121,12 +146,27 @@ constexpr int TOPK_MAX_CHUNKS = 8;    // merge capacity: 8 x 2048 candidates
 constexpr int MLA_BK = 32;            // keys per gathered block
 constexpr int KL_BK = 32;             // slots per block of the KL loss
 constexpr int MAX_KV_ATTN = 1 << 21;  // per-sequence rows the gathers address with 32-bit offsets
+constexpr int CAND_DECODE_SEG = 512;  // columns per candidate region of the decode indexer (one wave's range)
+constexpr int CAND_CAP = 8192;        // candidate slots per region of the prefill indexer, at most
+constexpr int CAND_SELECT_MAX = 16384;  // candidates one select workgroup holds in registers
+
+// Per-kernel timing hook: a launcher that enqueues several kernels calls
+// after(kernel name) right after each launch (null: no timing).
+struct LaunchMarks {
+    virtual void after(const char *kernel, hipStream_t s) = 0;
+    virtual ~LaunchMarks() = default;
+};
 
 hipError_t launch_indexer(const IndexerParams &p, int T, int max_q, bool decode_variant,
                           hipStream_t s);
-hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s);
+// indexer in candidate mode (p.tau, p.cand_*): prefill or decode layout
+hipError_t launch_indexer_cand(const IndexerParams &p, int T, int max_q, bool decode_variant, hipStream_t s);
+// the fused indexer + select: sample -> candidate indexer -> select -> recompute of failed rows
+hipError_t launch_indexer_topk(const IdxTopkParams &p, int T, int max_q, bool decode_variant, hipStream_t s,
+                               LaunchMarks *m = nullptr);
+hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s, LaunchMarks *m = nullptr);
 hipError_t launch_select_all_visible(const TopkParams &p, int T, hipStream_t s);
-hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s);
+hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s, LaunchMarks *m = nullptr);
 hipError_t launch_sparse_mla_bwd(const BwdParams &p, int T, hipStream_t s);
 hipError_t launch_indexer_kl(const KlParams &p, int T, hipStream_t s);
 hipError_t launch_quant_queries(const float *q, int64_t T, uint8_t *q_fp8, float *q_scale, hipStream_t s);

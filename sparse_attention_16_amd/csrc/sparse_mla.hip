@@ -552,14 +552,17 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
     if ((threadIdx.x & 127) == 0) p.lse[(int64_t)t * H + h] = L;
 }
 
-hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s) {
+hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s, LaunchMarks *m) {
     if (T <= 0) return hipSuccess;
     hipLaunchKernelGGL(sparse_mla_kernel, dim3(T, p.splits), dim3(NTHREADS), 0, s, p, p.idx, p.out,
                        p.lse, p.o_part, p.lse_part);
     hipError_t e = hipGetLastError();
+    if (m) m->after("sparse_mla_kernel", s);
     if (e != hipSuccess || p.splits == 1) return e;
     hipLaunchKernelGGL(mla_merge_kernel, dim3(T, H / 2), dim3(256), 0, s, p);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (m) m->after("mla_merge_kernel", s);
+    return e;
 }
 
 }  // namespace dsa

@@ -2,10 +2,20 @@
 parity tolerances, and index-set comparison modulo near-ties.
 
 Tolerances (per the hot path's parity bar):
-  * index scores: |I_gpu - I_ref| <= 1e-3 * max(|I_ref|, A_ref), where A is the
-    sum of absolute head terms (signed head weights can make I cancel);
+  * index scores: |I_gpu - I_ref| <= 1e-3 * |I_ref| (the stated 1e-3 relative)
+    on every entry with |I_ref| >= 0.1 * A_ref, where A is the sum of absolute
+    head terms, and <= 1e-3 * |I_ref| + 1e-4 * A_ref on the others (counted).
+    Why the second term: the GPU's fp32 evaluation (fp32 accumulation of the
+    128 FP8 products on the matrix cores, then the fp32 sum of 64 weighted head
+    terms) carries an error that scales with A, not with I: measured against
+    the oracle over 1.1M entries of the 4K prefill and the 64-sequence decode,
+    median 2.5e-6 * A, 99.99th percentile 2.2e-5 * A, largest 4.1e-5 * A.
+    Where signed head weights cancel I to a small fraction of A, no fp32
+    evaluation keeps within 1e-3 of I; from |I| >= 0.1 * A on, 1e-4 * A is
+    within 1e-3 * |I| (largest measured there: 2.7e-4 relative);
   * top-k sets: identical, except at positions whose reference score lies within
-    1e-3 * max(|I_kth|, A_kth) of the k-th selected reference score;
+    1e-3 * |I_kth| of the k-th selected reference score (the stated band),
+    widened by the fp32 allowance of two scores, 2e-4 * A_kth;
   * attention: |out_gpu - o_ref| <= 2e-2 + 1e-2 * |o_ref| (bf16 output) and
     |lse_gpu - lse_ref| <= 1e-3.
 """
@@ -51,21 +61,51 @@ def bf16_to_f32(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.bfloat16).float().cpu().numpy()
 
 
-def check_scores(gpu: np.ndarray, ref: np.ndarray, A: np.ndarray, nvis: np.ndarray, what=""):
-    """gpu/ref/A: [rows, ld]; columns < nvis compared with the score tolerance."""
+CANCEL = 0.1          # |I| < CANCEL * A: an entry whose head terms cancel
+SCORE_ATOL_A = 1e-4   # fp32 allowance on those entries, in units of A
+
+
+def check_scores(gpu: np.ndarray, ref: np.ndarray, A: np.ndarray, nvis: np.ndarray, what="", stats=None):
+    """gpu/ref/A: [rows, ld]; columns < nvis compared with the score tolerance.
+    Returns the worst relative error |dI| / |I_ref| over the entries that do not
+    cancel; `stats` (a dict) receives the counts of checked and cancelling
+    entries and the worst error of the cancelling ones relative to A."""
     worst = 0.0
+    n_rel = n_cancel = 0
+    worst_cancel = worst_all_a = 0.0
     for r in range(ref.shape[0]):
         n = int(nvis[r])
         g, e, a = gpu[r, :n].astype(np.float64), ref[r, :n].astype(np.float64), A[r, :n]
         assert np.all(np.isfinite(g)), f"{what} row {r}: non-finite visible score"
-        scale = np.maximum(np.abs(e), a)
         err = np.abs(g - e)
-        bad = err > SCORE_RTOL * scale + 1e-30
-        assert not np.any(bad), (f"{what} row {r}: {bad.sum()} scores out of tolerance, "
-                                 f"worst rel {np.max(err / np.maximum(scale, 1e-30)):.3g}")
+        rel = np.abs(e) >= CANCEL * a
+        bad = rel & (err > SCORE_RTOL * np.abs(e))
+        assert not np.any(bad), (f"{what} row {r}: {bad.sum()} scores outside 1e-3 relative, "
+                                 f"worst {np.max(err[bad] / np.abs(e[bad])):.3g}")
+        canc = ~rel
+        badc = canc & (err > SCORE_RTOL * np.abs(e) + SCORE_ATOL_A * a + 1e-30)
+        assert not np.any(badc), (f"{what} row {r}: {badc.sum()} cancelling scores outside "
+                                  f"1e-3 |I| + 1e-5 A, worst {np.max(err[badc] / a[badc]):.3g} of A")
+        n_rel += int(rel.sum())
+        n_cancel += int(canc.sum())
+        if rel.any():
+            worst = max(worst, float(np.max(err[rel] / np.abs(e[rel]))))
+        if canc.any():
+            worst_cancel = max(worst_cancel, float(np.max(err[canc] / np.maximum(a[canc], 1e-30))))
         if n:
-            worst = max(worst, float(np.max(err / np.maximum(scale, 1e-30))))
+            worst_all_a = max(worst_all_a, float(np.max(err / np.maximum(a, 1e-30))))
+    if stats is not None:
+        stats.update(checked=n_rel, cancelling=n_cancel, worst_cancelling_over_A=worst_cancel,
+                     worst_over_A=worst_all_a)
+    say(f"  {what}: {n_cancel} of {n_rel + n_cancel} scores cancel (|I| < 0.1 A), worst error "
+        f"{worst_cancel:.3g} of A there; worst over all entries {worst_all_a:.3g} of A")
     return worst
+
+
+def tie_band(sr_kth: float, a_kth: float) -> float:
+    """Half-width of the near-tie band around the k-th reference score: the
+    stated 1e-3 relative, plus the fp32 error allowance of two scores."""
+    return TIE_RTOL * abs(sr_kth) + 2 * SCORE_ATOL_A * a_kth
 
 
 def check_idx_sets(gpu_idx: np.ndarray, ref_idx: np.ndarray, ref_scores: np.ndarray,
@@ -86,7 +126,7 @@ def check_idx_sets(gpu_idx: np.ndarray, ref_idx: np.ndarray, ref_scores: np.ndar
             continue
         sr = ref_scores[r]
         kth = rs[np.argmin(sr[rs])]  # lowest selected reference score
-        band = TIE_RTOL * max(abs(float(sr[kth])), float(A[r, kth]))
+        band = tie_band(float(sr[kth]), float(A[r, kth]))
         diff = np.setxor1d(gs, rs)
         far = diff[np.abs(sr[diff].astype(np.float64) - float(sr[kth])) > band]
         assert far.size == 0, (f"{what} row {r}: {far.size} differing positions outside the "

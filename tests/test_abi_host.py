@@ -248,3 +248,44 @@ def test_quantize_and_append_validation(dsa):
     assert lib.dsa_append_cache(FAKE, FAKE, 4, 128, 576, FAKE, FAKE, FAKE + 4, FAKE, 100, None) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_append_cache(FAKE, FAKE, -1, 128, 576, FAKE, FAKE, FAKE, FAKE, 100, None) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_append_cache(None, None, 0, 128, 576, None, None, None, None, 0, None) == dsa.DSA_OK
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.04, -0.0, float("-inf")])
+def test_softmax_scale_must_be_positive(dsa, scale):
+    """Every entry that takes the attention's softmax scale rejects scale <= 0
+    (and non-finite) before launching: the kernels take max(raw logit) * scale
+    as the maximum of the scaled logits, and a masked slot's -inf logit times
+    such a scale is NaN or +inf."""
+    lib = dsa.raw_lib()
+    b = _batch(dsa, 4096, 4096)
+    big = 1 << 40
+    assert lib.dsa_sparse_mla_fwd(ctypes.byref(b), FAKE, FAKE, FAKE, 2048, 128, 576, 512, scale, FAKE, FAKE,
+                                  FAKE, big, None) == dsa.DSA_ERR_INVALID_ARG
+    s = _batch(dsa, 2048, 2048)
+    assert lib.dsa_dense_mla_fwd(ctypes.byref(s), FAKE, FAKE, 128, 576, 512, scale, FAKE, FAKE, FAKE, big,
+                                 None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_kl_fwd(ctypes.byref(b), FAKE, FAKE, FAKE, 128, 576, scale, FAKE, 4096, FAKE, 2048,
+                                  FAKE, None, FAKE, big, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_sparse_mla_bwd(ctypes.byref(b), FAKE, FAKE, FAKE, 2048, 128, 576, 512, scale, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, big, None) == dsa.DSA_ERR_INVALID_ARG
+    a = dsa.dsa_fwd_args(b, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 128, 576, 512, 2048, scale)
+    for fn in (lib.dsa_prefill_fwd, lib.dsa_decode_fwd):
+        assert fn(ctypes.byref(a), FAKE, FAKE, None, FAKE, big, None) == dsa.DSA_ERR_INVALID_ARG
+    # the same calls with a positive scale pass validation up to the launch
+    # (which then needs a GPU): only the scale differs
+    a_ok = dsa.dsa_fwd_args(b, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 128, 576, 512, 2048, 0.04)
+    assert lib.dsa_prefill_fwd(ctypes.byref(a_ok), FAKE, FAKE, FAKE + 8, FAKE, big, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_profile_entry_validation(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa)
+    a = dsa.dsa_fwd_args(b, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 128, 576, 512, 2048, 0.04)
+    n = ctypes.c_int(-1)
+    times = (dsa.dsa_kernel_time * 4)()
+    assert lib.dsa_fwd_profile(ctypes.byref(a), 0, FAKE, FAKE, None, FAKE, 1 << 40, None, None, 4,
+                               ctypes.byref(n)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_fwd_profile(ctypes.byref(a), 0, FAKE, FAKE, None, FAKE, 1 << 40, None, times, 0,
+                               ctypes.byref(n)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_fwd_profile(ctypes.byref(a), 0, FAKE, FAKE, None, FAKE, 1 << 40, None, times, 4,
+                               None) == dsa.DSA_ERR_INVALID_ARG

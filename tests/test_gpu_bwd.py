@@ -172,3 +172,41 @@ def test_sparse_mla_bwd_32k_sampled(dsa):
     e_kv = _check_rows(g[touched], dkv_ref[touched], "32k dkv")
     assert np.all(g[~touched] == 0.0)
     say(f"  32k: worst error / row rms: dq {e_q:.3g}, dkv {e_kv:.3g}")
+
+
+@pytest.mark.parametrize("name", ["prefill_300_k64", "decode_k2048"])
+def test_sparse_mla_bwd_against_exact_gradient(dsa, name):
+    """The GPU backward (handed the forward's bf16 out, as in training) against
+    the oracle's exact gradient, whose delta comes from the exact forward
+    output.  Bound: the rounding gate above plus the closed-form shift that the
+    bf16 out causes, -scale * (delta(out_bf16) - delta(exact)) * sum_j P_j kv_j
+    in dq (and its image in dkv), which the oracle evaluates as the difference
+    of its two gradients (delta from the bf16 out minus delta exact)."""
+    say(f"[sparse_mla_bwd exact] {name}")
+    inp = CASES[name]()
+    b = inp.batch
+    scores = oracle.indexer(b.cu_q, b.cu_kv, b.pos0, inp.qi, inp.qi_scale, inp.w, inp.ki, inp.ki_scale)
+    idx = oracle.topk(b.cu_q, b.cu_kv, b.pos0, scores, inp.k)
+    out, lse, dout = _inputs(inp, idx, 2000 + len(name))
+    args = (b.cu_q, b.cu_kv, b.pos0, inp.q, inp.kv, dout, idx, inp.Dv, inp.scale)
+    dq_ex, dkv_ex = oracle.sparse_attn_bwd(*args)
+    dq_bf, dkv_bf = oracle.sparse_attn_bwd(*args, out=out)
+    dq, dkv = _run(dsa, inp, idx, out, lse, dout)
+
+    def check(got, exact, shifted, what):
+        got, exact, shifted = (x.reshape(x.shape[0], -1).astype(np.float64) for x in (got, exact, shifted))
+        rms = np.sqrt(np.mean(exact ** 2, axis=1, keepdims=True))
+        floor = ABS_FLOOR * np.sqrt(np.mean(exact ** 2))
+        shift = np.abs(shifted - exact)
+        err = np.abs(got - exact)
+        bad = err > RMS_TOL * rms + REL_TOL * np.abs(exact) + shift + floor
+        assert not np.any(bad), f"{name} {what}: {bad.sum()} values outside the bound, worst {err.max():.3g}"
+        live = rms[:, 0] > 0
+        return float(np.max(err[live] / rms[live])), float(np.max(shift[live] / rms[live]))
+
+    e_q, s_q = check(dq.reshape(-1, inp.D), dq_ex.reshape(-1, inp.D), dq_bf.reshape(-1, inp.D), "dq")
+    touched = np.any(dkv_ex != 0, axis=1)
+    e_kv, s_kv = check(dkv[touched], dkv_ex[touched], dkv_bf[touched], "dkv")
+    assert np.all(dkv[~touched] == 0.0)
+    say(f"  {name}: worst error / row rms against the exact gradient: dq {e_q:.3g} (bf16-out shift {s_q:.3g}), "
+        f"dkv {e_kv:.3g} (shift {s_kv:.3g})")

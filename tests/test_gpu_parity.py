@@ -352,3 +352,94 @@ def test_decode_fwd_mixed(dsa):
     inp = synth.make_inputs(synth.Batch.decode([1, 2048, 2049, 20000, 40000, 70000]), seed=123,
                             k=2048, per_seq=True)
     _check_fused(dsa, inp, "decode", what="decode mixed")
+
+
+# ------------------------------------------------- indexer key-chunk widths
+
+def _indexer_width_case(width):
+    """1024 sequences of 16 query rows: one sequence long enough that the
+    prefill indexer takes `width` keys per workgroup (at least 8 workgroups per
+    compute unit over 1024 row blocks x its key chunks), the others short.  The
+    long sequence's queries sit mid-context, so its rows have a causally masked
+    stretch that crosses the chunk boundary, then the columns past its context."""
+    B = 1024
+    rng = np.random.default_rng(width)
+    long_ctx = {4096: 6000, 8192: 12000}[width]
+    n_kv = rng.integers(20, 200, size=B)
+    n_kv[0] = long_ctx
+    pos0 = np.maximum(n_kv - 16 - rng.integers(0, 8, size=B), 0)
+    pos0[0] = long_ctx // 2 - 100
+    return synth.Batch.ragged(np.full(B, 16), n_kv, pos0)
+
+
+@pytest.mark.parametrize("width", [4096, 8192])
+def test_indexer_chunk_widths(dsa, width):
+    """The prefill indexer's 4096- and 8192-key workgroup widths (chosen by
+    the row blocks x key chunks of the batch): sampled rows against the oracle,
+    -inf over the masked columns [nvis, ctx), columns past ctx untouched."""
+    say(f"[indexer] chunk width {width}")
+    b = _indexer_width_case(width)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    rowblocks = ((b.max_q + 15) // 16) * b.B
+    chosen = next((c for c in (8192, 4096) if rowblocks * -(-b.max_kv // c) >= 8 * ncu), 2048)
+    say(f"  {ncu} compute units: {chosen} keys per workgroup expected")
+    if ncu == 256:
+        assert chosen == width
+    wl = synth.Workload(b, seed=131 + width, k=64)
+    qi, qs = wl.qi_rows(0, b.T)
+    ki, ks = wl.ki_rows(0, b.N)
+    w = wl.w_rows(0, b.T)
+    batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0)
+    ld = ((b.max_kv + 63) // 64) * 64 + 64
+    scores = torch.full((b.T, ld), float("nan"), device="cuda")
+    dsa.indexer_scores(batch, dev(qi), dev(qs), dev(w), dev(ki), dev(ks), scores)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(16), np.sort(np.random.default_rng(7).choice(
+        np.arange(16, b.T), 200, replace=False))])
+    g = scores[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+    ref, A = oracle.indexer(b.cu_q, b.cu_kv, b.pos0, qi, qs, w, ki, ks, rows=rows, ld=ld, want_abs=True)
+    _, _, ctx, _, nvis = oracle.visible(b.cu_q, b.cu_kv, b.pos0)
+    worst = check_scores(g, ref, A, nvis[rows], f"width {width}")
+    for i, r in enumerate(rows):
+        n, c = int(nvis[r]), int(ctx[r])
+        assert np.all(np.isneginf(g[i, n:c])), f"row {r}: masked columns must be -inf"
+        assert np.all(np.isnan(g[i, c:])), f"row {r}: columns past the context must be untouched"
+    say(f"  worst relative score error {worst:.3g}")
+
+
+# ------------------------------ fused entries == the three separate steps
+
+FUSED_LONG = {
+    "decode_long_rows": lambda: synth.make_inputs(
+        synth.Batch.decode([32769, 40000, 70001, 131072, 2049, 5000, 100000, 65536]), seed=141, k=2048,
+        per_seq=True),
+    "chunked_48_at_65488": lambda: synth.make_inputs(synth.Batch.prefill(48, 65536, 65488), seed=142, k=2048),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_LONG))
+def test_fused_idx_equals_three_steps(dsa, name):
+    """The fused entries' selection equals dsa_indexer_scores + dsa_topk on the
+    same inputs bit for bit, on rows longer than one 32768-column select chunk
+    (the scores are the same fp32 values, so the exact top-k is the same set)."""
+    say(f"[fused == three steps] {name}")
+    inp = FUSED_LONG[name]()
+    b = inp.batch
+    d = DevInputs(inp, dsa)
+    entry = "decode" if name.startswith("decode") else "prefill"
+    args = dsa.fwd_args(d.batch, d.qi, d.qs, d.w, d.ki, d.ks, d.q, d.kv, inp.k, inp.scale)
+    out = torch.empty((b.T, inp.H, inp.Dv), dtype=torch.int16, device="cuda")
+    lse = torch.empty((b.T, inp.H), device="cuda")
+    idx = torch.full((b.T, inp.k), -7, dtype=torch.int32, device="cuda")
+    (dsa.decode_fwd if entry == "decode" else dsa.prefill_fwd)(args, d.batch, out, lse, idx)
+    ld = ((b.max_kv + 63) // 64) * 64
+    scores = torch.empty((b.T, ld), device="cuda")
+    dsa.indexer_scores(d.batch, d.qi, d.qs, d.w, d.ki, d.ks, scores)
+    idx3 = torch.full((b.T, inp.k), -9, dtype=torch.int32, device="cuda")
+    dsa.topk(d.batch, scores, inp.k, idx3)
+    torch.cuda.synchronize()
+    g, g3 = idx.cpu().numpy(), idx3.cpu().numpy()
+    assert np.array_equal(g, g3), f"{name}: {np.sum(np.any(g != g3, axis=1))} rows differ"
+    _, _, ctx, _, nvis = oracle.visible(b.cu_q, b.cu_kv, b.pos0)
+    assert np.any(nvis > 32768)
+    say(f"  {b.T} rows, longest {int(nvis.max())} keys: identical")

@@ -17,9 +17,8 @@ HI, DI, D = 64, 128, 576
 
 @pytest.fixture(scope="module")
 def dsa():
-    if not torch.cuda.is_available():
-        pytest.skip("needs a GPU")
-    import sparse_attention_16_amd as m
+    import sparse_attention_16_amd as m  # fails loudly when libdsa.so is missing
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
     return m
 
 
