@@ -628,7 +628,7 @@ def kernel_roof(name, wl, entry, nvis, ms_mean, ms_median, splits=1, items=-1):
     b = wl.batch
     k, T = wl.k, b.T
     long_rows = nvis > k
-    if name == "indexer_sample_kernel":
+    if name in ("indexer_sample_kernel", "indexer_sample_row_kernel"):
         bound, work = "mfma", 2.0 * HI * DI * sampled_pairs(b, k)   # fp8 flops of the sampled pairs
         peak, unit, target = PEAK_FP8_TFLOPS, "TFLOP/s", 0.5
     elif name == "indexer_prefill_kernel<cand>":
@@ -638,7 +638,7 @@ def kernel_roof(name, wl, entry, nvis, ms_mean, ms_median, splits=1, items=-1):
         # keys (128 code bytes + 4 scale bytes) of rows that see more than k, their query rows
         work = (DI + 4) * float(np.sum(nvis[long_rows])) + float(np.sum(long_rows)) * (HI * DI + HI * 8)
         bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.5
-    elif name == "cand_select_kernel":
+    elif name == "cand_select_wave_kernel":
         # candidate keys read, the selected positions read, idx written
         work = 4.0 * max(items, 0) + 8.0 * k * T
         bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.6

@@ -150,7 +150,7 @@ CandLayout cand_layout(const dsa_batch *b, int k, bool decode) {
     c.key = c.cnt + up(T * c.nseg * 4);
     c.pos = c.key + up(slots * 4);
     c.fb = c.pos + up(slots * 4);
-    c.total = c.fb + up((FB_LIST + T) * 4);
+    c.total = c.fb + up((FB_LIST + 2 * T) * 4);
     return c;
 }
 
@@ -620,7 +620,7 @@ dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, 
             times[i].kernel = tl.name[i];
             times[i].ms = ms;
             times[i].items = -1;
-            if (std::strcmp(tl.name[i], "cand_select_kernel") == 0) times[i].items = fb[2];
+            if (std::strcmp(tl.name[i], "cand_select_wave_kernel") == 0) times[i].items = fb[2];
             if (std::strcmp(tl.name[i], "idx_fallback_kernel") == 0) times[i].items = fb[0];
             *n_times = i + 1;
         }

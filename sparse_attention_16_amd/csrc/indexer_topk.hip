@@ -74,9 +74,7 @@ __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
     __shared__ uint32_t samp[ST_ROWS][SMP_MAX];
 
     if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
-        tp.fb[0] = 0;   // recompute queue: empty (this kernel runs first)
-        tp.fb[1] = 0;
-        tp.fb[2] = 0;   // candidates selected over (a count for measurement)
+        for (int i = 0; i < FB_LIST; ++i) tp.fb[i] = 0;   // queues empty, counts 0 (this kernel runs first)
     }
     const int b = blockIdx.z;
     const int q0 = p.cu_q[b];
@@ -198,102 +196,452 @@ __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// 3. Exact select over a row's candidates.  Grid: x = query row; one 1024-
-// thread workgroup (two per compute unit).  The regions' counts give each
-// region's place in the row's candidate array (column order); each thread
-// loads 4G consecutive candidates (G <= 4) as keys with their positions, and
-// the register select emits the positions of the k selected ones, ascending.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(TPB, 2) void cand_select_kernel(IdxTopkParams tp) {
+// Threshold of one query row per workgroup (decode-shaped batches, where a
+// sequence has a single query row and a 16-row block would score 15 empty
+// rows).  Same sample grid as above for a block of one row (so the same
+// threshold); the 8 waves each gather and score 128 sampled keys in one pass
+// (B operands loaded straight into registers), wave 0 bisects.  Grid: x = row.
+__global__ __launch_bounds__(512) void indexer_sample_row_kernel(IdxTopkParams tp) {
     const IndexerParams &p = tp.ix;
-    __shared__ SelectShared sh;
-    __shared__ int32_t npre[MAX_SEG + 1];
-    __shared__ int16_t nreg[MAX_SEG];
-    __shared__ int fail, nnz;
-    const int t = blockIdx.x, tid = threadIdx.x, k = tp.k;
+    __shared__ uint32_t samp[SMP_MAX];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        for (int i = 0; i < FB_LIST; ++i) tp.fb[i] = 0;   // queues empty, counts 0 (this kernel runs first)
+    }
+    const int t = blockIdx.x;
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    const int n = ri.nvis, k = tp.k;
+    const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
+    if (n <= NO_SAMPLE || n <= k) {
+        if (tid == 0) tp.tau[t] = 0u;
+        return;
+    }
+    const int b = find_seq(p.cu_q, p.B, t);
+    const int block = (t - p.cu_q[b]) / ST_ROWS;
+    int m = n / SMP_RATE;
+    m = m < SMP_MIN ? SMP_MIN : (m > SMP_MAX ? SMP_MAX : m);
+    const int stride = n / m;
+    const int o = sample_offset(block, b, stride);
+    i32x8 qa[4];
+    float wq[4][4];
+    load_query(p, t, true, qa, wq);
+    // wave w: sampled keys 128w + 16st + (l & 15), st < 8; all gathers first
+    i32x8 kb[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        const int i = 128 * wave + 16 * st + (l & 15);
+        const int s = i < m ? o + i * stride : o;
+        const uint8_t *src = p.k + (ri.kv0 + s) * DI + 32 * (l >> 4);
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(src);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(src + 16);
+        kb[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    float ks[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int i = 128 * wave + 64 * h + l;
+        ks[h] = i < m ? p.k_scale[ri.kv0 + o + i * stride] : 0.f;
+    }
+    float part[4];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        f32x4 c[4];
+        block_mfma(qa, kb[st], c);
+        part[st & 3] = block_epilogue(c, wq);
+        if ((st & 3) == 3) {
+            const int h = st >> 2;
+            const int i = 128 * wave + 64 * h + l;
+            const float v = reduce_scatter4(part);
+            if (i < SMP_MAX) samp[i] = i < m ? score_key(v * ks[h]) : 0u;
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    uint32_t kr[SMP_MAX / kWave];
+#pragma unroll
+    for (int j = 0; j < SMP_MAX / kWave; ++j) kr[j] = samp[j * kWave + l];
+    const float mu = (float)k * (float)m / (float)n;
+    const int rank = (int)ceilf(mu + SMP_SIGMA * sqrtf(mu)) + 1;
+    uint32_t tau = 0u;
+    if (rank <= m) {
+        uint32_t x = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t y = x | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int j = 0; j < SMP_MAX / kWave; ++j) cnt += __popcll(__ballot(kr[j] >= y));
+            if (cnt >= rank) x = y;
+        }
+        tau = x;
+    }
+    if (l == 0) tp.tau[t] = tau;
+}
+
+// ---------------------------------------------------------------------------
+// 3. Exact select over a row's candidates.
+//
+// cand_select_wave_kernel: one wave per query row, no barriers.  The
+// region counts give the row's candidate array (the non-empty regions in
+// order, in per-wave LDS), each lane loads a run of consecutive candidates
+// as keys (lane-major order = column order; at most 4096 per row), the k-th
+// largest key kappa comes from a bisection on the key bits (ballot counts),
+// and each lane writes its selected positions (keys > kappa, then the first
+// keys == kappa in column order up to k) at its scanned offset: ascending.
+// Rows with more candidates go to a queue for the workgroup select below;
+// rows whose candidates cannot be complete go to the recompute queue.
+// ---------------------------------------------------------------------------
+constexpr int SEL_WAVES = 4;        // rows per workgroup of the wave select
+constexpr int SEL_R = 64;           // candidates per lane, at most
+constexpr int SEL_WAVE_MAX = SEL_R * kWave;
+constexpr int SEL_BINS = 256;      // value bins of the wave select's histogram
+constexpr int SEL_BLOCK_ROWS = 4;   // batches of at most this many rows per compute unit: workgroup select
+
+namespace {
+
+// Exclusive prefix over the wave's lanes (DPP inclusive scan minus own).
+__device__ __forceinline__ uint32_t wave_excl_add(uint32_t v) { return wave_scan_add(v) - v; }
+
+}  // namespace
+
+__global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTopkParams tp, int T) {
+    const IndexerParams &p = tp.ix;
+    __shared__ int32_t npre_s[SEL_WAVES][MAX_SEG + 1];
+    __shared__ int16_t nreg_s[SEL_WAVES][MAX_SEG];
+    __shared__ uint32_t hist_s[SEL_WAVES][SEL_BINS];
+    __shared__ uint32_t list_s[SEL_WAVES][kWave];
+    const int wave = threadIdx.x >> 6, l = lane_id(), k = tp.k;
+    const int t = blockIdx.x * SEL_WAVES + wave;
+    if (t >= T) return;
+    int32_t *npre = npre_s[wave];
+    int16_t *nreg = nreg_s[wave];
     const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
     const int n = ri.nvis;
     int32_t *out = tp.idx + (int64_t)t * k;
     if (n <= k) {   // every visible key, ascending, then -1
-        for (int j = tid; j < k; j += TPB) out[j] = j < n ? j : -1;
+        for (int j = l; j < k; j += kWave) out[j] = j < n ? j : -1;
         return;
     }
-    const int nseg_t = (n + p.seg_w - 1) / p.seg_w;   // regions holding the row's visible columns
-    int cv = 0;
+    // the row's non-empty regions: npre[e] = first candidate, nreg[e] = region
+    const int nseg_t = (n + p.seg_w - 1) / p.seg_w;
+    const int64_t rows0 = (int64_t)t * p.nseg;
+    uint32_t off = 0, nr = 0;
     bool ovf = false;
-    if (tid < nseg_t) {
-        const int c = p.cand_cnt[(int64_t)t * p.nseg + tid];
-        ovf = c > p.cap || c < 0;
-        cv = ovf ? 0 : c;
+    for (int base = 0; base < nseg_t; base += kWave) {
+        const int r = base + l;
+        int cnt = r < nseg_t ? p.cand_cnt[rows0 + r] : 0;
+        if (cnt > p.cap || cnt < 0) {
+            ovf = true;
+            cnt = 0;
+        }
+        const uint32_t incl = wave_scan_add((uint32_t)cnt);
+        const uint64_t nz = __ballot(cnt > 0);
+        const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(nz >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)nz, 0u));
+        if (cnt > 0) {
+            npre[nr + rank] = (int32_t)(off + incl - (uint32_t)cnt);
+            nreg[nr + rank] = (int16_t)r;
+        }
+        off += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        nr += (uint32_t)__popcll(nz);
     }
-    if (tid == 0) fail = 0;
-    lds_barrier();
-    if (ovf) fail = 1;
-    // the non-empty regions, in order: npre[i] = first candidate of the i-th
-    // one, nreg[i] = its region (so consecutive candidates cross at most one
-    // boundary)
-    const uint32_t off = block_excl_scan((uint32_t)cv, sh.wtot);
-    const uint32_t nz = block_excl_scan(cv > 0 ? 1u : 0u, sh.wtot);
-    if (cv > 0) {
-        npre[nz] = (int32_t)off;
-        nreg[nz] = tid;
-    }
-    if (tid == nseg_t - 1) {
-        npre[nz + (cv > 0 ? 1 : 0)] = (int32_t)(off + cv);   // sentinel: the total
-        nnz = (int)nz + (cv > 0 ? 1 : 0);
-    }
-    lds_barrier();
-    const int nr = nnz;
-    const int c = npre[nr];
+    if (l == 0) npre[nr] = (int32_t)off;
+    const int c = (int)off;
     const uint32_t tau = tp.tau[t];
-    // exact only if every key that can be selected is a candidate: no region
-    // overflowed and, with a threshold, at least k keys reached it
-    if (fail || (tau != 0u && c < k) || (tau == 0u && c != n) || c > CAND_SELECT_MAX) {
-        if (tid == 0) {
+    if (__ballot(ovf) != 0ull || (tau != 0u && c < k) || (tau == 0u && c != n) || c > CAND_SELECT_MAX) {
+        if (l == 0) {
             const int slot = atomicAdd(&tp.fb[0], 1);
             tp.fb[FB_LIST + slot] = t;
         }
         return;
     }
-    if (tid == 0) atomicAdd(&tp.fb[2], c);
-    const int64_t rows0 = (int64_t)t * p.nseg;
-    // list entry holding candidate j (j < c): the last i with npre[i] <= j
+    if (l == 0) atomicAdd(&tp.fb[2], c);
+    if (c > SEL_WAVE_MAX) {   // too many for one wave's registers: the workgroup select takes it
+        if (l == 0) {
+            const int slot = atomicAdd(&tp.fb[3], 1);
+            tp.fb[FB_LIST + T + slot] = t;
+        }
+        return;
+    }
+    // lane l: candidates l*R .. l*R + R - 1 (R = ceil(c / 64)), in column order
+    const int R = (c + kWave - 1) / kWave;
+    const int j0 = l * R;
     auto entry_of = [&](int j) {
-        int lo = 0, hi = nr - 1;
+        int lo = 0, hi = (int)nr - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (npre[mid] <= j) lo = mid; else hi = mid - 1;
         }
         return lo;
     };
-    auto slot_of = [&](int j, int e) { return (rows0 + nreg[e]) * p.cap + (j - npre[e]); };
-    if (c == k) {   // every candidate is selected; they are already in column order
-        for (int j = tid; j < k; j += TPB) out[j] = p.cand_pos[slot_of(j, entry_of(j))];
-        return;
-    }
-    // thread tid: candidates 4G*tid .. 4G*tid + 4G - 1 of the row (column order)
-    const int G = (c + 4 * TPB - 1) / (4 * TPB);
-    const int j0 = 4 * G * tid;
-    int e = j0 < c ? entry_of(j0) : 0;
-    uint32_t kr[16], lmin = 0xFFFFFFFFu, lmax = 0u;
+    const int e0 = j0 < c ? entry_of(j0) : 0;
+    const int64_t a_safe = (rows0 + nreg[0]) * p.cap;   // a valid slot (the first candidate)
+    // Slot of each of this lane's candidates, walking the (non-empty) regions
+    // forward: consecutive candidates cross at most one boundary.  The loads
+    // are all issued before any of their values is used.
+    uint32_t kr[SEL_R];
+    if (nr == 1) {   // the whole row in one region (prefill layout): consecutive slots
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int j = j0 + i;
-        const bool in = i / 4 < G && j < c;
-        e += (in && j >= npre[e + 1]) ? 1 : 0;
-        kr[i] = in ? score_key(__uint_as_float(p.cand_key[slot_of(j, e)])) : 0u;
+        for (int i = 0; i < SEL_R; ++i) {
+            const int j = j0 + i;
+            kr[i] = p.cand_key[i < R && j < c ? a_safe + j : a_safe];
+        }
+    } else {
+        int e = e0, bnd = npre[e0 + 1];
+        int64_t dlt = (rows0 + nreg[e0]) * p.cap - npre[e0];
+#pragma unroll
+        for (int i = 0; i < SEL_R; ++i) {
+            const int j = j0 + i;
+            const bool in = i < R && j < c;
+            if (in && j >= bnd) {
+                ++e;
+                bnd = npre[e + 1];
+                dlt = (rows0 + nreg[e]) * p.cap - npre[e];
+            }
+            kr[i] = p.cand_key[in ? dlt + j : a_safe];
+        }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        lmin = kr[i] != 0u && kr[i] < lmin ? kr[i] : lmin;
-        lmax = kr[i] > lmax ? kr[i] : lmax;
+    for (int i = 0; i < SEL_R; ++i) kr[i] = (i < R && j0 + i < c) ? score_key(__uint_as_float(kr[i])) : 0u;
+    // kappa, the k-th largest key.  A 256-bin histogram of the keys by value
+    // over [min, max] (a non-decreasing map, so bins keep the order) names the
+    // bin b1 that holds it; b1's keys (a few dozen on spread-out scores) are
+    // gathered into one register per lane and bisected.  A range that cannot
+    // be binned, or a crowded b1 (many equal scores), takes the bisection over
+    // all keys instead.
+    uint32_t kappa = 0u;
+    bool found = false;
+    {
+        uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
+#pragma unroll
+        for (int i = 0; i < SEL_R; ++i) {
+            lmn = kr[i] != 0u && kr[i] < lmn ? kr[i] : lmn;
+            lmx = kr[i] > lmx ? kr[i] : lmx;
+        }
+        const uint32_t kmin = (uint32_t)__builtin_amdgcn_readlane(
+            (int)wave_scan(lmn, 0xFFFFFFFFu, [](uint32_t a, uint32_t b2) { return a < b2 ? a : b2; }), 63);
+        const uint32_t kmax = (uint32_t)__builtin_amdgcn_readlane(
+            (int)wave_scan(lmx, 0u, [](uint32_t a, uint32_t b2) { return a > b2 ? a : b2; }), 63);
+        const float vmin = key_value(kmin), vmax = key_value(kmax);
+        const float range = vmax - vmin;
+        const float inv = (float)SEL_BINS / range;
+        if (range > 0.f && range < INFINITY && inv < INFINITY) {
+            uint32_t *hist = hist_s[wave];
+#pragma unroll
+            for (int q = 0; q < SEL_BINS / kWave; ++q) hist[q * kWave + l] = 0u;
+            auto bin_of = [&](uint32_t key) {
+                return (uint32_t)fminf((key_value(key) - vmin) * inv, (float)(SEL_BINS - 1));
+            };
+#pragma unroll
+            for (int i = 0; i < SEL_R; ++i)
+                if (kr[i] != 0u) atomicAdd(&hist[bin_of(kr[i])], 1u);
+            // lane l owns bins top - 4l - q (q < 4), scanned from the top
+            uint32_t c4[SEL_BINS / kWave], sum = 0;
+#pragma unroll
+            for (int q = 0; q < SEL_BINS / kWave; ++q) {
+                c4[q] = hist[SEL_BINS - 1 - (SEL_BINS / kWave) * l - q];
+                sum += c4[q];
+            }
+            uint32_t above = wave_excl_add(sum);
+            int my_b1 = -1;
+            uint32_t my_rem = 0;
+#pragma unroll
+            for (int q = 0; q < SEL_BINS / kWave; ++q) {
+                if (above < (uint32_t)k && (uint32_t)k <= above + c4[q]) {
+                    my_b1 = SEL_BINS - 1 - (SEL_BINS / kWave) * l - q;
+                    my_rem = (uint32_t)k - above;
+                }
+                above += c4[q];
+            }
+            const uint64_t own = __ballot(my_b1 >= 0);   // exactly one lane
+            const int src = (int)__builtin_ctzll(own);
+            const uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane(my_b1, src);
+            const uint32_t rem = (uint32_t)__builtin_amdgcn_readlane((int)my_rem, src);
+            const uint32_t nb1 = hist[b1];
+            if (nb1 <= (uint32_t)kWave) {
+                uint32_t *lst = list_s[wave];
+                uint32_t cnt = 0;
+#pragma unroll
+                for (int i = 0; i < SEL_R; ++i) {
+                    const bool inb = kr[i] != 0u && bin_of(kr[i]) == b1;
+                    const uint64_t m = __ballot(inb);
+                    if (inb) {
+                        const uint32_t r2 = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        lst[cnt + r2] = kr[i];
+                    }
+                    cnt += (uint32_t)__popcll(m);
+                }
+                const uint32_t xk = (uint32_t)l < nb1 ? lst[l] : 0u;
+                // the rem-th largest of b1's keys
+                uint32_t x = 0u;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t y = x | (1u << bit);
+                    if ((uint32_t)__popcll(__ballot(xk >= y)) >= rem) x = y;
+                }
+                kappa = x;
+                found = true;
+            }
+        }
     }
-    select_regs<4>(kr, G, lmin, lmax, k, sh, tid, false, [](int) {});
-    // sh.ocol: the selected candidates' indices, ascending (= column order)
-    for (int j = tid; j < k; j += TPB) {
-        const int cj = sh.ocol[j];
-        out[j] = p.cand_pos[slot_of(cj, entry_of(cj))];
+    if (!found) {
+        // the largest x with #(keys >= x) >= k, i.e. the k-th largest key
+        uint32_t x = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t y = x | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < SEL_R; ++i) cnt += __popcll(__ballot(kr[i] >= y));
+            if (cnt >= k) x = y;
+        }
+        kappa = x;
+    }
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < SEL_R; ++i) {
+        gt += kr[i] > kappa ? 1u : 0u;
+        eq += kr[i] == kappa ? 1u : 0u;
+    }
+    // keys == kappa taken in column order until k are selected
+    const uint32_t gt_all = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_add(gt), 63);
+    const uint32_t need_eq = (uint32_t)k - gt_all;
+    const uint32_t eq_before = wave_excl_add(eq);
+    uint32_t eq_take = need_eq > eq_before ? need_eq - eq_before : 0u;
+    eq_take = eq_take < eq ? eq_take : eq;
+    uint32_t slot = wave_excl_add(gt + eq_take);
+    // selected candidates as a bit mask, then their positions (loads first,
+    // into the key registers), then the ascending writes
+    uint64_t take = 0ull;
+#pragma unroll
+    for (int i = 0; i < SEL_R; ++i) {
+        bool tk = kr[i] > kappa;
+        if (kr[i] == kappa && eq_take != 0u) {
+            tk = true;
+            --eq_take;
+        }
+        take |= (uint64_t)(tk ? 1u : 0u) << i;
+    }
+    if (nr == 1) {
+#pragma unroll
+        for (int i = 0; i < SEL_R; ++i) kr[i] = (uint32_t)p.cand_pos[(take >> i) & 1ull ? a_safe + j0 + i : a_safe];
+    } else {
+        int e = e0, bnd = npre[e0 + 1];
+        int64_t dlt = (rows0 + nreg[e0]) * p.cap - npre[e0];
+#pragma unroll
+        for (int i = 0; i < SEL_R; ++i) {
+            const int j = j0 + i;
+            const bool in = i < R && j < c;
+            if (in && j >= bnd) {
+                ++e;
+                bnd = npre[e + 1];
+                dlt = (rows0 + nreg[e]) * p.cap - npre[e];
+            }
+            kr[i] = (uint32_t)p.cand_pos[(take >> i) & 1ull ? dlt + j : a_safe];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < SEL_R; ++i)
+        if ((take >> i) & 1ull) out[slot++] = (int32_t)kr[i];
+}
+
+// cand_select_kernel: the register select of select_core.h over one row's
+// candidates (up to 16384) per 1024-thread workgroup.  Two modes: every row
+// (grid = rows; batches of few rows, e.g. decode, where one workgroup per row
+// is faster than one wave), with the completeness checks; or the rows the wave
+// select queued (persistent workgroups, checks already done).  The candidates
+// are loaded 4G per thread (G <= 4); positions are looked up afterwards.
+__global__ __launch_bounds__(TPB, 2) void cand_select_kernel(IdxTopkParams tp, int T, int from_queue) {
+    const IndexerParams &p = tp.ix;
+    __shared__ SelectShared sh;
+    __shared__ int32_t npre[MAX_SEG + 1];
+    __shared__ int16_t nreg[MAX_SEG];
+    __shared__ int next, nnz, fail;
+    const int tid = threadIdx.x, k = tp.k;
+    const int queued = from_queue ? *static_cast<volatile int32_t *>(&tp.fb[3]) : 1;
+    if (queued == 0) return;
+    for (int it = 0;; ++it) {
+        int t;
+        if (from_queue) {
+            if (tid == 0) next = atomicAdd(&tp.fb[4], 1);
+            lds_barrier();
+            const int qi = next;
+            lds_barrier();
+            if (qi >= queued) break;
+            t = tp.fb[FB_LIST + T + qi];
+        } else {
+            if (it > 0) break;
+            t = blockIdx.x;
+        }
+        const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+        const int n = ri.nvis;
+        int32_t *out = tp.idx + (int64_t)t * k;
+        if (n <= k) {   // (every-row mode) every visible key, ascending, then -1
+            for (int j = tid; j < k; j += TPB) out[j] = j < n ? j : -1;
+            continue;
+        }
+        const int nseg_t = (n + p.seg_w - 1) / p.seg_w;
+        const int64_t rows0 = (int64_t)t * p.nseg;
+        int cv = tid < nseg_t ? p.cand_cnt[rows0 + tid] : 0;
+        const bool ovf = cv > p.cap || cv < 0;
+        cv = ovf ? 0 : cv;
+        if (tid == 0) fail = 0;
+        lds_barrier();
+        if (ovf) fail = 1;
+        const uint32_t off = block_excl_scan((uint32_t)cv, sh.wtot);
+        const uint32_t nz = block_excl_scan(cv > 0 ? 1u : 0u, sh.wtot);
+        if (cv > 0) {
+            npre[nz] = (int32_t)off;
+            nreg[nz] = (int16_t)tid;
+        }
+        if (tid == nseg_t - 1) {
+            npre[nz + (cv > 0 ? 1 : 0)] = (int32_t)(off + cv);
+            nnz = (int)nz + (cv > 0 ? 1 : 0);
+        }
+        lds_barrier();
+        const int nr = nnz;
+        const int c = npre[nr];
+        if (!from_queue) {
+            // exact only if every key that can be selected is a candidate
+            const uint32_t tau = tp.tau[t];
+            if (fail || (tau != 0u && c < k) || (tau == 0u && c != n) || c > CAND_SELECT_MAX) {
+                if (tid == 0) {
+                    const int slot = atomicAdd(&tp.fb[0], 1);
+                    tp.fb[FB_LIST + slot] = t;
+                }
+                continue;
+            }
+            if (tid == 0) atomicAdd(&tp.fb[2], c);
+        }
+        auto entry_of = [&](int j) {
+            int lo = 0, hi = nr - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (npre[mid] <= j) lo = mid; else hi = mid - 1;
+            }
+            return lo;
+        };
+        auto slot_of = [&](int j, int e) { return (rows0 + nreg[e]) * p.cap + (j - npre[e]); };
+        // thread tid: candidates 4G*tid .. 4G*tid + 4G - 1 of the row (column order)
+        const int G = (c + 4 * TPB - 1) / (4 * TPB);
+        const int j0 = 4 * G * tid;
+        int e = j0 < c ? entry_of(j0) : 0;
+        uint32_t kr[16], lmin = 0xFFFFFFFFu, lmax = 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = j0 + i;
+            const bool in = i / 4 < G && j < c;
+            e += (in && j >= npre[e + 1]) ? 1 : 0;
+            kr[i] = in ? score_key(__uint_as_float(p.cand_key[slot_of(j, e)])) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            lmin = kr[i] != 0u && kr[i] < lmin ? kr[i] : lmin;
+            lmax = kr[i] > lmax ? kr[i] : lmax;
+        }
+        select_regs<4>(kr, G, lmin, lmax, k, sh, tid, false, [](int) {});
+        // sh.ocol: the selected candidates' indices, ascending (= column order)
+        for (int j = tid; j < k; j += TPB) {
+            const int cj = sh.ocol[j];
+            out[j] = p.cand_pos[slot_of(cj, entry_of(cj))];
+        }
+        lds_barrier();   // sh, npre free for the next row
     }
 }
 
@@ -314,6 +662,7 @@ __global__ __launch_bounds__(TPB) void idx_fallback_kernel(IdxTopkParams tp) {
     const int tid = threadIdx.x, k = tp.k;
     const int wave = tid >> 6, l = lane_id();
     const int queued = *static_cast<volatile int32_t *>(&tp.fb[0]);
+    if (queued == 0) return;   // (the usual case: every row's candidates were complete)
     for (;;) {
         if (tid == 0) next = atomicAdd(&tp.fb[1], 1);
         lds_barrier();
@@ -421,17 +770,19 @@ hipError_t launch_indexer_topk(const IdxTopkParams &tp, int T, int max_q, bool d
     if (T <= 0) return hipSuccess;
     const IndexerParams &p = tp.ix;
     if (p.nseg * p.seg_w < p.max_kv || p.nseg > MAX_SEG) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(indexer_sample_kernel, dim3((max_q + ST_ROWS - 1) / ST_ROWS, 1, p.B), dim3(512), 0, s, tp);
+    if (decode_variant) {
+        hipLaunchKernelGGL(indexer_sample_row_kernel, dim3(T), dim3(512), 0, s, tp);
+    } else {
+        hipLaunchKernelGGL(indexer_sample_kernel, dim3((max_q + ST_ROWS - 1) / ST_ROWS, 1, p.B), dim3(512), 0, s,
+                           tp);
+    }
     hipError_t e = hipGetLastError();
-    if (marks) marks->after("indexer_sample_kernel", s);
+    if (marks) marks->after(decode_variant ? "indexer_sample_row_kernel" : "indexer_sample_kernel", s);
     if (e != hipSuccess) return e;
     if (p.max_kv > 0) {
         if ((e = launch_indexer_cand(p, T, max_q, decode_variant, s)) != hipSuccess) return e;
         if (marks) marks->after(decode_variant ? "indexer_decode_kernel<cand>" : "indexer_prefill_kernel<cand>", s);
     }
-    hipLaunchKernelGGL(cand_select_kernel, dim3(T), dim3(TPB), 0, s, tp);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (marks) marks->after("cand_select_kernel", s);
     static int ncu = 0;
     if (ncu == 0) {
         int dev = 0, nn = 0;
@@ -439,6 +790,21 @@ hipError_t launch_indexer_topk(const IdxTopkParams &tp, int T, int max_q, bool d
             hipDeviceGetAttribute(&nn, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || nn <= 0)
             nn = 256;
         ncu = nn;
+    }
+    if (T <= SEL_BLOCK_ROWS * ncu) {
+        // few rows: one workgroup per row
+        hipLaunchKernelGGL(cand_select_kernel, dim3(T), dim3(TPB), 0, s, tp, T, 0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (marks) marks->after("cand_select_kernel", s);
+    } else {
+        // many rows: one wave per row; rows with too many candidates for a wave queued
+        hipLaunchKernelGGL(cand_select_wave_kernel, dim3((T + SEL_WAVES - 1) / SEL_WAVES), dim3(64 * SEL_WAVES), 0,
+                           s, tp, T);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (marks) marks->after("cand_select_wave_kernel", s);
+        hipLaunchKernelGGL(cand_select_kernel, dim3(T < 2 * ncu ? T : 2 * ncu), dim3(TPB), 0, s, tp, T, 1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (marks) marks->after("cand_select_kernel", s);
     }
     hipLaunchKernelGGL(idx_fallback_kernel, dim3(T < ncu ? T : ncu), dim3(TPB), 0, s, tp);
     e = hipGetLastError();

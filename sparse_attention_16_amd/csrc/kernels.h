@@ -45,10 +45,11 @@ struct IdxTopkParams {
     uint32_t *tau;          // [T] written by the sample kernel (same array as ix.tau)
     int k;
     int32_t *idx;           // [T, k] out
-    int32_t *fb;            // [FB_LIST + T]: rows queued for the recompute, next queue entry,
-                            // candidates selected over (all rows), then the queued rows
+    int32_t *fb;            // [FB_LIST + 2T]: recompute queue (count, next), candidates selected
+                            // over (all rows), workgroup-select queue (count, next), then the
+                            // recompute queue's rows [T] and the workgroup-select queue's rows [T]
 };
-constexpr int FB_LIST = 3;
+constexpr int FB_LIST = 5;
 
 struct TopkParams {
     const int32_t *cu_q;

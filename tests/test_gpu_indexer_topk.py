@@ -159,3 +159,43 @@ def test_indexer_topk_workspace_and_validation(dsa):
     with pytest.raises(dsa.DsaError) as e:
         dsa.indexer_topk(d.batch, d.qi, d.qs, d.w, d.ki, d.ks, inp.k, idx, ws=small)
     assert e.value.status == dsa.DSA_ERR_WORKSPACE
+
+
+def _wave_case(name):
+    """Batches of more than 4 rows per compute unit, which take the select with
+    one wave per row: 1100 query rows at the end of a context."""
+    if name == "spread":          # ~3k candidates per row: the histogram path
+        return synth.make_inputs(synth.Batch.prefill(1100, 6000, 4900), seed=161, k=2048), None
+    if name == "ties_1000":       # every score repeated ~6 times: exact ties around the k-th
+        return synth.make_inputs(synth.Batch.prefill(1100, 6000, 4900), seed=162, k=2048), 1000
+    if name == "ties_3_k64":      # three distinct scores per row: candidates all equal, no value bins
+        return synth.make_inputs(synth.Batch.prefill(1100, 6000, 4900), seed=163, k=64), 3
+    if name == "long_rows":       # ~4k+ candidates per row: more than one wave holds, the workgroup select
+        return synth.make_inputs(synth.Batch.prefill(1100, 90000, 88900), seed=164, k=2048), None
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["spread", "ties_1000", "ties_3_k64", "long_rows"])
+def test_indexer_topk_wave_select(dsa, name):
+    say(f"[indexer_topk wave select] {name}")
+    inp, period = _wave_case(name)
+    if period is not None:
+        inp.ki[:] = inp.ki[np.arange(inp.ki.shape[0]) % period]
+        inp.ki_scale[:] = inp.ki_scale[np.arange(inp.ki.shape[0]) % period]
+    b = inp.batch
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert b.T > 4 * ncu or ncu != 256
+    d = DevInputs(inp, dsa)
+    idx = torch.full((b.T, inp.k), -7, dtype=torch.int32, device="cuda")
+    dsa.indexer_topk(d.batch, d.qi, d.qs, d.w, d.ki, d.ks, inp.k, idx)
+    idx3 = _three_steps(dsa, d, b, inp.k)
+    torch.cuda.synchronize()
+    g, g3 = idx.cpu().numpy(), idx3.cpu().numpy()
+    assert np.array_equal(g, g3), f"{name}: {np.sum(np.any(g != g3, axis=1))} rows differ from the three steps"
+    rows = np.array([0, 1, 517, b.T - 2, b.T - 1])
+    ref_s, A = oracle.indexer(b.cu_q, b.cu_kv, b.pos0, inp.qi, inp.qi_scale, inp.w, inp.ki, inp.ki_scale,
+                              rows=rows, want_abs=True)
+    ref_idx = oracle.topk(b.cu_q, b.cu_kv, b.pos0, ref_s, inp.k, rows=rows)
+    _, _, _, _, nvis = oracle.visible(b.cu_q, b.cu_kv, b.pos0)
+    differ = check_idx_sets(g[rows], ref_idx, ref_s, A, nvis[rows], inp.k, name)
+    say(f"  {b.T} rows identical to the three steps; {len(differ)} of {len(rows)} oracle rows differ at near-ties")
