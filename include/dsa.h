@@ -248,6 +248,23 @@ dsa_status dsa_prefill_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse,
 dsa_status dsa_decode_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse,
                           int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 
+/* dsa_decode_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, launches and results as
+ * dsa_decode_fwd (bit for bit); the workspace is a static device array of
+ * the library, dsa_decode_fwd_noalloc_max_bytes() = 128 MiB, one copy per
+ * GPU, held until the process ends (enough for 64 sequences of 128K-token
+ * contexts, or 256 of 32K).  A batch whose dsa_workspace_size(DSA_WS_DECODE,
+ * ...) exceeds it returns DSA_ERR_WORKSPACE before any launch.  The call
+ * allocates nothing: on its first use on a device it looks up that device's
+ * copy of the array (hipGetSymbolAddress).  Every call on a GPU shares that
+ * GPU's array and leaves its last contents there (the kernels clear what they
+ * need cleared): calls that overlap on one GPU (several streams, several host
+ * threads) race, so serialise them. */
+dsa_status dsa_decode_fwd_noalloc(const dsa_fwd_args *args, uint16_t *out, float *lse,
+                                  int32_t *idx_out, void *stream);
+size_t dsa_decode_fwd_noalloc_max_bytes(void);
+
 /* Measurement helper (not part of the hot path's data flow): runs the same
  * launches as dsa_prefill_fwd (decode = 0) or dsa_decode_fwd (decode != 0)
  * with a HIP event recorded on `stream` before the first launch and after

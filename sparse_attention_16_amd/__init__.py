@@ -35,7 +35,7 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 
 EXPORTS = ("dsa_indexer_scores", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_dense_mla_fwd", "dsa_indexer_kl_fwd",
            "dsa_sparse_mla_bwd", "dsa_prefill_fwd",
-           "dsa_decode_fwd", "dsa_fwd_profile", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
+           "dsa_decode_fwd", "dsa_decode_fwd_noalloc", "dsa_decode_fwd_noalloc_max_bytes", "dsa_fwd_profile", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
            "dsa_status_string", "dsa_version")
 
 
@@ -76,6 +76,8 @@ _lib.dsa_indexer_kl_fwd.argtypes = [_BP, _P, _P, _P, _I, _I, _F, _P, _I64, _P, _
 _lib.dsa_sparse_mla_bwd.argtypes = [_BP, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_prefill_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_decode_fwd.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P, _SZ, _P]
+_lib.dsa_decode_fwd_noalloc.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P, _P]
+_lib.dsa_decode_fwd_noalloc_max_bytes.restype = _SZ
 _lib.dsa_fwd_profile.argtypes = [ctypes.POINTER(dsa_fwd_args), _I, _P, _P, _P, _P, _SZ, _P,
                                  ctypes.POINTER(dsa_kernel_time), _I, ctypes.POINTER(ctypes.c_int)]
 _lib.dsa_workspace_size.argtypes = [_I, _BP, _I, _I, _I]
@@ -86,7 +88,7 @@ _lib.dsa_status_string.argtypes = [_I]
 _lib.dsa_status_string.restype = ctypes.c_char_p
 _lib.dsa_version.restype = ctypes.c_char_p
 for _name in ("dsa_indexer_scores", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_fwd",
-              "dsa_decode_fwd", "dsa_fwd_profile"):
+              "dsa_decode_fwd", "dsa_decode_fwd_noalloc", "dsa_fwd_profile"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -280,6 +282,14 @@ def decode_fwd(args: dsa_fwd_args, batch: Batch, out, lse, idx_out=None, ws=None
     """Whole hot path (indexer -> top-k -> sparse MLA), decode-tuned (split-KV)."""
     return _fwd(_lib.dsa_decode_fwd, WS_DECODE, "dsa_decode_fwd", args, batch, out, lse,
                 idx_out, ws, stream)
+
+
+def decode_fwd_noalloc(args: dsa_fwd_args, out, lse, idx_out=None, stream=None):
+    """dsa_decode_fwd on the library's static scratch (no workspace, no
+    allocation; see dsa_decode_fwd_noalloc)."""
+    st = _lib.dsa_decode_fwd_noalloc(ctypes.byref(args), _ptr(out), _ptr(lse), _ptr(idx_out), _stream(stream))
+    _check(st, "dsa_decode_fwd_noalloc")
+    return out, lse
 
 
 def fwd_profile(args: dsa_fwd_args, batch: Batch, out, lse, idx_out=None, ws=None, decode=False, stream=None):

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 namespace {
 
@@ -356,6 +357,31 @@ dsa_status run_fwd(const dsa_fwd_args *a, uint16_t *out, float *lse, int32_t *id
     return hip_status(launch_sparse_mla(mp, b->total_q, s, tl));
 }
 
+// Static scratch of the allocation-free decode entry: device memory that the
+// library owns for the process's lifetime, one copy per GPU (each at its own
+// address).  Host code never passes the array's name to a kernel (on the host
+// it is a stand-in, not a device address): the address is taken once per
+// device with hipGetSymbolAddress, with that device current, and kept.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, or null on a HIP error.
+void *scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -587,6 +613,22 @@ dsa_status dsa_decode_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse, i
                           void *ws, size_t ws_bytes, void *stream) {
     return run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, true);
 }
+
+dsa_status dsa_decode_fwd_noalloc(const dsa_fwd_args *args, uint16_t *out, float *lse, int32_t *idx_out,
+                                  void *stream) {
+    if (!args) return DSA_ERR_INVALID_ARG;
+    dsa_status st = check_batch(&args->batch);
+    if (st != DSA_OK) return st;
+    if ((st = check_k(args->k)) != DSA_OK) return st;
+    if (args->batch.max_kv > kMaxKvTopk) return DSA_ERR_UNSUPPORTED;
+    if (args->batch.total_q == 0) return DSA_OK;
+    if (fwd_ws(&args->batch, args->k, true) > kScratchBytes) return DSA_ERR_WORKSPACE;
+    void *ws = scratch_on_current_device();
+    if (!ws) return DSA_ERR_HIP;
+    return run_fwd(args, out, lse, idx_out, ws, kScratchBytes, stream, true);
+}
+
+size_t dsa_decode_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
 
 dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, float *lse, int32_t *idx_out,
                            void *ws, size_t ws_bytes, void *stream, dsa_kernel_time *times, int max_times,
