@@ -22,7 +22,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dsa_oracle.c")
-_LIB = os.path.join(_HERE, "libdsa_oracle.so")
+# DSA_ORACLE_LIBRARY names another build of dsa_oracle.c (the AddressSanitizer
+# build the CPU tests make); by default the in-tree library is used.
+_ASAN_LIB = os.environ.get("DSA_ORACLE_LIBRARY")
+_IN_TREE_LIB = os.path.join(_HERE, "libdsa_oracle.so")
+_LIB = _ASAN_LIB or _IN_TREE_LIB
 _lib = None
 
 F32, BF16, E4M3 = 0, 1, 2
@@ -30,18 +34,33 @@ F32, BF16, E4M3 = 0, 1, 2
 
 def build(force: bool = True) -> str:
     """Compile dsa_oracle.c into libdsa_oracle.so with gcc (-O2, OpenMP)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+    out = _IN_TREE_LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp%d" % os.getpid()
         subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
                         "-o", tmp, _SRC, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, out)
+    return out
+
+
+def build_asan(out: str) -> str:
+    """Compile dsa_oracle.c with gcc's AddressSanitizer into ``out``.
+
+    The library expects the sanitizer runtime to be loaded first
+    (LD_PRELOAD of gcc's libasan) and is selected with DSA_ORACLE_LIBRARY.
+    """
+    subprocess.run(["gcc", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+                    "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", out, _SRC, "-lm"], check=True)
+    return out
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if _ASAN_LIB:
+            if not os.path.exists(_ASAN_LIB):
+                raise FileNotFoundError(_ASAN_LIB)
+        elif not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         L = ctypes.CDLL(_LIB)
         p, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double

@@ -20,7 +20,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdsa.so")
+# DSA_LIBRARY names another build of the same library (the host-sanitised
+# build the CPU tests make); by default the in-tree libdsa.so is loaded.
+LIB_PATH = os.environ.get("DSA_LIBRARY") or os.path.join(_PKG, "libdsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

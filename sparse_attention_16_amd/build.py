@@ -1,6 +1,7 @@
 """Builds libdsa.so (the gfx950 HIP kernels + the C ABI of include/dsa.h) in-tree.
 
-    python -m sparse_attention_16_amd.build
+    python sparse_attention_16_amd/build.py               # in-tree libdsa.so
+    python sparse_attention_16_amd/build.py --host-asan   # _build/asan/libdsa.so
 """
 from __future__ import annotations
 
@@ -51,5 +52,44 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_asan(out_dir: str) -> str:
+    """Builds the library with AddressSanitizer on its host code only.
+
+    The device code is compiled as usual (the sanitizer does not reach it);
+    the host side (argument validation, workspace sizing, launch set-up) is
+    instrumented.  Load it with the sanitizer runtime preloaded (clang's
+    libclang_rt.asan) and select it with DSA_LIBRARY.  The sources are
+    compiled in parallel, one process per file.
+    """
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f not in ("-O3", "-shared")]
+    flags += ["-O1", "-g", "-Xarch_host", "-fsanitize=address",
+              "-Xarch_host", "-fno-omit-frame-pointer"]
+    procs, objs = [], []
+    for src in sources():
+        obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+        objs.append(obj)
+        procs.append(subprocess.Popen(
+            [hipcc, "-c", *flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC, src, "-o", obj],
+            stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    errs = []
+    for p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            errs.append(out)
+    if errs:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
+    lib = os.path.join(out_dir, "libdsa.so")
+    r = subprocess.run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", lib],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc link failed:\n" + r.stdout + r.stderr)
+    return lib
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-asan" in sys.argv:
+        print(build_host_asan(os.path.join(ROOT, "_build", "asan")))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -10,7 +10,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LIB = os.path.join(ROOT, "sparse_attention_16_amd", "libdsa.so")
+LIB = os.environ.get("DSA_LIBRARY") or os.path.join(ROOT, "sparse_attention_16_amd", "libdsa.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdsa.so not built")
 
