@@ -26,7 +26,9 @@
 //             each slot's 576 sums, rounded to bf16 into a workspace;
 //   bwd_count, bwd_scan_*, bwd_scatter: the chunk's usable slots sorted by
 //             cache row (counting sort);
-//   bwd_reduce: per cache row, its listed sums added in fp32 into dkv.
+//   bwd_reduce: per cache row, its listed sums added in fp32 into dkv in
+//             ascending slot order (the list sorted first), so dkv is the
+//             same bit for bit on every run.
 // (fp32 atomic adds of every slot's sums into dkv were bound by the atomic
 // rate: 3.75e10 adds at 32K take 113 ms; this route moves 2 x 1152 bytes
 // per slot through memory instead.)
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(256) void bwd_scan_add_kernel(int32_t *x, int64_t n
 }
 
 // The chunk's usable slots listed by cache row (order within a row is the
-// order the atomics land in).
+// order the atomics land in; the reduce sorts each row's list first).
 __global__ __launch_bounds__(256) void bwd_scatter_kernel(BwdParams p) {
     const int t = p.t0 + (int)blockIdx.x;
     const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
@@ -565,27 +567,76 @@ __global__ __launch_bounds__(256) void bwd_scatter_kernel(BwdParams p) {
     }
 }
 
+constexpr int RED_T = 128;        // threads of the reduce workgroup
+constexpr int SORT_CAP = 4096;    // longest list sorted in LDS (16 KB)
+
+// Ascending sort of a[0 .. m) by the workgroup (bitonic network over the next
+// power of two P >= m, with every comparator putting the smaller value at the
+// lower index: the first step of each merge pairs i with its mirror i ^ (kk-1),
+// the later ones i with i + jj).  The positions m .. P are taken as +inf and
+// never touched: a comparator whose upper element lies there already holds
+// the smaller value below.  sync() orders each step's accesses before the next.
+template <typename Ptr, typename Sync>
+__device__ __forceinline__ void sort_ascending(Ptr a, int m, Sync sync) {
+    int P = 1;
+    while (P < m) P <<= 1;
+    for (int kk = 2; kk <= P; kk <<= 1) {
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+            const int lg = 31 - __builtin_clz(jj);
+            for (int c = (int)threadIdx.x; c < (P >> 1); c += RED_T) {
+                const int i = ((c >> lg) << (lg + 1)) + (c & (jj - 1));
+                const int u = jj == (kk >> 1) ? (i ^ (kk - 1)) : i + jj;
+                if (u < m) {
+                    const int32_t x = a[i], y = a[u];
+                    if (y < x) {
+                        a[i] = y;
+                        a[u] = x;
+                    }
+                }
+            }
+            sync();
+        }
+    }
+}
+
 // dkv[s, :] += the chunk's listed contributions to cache row s, summed in
-// fp32 (one workgroup per cache row; threads 0..71 own 8 dims each).
-__global__ __launch_bounds__(128) void bwd_reduce_kernel(BwdParams p) {
+// fp32 in ascending slot order (the list is sorted first, so the sums and
+// their rounding do not depend on the order the scatter's atomics landed in):
+// one workgroup per cache row, threads 0..71 own 8 dims each.  Lists up to
+// SORT_CAP entries are sorted in LDS, longer ones (only rows selected by
+// more than 4096 slots of the chunk, i.e. repeated positions) in place.
+__global__ __launch_bounds__(RED_T) void bwd_reduce_kernel(BwdParams p) {
+    __shared__ int32_t srt[SORT_CAP];
     const int64_t s = blockIdx.x;
     const int32_t beg = p.cnt[s], end = p.cnt[s + 1];
-    if (beg == end || threadIdx.x >= D / 8) return;
+    const int m = end - beg;
+    if (m <= 0) return;
+    const int32_t *lst;
+    if (m <= SORT_CAP) {
+        for (int i = (int)threadIdx.x; i < m; i += RED_T) srt[i] = p.list[beg + i];
+        lds_barrier();
+        if (m > 1) sort_ascending(srt, m, [] { lds_barrier(); });
+        lst = srt;
+    } else {
+        sort_ascending(p.list + beg, m, [] { __syncthreads(); });
+        lst = p.list + beg;
+    }
+    if (threadIdx.x >= D / 8) return;
     const int d0 = 8 * (int)threadIdx.x;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int32_t i = beg;
-    for (; i + 4 <= end; i += 4) {
+    int i = 0;
+    for (; i + 4 <= m; i += 4) {
         bf16x8 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            v[u] = *reinterpret_cast<const bf16x8 *>(p.g + (int64_t)p.list[i + u] * D + d0);
+            v[u] = *reinterpret_cast<const bf16x8 *>(p.g + (int64_t)lst[i + u] * D + d0);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e];
     }
-    for (; i < end; ++i) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p.g + (int64_t)p.list[i] * D + d0);
+    for (; i < m; ++i) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p.g + (int64_t)lst[i] * D + d0);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
     }
@@ -624,7 +675,7 @@ hipError_t launch_sparse_mla_bwd(const BwdParams &p0, int T, hipStream_t s) {
             hipLaunchKernelGGL(bwd_scan_totals_kernel, dim3(1), dim3(1024), 0, s, p.bsum, (int)nb);
             hipLaunchKernelGGL(bwd_scan_add_kernel, dim3(nb), dim3(256), 0, s, p.cnt, nscan, p.bsum, p.cur, N);
             hipLaunchKernelGGL(bwd_scatter_kernel, dim3(p.tc), dim3(256), 0, s, p);
-            hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)N), dim3(128), 0, s, p);
+            hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)N), dim3(RED_T), 0, s, p);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
