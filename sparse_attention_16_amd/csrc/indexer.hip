@@ -198,7 +198,8 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
 // waves split the chunk into 64-key groups (wave w: groups w, w+4, ...).  A
 // key is used by a single query row, so nothing is shared: each wave streams
 // its own groups, DC_NBUF deep, into a private LDS ring with direct-to-LDS
-// loads (no registers held while they fly, no barriers), then reads each
+// loads (no registers held while they fly, no barriers; non-temporal, as
+// each key is read once), then reads each
 // 16-key B operand back as two 16-byte LDS reads.  Every load moves one
 // contiguous KB (8 key rows) in its natural order, so each touches the fewest
 // cache lines; the operand layout comes from the LDS reads.  Grid: x = query
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerPa
         for (int j = 0; j < 8; ++j) {   // keys 8j .. 8j+7 of the group, lane l: key 8j + l/8, bytes 16*(l%8)
             const int key = g0 + 8 * j + (l >> 3);
             const uint32_t kk = (uint32_t)(key < comp_end ? key : c0);
-            dma_b128(kbase, kk * DI + 16 * (l & 7), (const DSA_LDS void *)&kst[wave][b][j * 1024]);
+            dma_b128_nt(kbase, kk * DI + 16 * (l & 7), (const DSA_LDS void *)&kst[wave][b][j * 1024]);
         }
         const int key = g0 + l;
         dma_b32(sbase, 4u * (uint32_t)(key < comp_end ? key : c0), (const DSA_LDS void *)&sst[wave][b][0]);

@@ -522,34 +522,52 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
 // Combines split partials: lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) o_s.
 // The partials o_s are normalised and stored in bf16 (half the bytes of the
 // round trip through memory; their rounding, 2^-9 relative, is of the order
-// of the final bf16 rounding of out); the combination runs in fp32.
-// Grid: x = query row, y = pair of heads; 128 threads x 4 value columns per head.
+// of the final bf16 rounding of out); the combination runs in fp32.  A split
+// without usable keys (lse_s = -inf) wrote o_s = 0 and gets weight 0.
+// Grid: x = query row, y = group of 4 heads; 64 threads x 8 value columns per
+// head, the partials of four splits loaded together.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
     const int t = blockIdx.x;
-    const int h = 2 * blockIdx.y + (threadIdx.x >> 7);
-    const int c = 4 * (threadIdx.x & 127);
+    const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+    const int c = 8 * (threadIdx.x & 63);
     const int S = p.splits;
     const float *lp = p.lse_part + (int64_t)t * S * H + h;
     float mx = -INFINITY;
     for (int s = 0; s < S; ++s) mx = fmaxf(mx, lp[(int64_t)s * H]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float L = -INFINITY;
     if (mx != -INFINITY) {
         float den = 0.f;
         for (int s = 0; s < S; ++s) den += expf(lp[(int64_t)s * H] - mx);
         L = mx + logf(den);
-        for (int s = 0; s < S; ++s) {
+        const uint16_t *op = p.o_part + ((int64_t)t * S * H + h) * DV + c;
+        auto weight = [&](int s) {
             const float ls = lp[(int64_t)s * H];
-            if (ls == -INFINITY) continue;
-            const bf16x4 v = *reinterpret_cast<const bf16x4 *>(
-                p.o_part + (((int64_t)t * S + s) * H + h) * DV + c);
-            const float wgt = expf(ls - L);
-            acc += f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]} * wgt;
+            return ls == -INFINITY ? 0.f : expf(ls - L);
+        };
+        int s = 0;
+        for (; s + 4 <= S; s += 4) {
+            bf16x8 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const bf16x8 *>(op + (int64_t)(s + u) * H * DV);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float wgt = weight(s + u);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e] * wgt;
+            }
+        }
+        for (; s < S; ++s) {
+            const bf16x8 v = *reinterpret_cast<const bf16x8 *>(op + (int64_t)s * H * DV);
+            const float wgt = weight(s);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += (float)v[e] * wgt;
         }
     }
-    const bf16x4 v = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
-    *reinterpret_cast<bf16x4 *>(p.out + ((int64_t)t * H + h) * DV + c) = v;
-    if ((threadIdx.x & 127) == 0) p.lse[(int64_t)t * H + h] = L;
+    const bf16x8 v = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3],
+                      (__bf16)acc[4], (__bf16)acc[5], (__bf16)acc[6], (__bf16)acc[7]};
+    *reinterpret_cast<bf16x8 *>(p.out + ((int64_t)t * H + h) * DV + c) = v;
+    if ((threadIdx.x & 63) == 0) p.lse[(int64_t)t * H + h] = L;
 }
 
 hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s, LaunchMarks *m) {
@@ -559,7 +577,7 @@ hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s, LaunchMar
     hipError_t e = hipGetLastError();
     if (m) m->after("sparse_mla_kernel", s);
     if (e != hipSuccess || p.splits == 1) return e;
-    hipLaunchKernelGGL(mla_merge_kernel, dim3(T, H / 2), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(mla_merge_kernel, dim3(T, H / 4), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (m) m->after("mla_merge_kernel", s);
     return e;
