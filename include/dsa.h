@@ -31,6 +31,13 @@
  *    OCP format, max 448); query heads H = 128 over D = 576 bf16 dims
  *    (512 latent + 64 rope), value = the first Dv = 512 dims; 1 <= k <= 2048.
  *    Anything else returns DSA_ERR_UNSUPPORTED.
+ *  * Diagnostics, read from the environment at every call: DSA_LOG=1 prints
+ *    one line per call on stderr (batch, k, workspace given, the fused
+ *    entries' launch plan, the status); DSA_DEBUG_CHECKS=1 validates every
+ *    selection an entry produces (dsa_topk, dsa_indexer_topk, the fused
+ *    entries) with dsa_check_selection, which drains the stream, and returns
+ *    DSA_ERR_CHECK if a row breaks the contract.  Both are off by default and
+ *    have no place under graph capture.
  *  * Every `scale` argument (the softmax scale of the attention) must be
  *    finite and > 0, else DSA_ERR_INVALID_ARG.
  *  * Positions: score columns and idx entries are positions local to their
@@ -53,7 +60,9 @@ typedef enum {
     DSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, stride or alignment */
     DSA_ERR_UNSUPPORTED = 2,   /* shape outside the supported set above */
     DSA_ERR_WORKSPACE = 3,     /* workspace null or smaller than required */
-    DSA_ERR_HIP = 4            /* the HIP runtime rejected a launch */
+    DSA_ERR_HIP = 4,           /* the HIP runtime rejected a launch */
+    DSA_ERR_CHECK = 5          /* debug mode (DSA_DEBUG_CHECKS) found an output that
+                                  breaks its contract */
 } dsa_status;
 
 /* Ragged batch of B sequences.  The scalars are host values (used for
@@ -285,6 +294,17 @@ typedef struct {
 dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, float *lse,
                            int32_t *idx_out, void *ws, size_t ws_bytes, void *stream,
                            dsa_kernel_time *times, int max_times, int *n_times);
+
+/* Validation of a selection against the contract of Top-k ([R] "Отбор и
+ * основное внимание": the k top-scored visible keys of each query row):
+ * every row t of idx [T, k] int32 (device) must hold exactly min(k, n_t)
+ * positions, strictly ascending and inside 0..n_t-1 (n_t = the row's visible
+ * keys), then -1 in the remaining slots.  Writes the number of rows that do
+ * not to *bad_rows (host memory).  The call WAITS for `stream` (it reads the
+ * count back); the count lives in a small static device variable of the
+ * library, so concurrent calls on one GPU race.  This is the check that
+ * DSA_DEBUG_CHECKS=1 runs after every entry that selects. */
+dsa_status dsa_check_selection(const dsa_batch *batch, const int32_t *idx, int k, void *stream, int *bad_rows);
 
 /* FP8 quantisation of the indexer queries, the step before the index score
  * ([R] "Молниеносный индексатор": the indexer runs on FP8 values).  Per

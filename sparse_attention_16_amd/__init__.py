@@ -8,7 +8,7 @@ library is missing: there is no fallback implementation.
 
 Entry points (same names as the C ABI, without the ``dsa_`` prefix):
     indexer_scores, indexer_topk, topk, sparse_mla_fwd, dense_mla_fwd, indexer_kl_fwd, sparse_mla_bwd, prefill_fwd,
-    decode_fwd, fwd_profile (measurement helper),
+    decode_fwd, fwd_profile (measurement helper), check_selection (validation),
     quantize_queries, append_cache,
     workspace_size, status_string, version
 """
@@ -31,13 +31,14 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP, DSA_ERR_CHECK = range(6)
 (WS_TOPK, WS_SPARSE_MLA, WS_PREFILL, WS_DECODE, WS_DENSE_MLA, WS_INDEXER_KL, WS_SPARSE_MLA_BWD,
  WS_INDEXER_TOPK) = range(8)
 
 EXPORTS = ("dsa_indexer_scores", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_dense_mla_fwd", "dsa_indexer_kl_fwd",
            "dsa_sparse_mla_bwd", "dsa_prefill_fwd",
-           "dsa_decode_fwd", "dsa_decode_fwd_noalloc", "dsa_decode_fwd_noalloc_max_bytes", "dsa_fwd_profile", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
+           "dsa_decode_fwd", "dsa_decode_fwd_noalloc", "dsa_decode_fwd_noalloc_max_bytes", "dsa_fwd_profile",
+           "dsa_check_selection", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
            "dsa_status_string", "dsa_version")
 
 
@@ -82,6 +83,7 @@ _lib.dsa_decode_fwd_noalloc.argtypes = [ctypes.POINTER(dsa_fwd_args), _P, _P, _P
 _lib.dsa_decode_fwd_noalloc_max_bytes.restype = _SZ
 _lib.dsa_fwd_profile.argtypes = [ctypes.POINTER(dsa_fwd_args), _I, _P, _P, _P, _P, _SZ, _P,
                                  ctypes.POINTER(dsa_kernel_time), _I, ctypes.POINTER(ctypes.c_int)]
+_lib.dsa_check_selection.argtypes = [_BP, _P, _I, _P, ctypes.POINTER(ctypes.c_int)]
 _lib.dsa_workspace_size.argtypes = [_I, _BP, _I, _I, _I]
 _lib.dsa_quantize_queries.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
 _lib.dsa_append_cache.argtypes = [_P, _P, _I64, _I, _I, _P, _P, _P, _P, _I64, _P]
@@ -307,6 +309,16 @@ def fwd_profile(args: dsa_fwd_args, batch: Batch, out, lse, idx_out=None, ws=Non
                               nbytes, _stream(stream), times, 16, ctypes.byref(n))
     _check(st, "dsa_fwd_profile")
     return [(times[i].kernel.decode(), float(times[i].ms), int(times[i].items)) for i in range(n.value)]
+
+
+def check_selection(batch: Batch, idx, k: int = None, stream=None) -> int:
+    """Rows of idx [T, k] that break the top-k selection contract (see
+    dsa_check_selection; waits for the stream)."""
+    k = idx.shape[1] if k is None else k
+    bad = ctypes.c_int(-1)
+    st = _lib.dsa_check_selection(ctypes.byref(batch.c), _ptr(idx), int(k), _stream(stream), ctypes.byref(bad))
+    _check(st, "dsa_check_selection")
+    return bad.value
 
 
 def raw_lib():

@@ -4,6 +4,9 @@
 #include "kernels.h"
 
 #include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -299,6 +302,60 @@ struct Timeline final : LaunchMarks {
 // slot's -inf logit times a scale <= 0 is NaN or +inf.
 bool valid_scale(float scale) { return std::isfinite(scale) && scale > 0.f; }
 
+// Diagnostics, switched on from the environment and read at every call:
+//   DSA_LOG=1           one line per entry call on stderr: the batch, k, the
+//                       workspace given, the launch plan of the fused entries
+//                       and the status returned;
+//   DSA_DEBUG_CHECKS=1  every selection an entry produces (dsa_topk,
+//                       dsa_indexer_topk, the fused entries) is validated on
+//                       the device; a row that is not min(k, visible)
+//                       ascending visible positions followed by -1 makes the
+//                       call return DSA_ERR_CHECK.  The check drains the
+//                       stream, so it has no place under graph capture.
+bool env_flag(const char *name) {
+    const char *v = std::getenv(name);
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
+std::mutex g_log_mu;
+
+void log_line(const char *fmt, ...) {
+    std::lock_guard<std::mutex> lock(g_log_mu);
+    va_list ap;
+    va_start(ap, fmt);
+    std::fputs("[dsa] ", stderr);
+    std::vfprintf(stderr, fmt, ap);
+    std::fputc('\n', stderr);
+    va_end(ap);
+}
+
+template <typename F>
+dsa_status traced(const char *entry, const dsa_batch *b, int k, size_t ws_bytes, F &&body) {
+    const dsa_status st = body();
+    if (env_flag("DSA_LOG")) {
+        if (b)
+            log_line("%s B=%d total_q=%d max_q=%d max_kv=%d total_kv=%lld k=%d ws=%zu -> %s", entry, b->batch,
+                     b->total_q, b->max_q, b->max_kv, (long long)b->total_kv, k, ws_bytes, dsa_status_string(st));
+        else
+            log_line("%s -> %s", entry, dsa_status_string(st));
+    }
+    return st;
+}
+
+dsa_status debug_check(const char *entry, const dsa_batch *b, const int32_t *idx, int k, hipStream_t s) {
+    if (!env_flag("DSA_DEBUG_CHECKS") || b->total_q <= 0) return DSA_OK;
+    int bad = 0;
+    if (check_selection(b->cu_q, b->cu_kv, b->pos0, b->batch, b->total_kv, b->max_kv, b->total_q, idx, k, s,
+                        &bad) != hipSuccess)
+        return DSA_ERR_HIP;
+    if (bad > 0) {
+        log_line("%s: debug check: %d of %d rows break the selection contract", entry, bad, b->total_q);
+        return DSA_ERR_CHECK;
+    }
+    if (env_flag("DSA_LOG")) log_line("%s: debug check: %d rows ok", entry, b->total_q);
+    return DSA_OK;
+}
+
 dsa_status check_k(int k) {
     if (k < 1 || k > kKMax) return DSA_ERR_UNSUPPORTED;
     return DSA_OK;
@@ -341,10 +398,14 @@ dsa_status run_fwd(const dsa_fwd_args *a, uint16_t *out, float *lse, int32_t *id
     // selecting ("MHA with mask"); the split layout is the one the three-step
     // path uses for this k, so both give the same bits.
     if (b->max_kv <= a->k) {
+        if (env_flag("DSA_LOG"))
+            log_line("%s plan: short mode (every visible key), attention splits %d", decode ? "decode" : "prefill",
+                     mla_splits(b->total_q, a->k));
         if (idx_out) {
             TopkParams tp = make_topk(b, nullptr, 0, a->k, idx_out, nullptr);
             if ((st = hip_status(launch_select_all_visible(tp, b->total_q, s))) != DSA_OK) return st;
             if (tl) tl->after("select_all_visible_kernel", s);
+            if ((st = debug_check("select_all_visible", b, idx_out, a->k, s)) != DSA_OK) return st;
         }
         MlaParams mp = make_mla(b, a->q, a->kv, nullptr, a->k, a->scale, out, lse, mws, 1);
         return hip_status(launch_sparse_mla(mp, b->total_q, s, tl));
@@ -352,7 +413,14 @@ dsa_status run_fwd(const dsa_fwd_args *a, uint16_t *out, float *lse, int32_t *id
 
     // indexer -> top-k with the scores kept on chip (candidates only)
     IdxTopkParams tp = make_idxtopk(b, a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, a->k, idx, cws, decode);
+    if (env_flag("DSA_LOG")) {
+        const CandLayout c = cand_layout(b, a->k, decode);
+        log_line("%s plan: candidate regions of %d columns x %d per row (cap %d), %s select, attention splits %d",
+                 decode ? "decode" : "prefill", c.seg_w, c.nseg, c.cap,
+                 b->total_q <= 4 * device_cus() ? "workgroup" : "wave", mla_splits(b->total_q, a->k));
+    }
     if ((st = hip_status(launch_indexer_topk(tp, b->total_q, b->max_q, decode, s, tl))) != DSA_OK) return st;
+    if ((st = debug_check("indexer_topk", b, idx, a->k, s)) != DSA_OK) return st;
     MlaParams mp = make_mla(b, a->q, a->kv, idx, a->k, a->scale, out, lse, mws);
     return hip_status(launch_sparse_mla(mp, b->total_q, s, tl));
 }
@@ -388,247 +456,293 @@ extern "C" {
 
 dsa_status dsa_quantize_queries(const float *q, int64_t T, int HI, int DI, uint8_t *q_fp8,
                                 float *q_scale, void *stream) {
-    if (HI != kHI || DI != kDI) return DSA_ERR_UNSUPPORTED;
-    if (T < 0) return DSA_ERR_INVALID_ARG;
-    if (T == 0) return DSA_OK;
-    if (T > INT32_MAX) return DSA_ERR_UNSUPPORTED;
-    if (!q || !q_fp8 || !q_scale || !al16(q) || !al16(q_fp8) || !al16(q_scale)) return DSA_ERR_INVALID_ARG;
-    return hip_status(launch_quant_queries(q, T, q_fp8, q_scale, static_cast<hipStream_t>(stream)));
+    return traced("dsa_quantize_queries", nullptr, 0, 0, [&]() -> dsa_status {
+        if (HI != kHI || DI != kDI) return DSA_ERR_UNSUPPORTED;
+        if (T < 0) return DSA_ERR_INVALID_ARG;
+        if (T == 0) return DSA_OK;
+        if (T > INT32_MAX) return DSA_ERR_UNSUPPORTED;
+        if (!q || !q_fp8 || !q_scale || !al16(q) || !al16(q_fp8) || !al16(q_scale)) return DSA_ERR_INVALID_ARG;
+        return hip_status(launch_quant_queries(q, T, q_fp8, q_scale, static_cast<hipStream_t>(stream)));
+    });
 }
 
 dsa_status dsa_append_cache(const float *k_new, const uint16_t *kv_new, int64_t R, int DI, int D,
                             const int64_t *dst_rows, uint8_t *k_fp8, float *k_scale, uint16_t *kv,
                             int64_t N, void *stream) {
-    if (DI != kDI || D != kD) return DSA_ERR_UNSUPPORTED;
-    if (R < 0 || N < 0) return DSA_ERR_INVALID_ARG;
-    if (R == 0) return DSA_OK;
-    if (R > (int64_t)INT32_MAX * 8) return DSA_ERR_UNSUPPORTED;
-    if (!k_new || !dst_rows || !k_fp8 || !k_scale) return DSA_ERR_INVALID_ARG;
-    if ((kv_new == nullptr) != (kv == nullptr)) return DSA_ERR_INVALID_ARG;
-    const void *ptrs[] = {k_new, dst_rows, k_fp8, k_scale};
-    for (const void *p : ptrs)
-        if (!al16(p)) return DSA_ERR_INVALID_ARG;
-    if (kv_new && (!al16(kv_new) || !al16(kv))) return DSA_ERR_INVALID_ARG;
-    return hip_status(launch_append_cache(k_new, kv_new, R, dst_rows, k_fp8, k_scale, kv, N,
-                                          static_cast<hipStream_t>(stream)));
+    return traced("dsa_append_cache", nullptr, 0, 0, [&]() -> dsa_status {
+        if (DI != kDI || D != kD) return DSA_ERR_UNSUPPORTED;
+        if (R < 0 || N < 0) return DSA_ERR_INVALID_ARG;
+        if (R == 0) return DSA_OK;
+        if (R > (int64_t)INT32_MAX * 8) return DSA_ERR_UNSUPPORTED;
+        if (!k_new || !dst_rows || !k_fp8 || !k_scale) return DSA_ERR_INVALID_ARG;
+        if ((kv_new == nullptr) != (kv == nullptr)) return DSA_ERR_INVALID_ARG;
+        const void *ptrs[] = {k_new, dst_rows, k_fp8, k_scale};
+        for (const void *p : ptrs)
+            if (!al16(p)) return DSA_ERR_INVALID_ARG;
+        if (kv_new && (!al16(kv_new) || !al16(kv))) return DSA_ERR_INVALID_ARG;
+        return hip_status(launch_append_cache(k_new, kv_new, R, dst_rows, k_fp8, k_scale, kv, N,
+                                              static_cast<hipStream_t>(stream)));
+    });
 }
 
 dsa_status dsa_indexer_scores(const dsa_batch *batch, const uint8_t *q_fp8, const float *q_scale,
                               const float *w, const uint8_t *k_fp8, const float *k_scale, int HI,
                               int DI, float *scores, int64_t ld, void *stream) {
-    dsa_status st = check_batch(batch);
-    if (st != DSA_OK) return st;
-    if (HI != kHI || DI != kDI) return DSA_ERR_UNSUPPORTED;
-    if (batch->total_q == 0 || batch->max_kv == 0) return DSA_OK;
-    if (!q_fp8 || !q_scale || !w || !k_fp8 || !k_scale || !scores) return DSA_ERR_INVALID_ARG;
-    if (ld < batch->max_kv) return DSA_ERR_INVALID_ARG;
-    const void *ptrs[] = {q_fp8, q_scale, w, k_fp8, k_scale, scores};
-    for (const void *p : ptrs)
-        if (!al16(p)) return DSA_ERR_INVALID_ARG;
-    const bool decode = batch->max_q < 16;
-    IndexerParams p = make_indexer(batch, q_fp8, q_scale, w, k_fp8, k_scale, scores, ld,
-                                   indexer_chunk(batch, decode), 1);
-    return hip_status(launch_indexer(p, batch->total_q, batch->max_q, decode,
-                                     static_cast<hipStream_t>(stream)));
+    return traced("dsa_indexer_scores", batch, 0, 0, [&]() -> dsa_status {
+        dsa_status st = check_batch(batch);
+        if (st != DSA_OK) return st;
+        if (HI != kHI || DI != kDI) return DSA_ERR_UNSUPPORTED;
+        if (batch->total_q == 0 || batch->max_kv == 0) return DSA_OK;
+        if (!q_fp8 || !q_scale || !w || !k_fp8 || !k_scale || !scores) return DSA_ERR_INVALID_ARG;
+        if (ld < batch->max_kv) return DSA_ERR_INVALID_ARG;
+        const void *ptrs[] = {q_fp8, q_scale, w, k_fp8, k_scale, scores};
+        for (const void *p : ptrs)
+            if (!al16(p)) return DSA_ERR_INVALID_ARG;
+        const bool decode = batch->max_q < 16;
+        IndexerParams p = make_indexer(batch, q_fp8, q_scale, w, k_fp8, k_scale, scores, ld,
+                                       indexer_chunk(batch, decode), 1);
+        return hip_status(launch_indexer(p, batch->total_q, batch->max_q, decode,
+                                         static_cast<hipStream_t>(stream)));
+    });
 }
 
 dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld, int k, int32_t *idx,
                     void *ws, size_t ws_bytes, void *stream) {
-    dsa_status st = check_batch(batch);
-    if (st != DSA_OK) return st;
-    if ((st = check_k(k)) != DSA_OK) return st;
-    if (batch->max_kv > kMaxKvTopk) return DSA_ERR_UNSUPPORTED;
-    if (batch->total_q == 0) return DSA_OK;
-    if (!scores || !idx) return DSA_ERR_INVALID_ARG;
-    if (ld < batch->max_kv) return DSA_ERR_INVALID_ARG;
-    if (!al16(scores) || !al16(idx)) return DSA_ERR_INVALID_ARG;
-    const size_t need = topk_ws(batch, k);
-    if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
-    TopkParams p = make_topk(batch, scores, ld, k, idx, ws);
-    return hip_status(launch_topk(p, batch->total_q, static_cast<hipStream_t>(stream)));
+    return traced("dsa_topk", batch, k, ws_bytes, [&]() -> dsa_status {
+        dsa_status st = check_batch(batch);
+        if (st != DSA_OK) return st;
+        if ((st = check_k(k)) != DSA_OK) return st;
+        if (batch->max_kv > kMaxKvTopk) return DSA_ERR_UNSUPPORTED;
+        if (batch->total_q == 0) return DSA_OK;
+        if (!scores || !idx) return DSA_ERR_INVALID_ARG;
+        if (ld < batch->max_kv) return DSA_ERR_INVALID_ARG;
+        if (!al16(scores) || !al16(idx)) return DSA_ERR_INVALID_ARG;
+        const size_t need = topk_ws(batch, k);
+        if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
+        TopkParams p = make_topk(batch, scores, ld, k, idx, ws);
+        if ((st = hip_status(launch_topk(p, batch->total_q, static_cast<hipStream_t>(stream)))) != DSA_OK) return st;
+        return debug_check("dsa_topk", batch, idx, k, static_cast<hipStream_t>(stream));
+    });
 }
 
 dsa_status dsa_indexer_topk(const dsa_batch *batch, const uint8_t *q_fp8, const float *q_scale, const float *w,
                             const uint8_t *k_fp8, const float *k_scale, int HI, int DI, int k, int32_t *idx, void *ws,
                             size_t ws_bytes, void *stream) {
-    dsa_status st = check_batch(batch);
-    if (st != DSA_OK) return st;
-    if (HI != kHI || DI != kDI) return DSA_ERR_UNSUPPORTED;
-    if ((st = check_k(k)) != DSA_OK) return st;
-    if (batch->max_kv > kMaxKvTopk) return DSA_ERR_UNSUPPORTED;
-    if (batch->total_q == 0) return DSA_OK;
-    if (!q_fp8 || !q_scale || !w || !idx) return DSA_ERR_INVALID_ARG;
-    if (batch->total_kv > 0 && (!k_fp8 || !k_scale)) return DSA_ERR_INVALID_ARG;
-    const void *ptrs[] = {q_fp8, q_scale, w, idx};
-    for (const void *p : ptrs)
-        if (!al16(p)) return DSA_ERR_INVALID_ARG;
-    if (batch->total_kv > 0 && (!al16(k_fp8) || !al16(k_scale))) return DSA_ERR_INVALID_ARG;
-    const bool decode = batch->max_q < 16;
-    const size_t need = idxtopk_ws(batch, k, decode);
-    if (!ws || ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
-    IdxTopkParams tp = make_idxtopk(batch, q_fp8, q_scale, w, k_fp8, k_scale, k, idx, ws, decode);
-    return hip_status(launch_indexer_topk(tp, batch->total_q, batch->max_q, decode, static_cast<hipStream_t>(stream)));
+    return traced("dsa_indexer_topk", batch, k, ws_bytes, [&]() -> dsa_status {
+        dsa_status st = check_batch(batch);
+        if (st != DSA_OK) return st;
+        if (HI != kHI || DI != kDI) return DSA_ERR_UNSUPPORTED;
+        if ((st = check_k(k)) != DSA_OK) return st;
+        if (batch->max_kv > kMaxKvTopk) return DSA_ERR_UNSUPPORTED;
+        if (batch->total_q == 0) return DSA_OK;
+        if (!q_fp8 || !q_scale || !w || !idx) return DSA_ERR_INVALID_ARG;
+        if (batch->total_kv > 0 && (!k_fp8 || !k_scale)) return DSA_ERR_INVALID_ARG;
+        const void *ptrs[] = {q_fp8, q_scale, w, idx};
+        for (const void *p : ptrs)
+            if (!al16(p)) return DSA_ERR_INVALID_ARG;
+        if (batch->total_kv > 0 && (!al16(k_fp8) || !al16(k_scale))) return DSA_ERR_INVALID_ARG;
+        const bool decode = batch->max_q < 16;
+        const size_t need = idxtopk_ws(batch, k, decode);
+        if (!ws || ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
+        IdxTopkParams tp = make_idxtopk(batch, q_fp8, q_scale, w, k_fp8, k_scale, k, idx, ws, decode);
+        if ((st = hip_status(launch_indexer_topk(tp, batch->total_q, batch->max_q, decode,
+                                                 static_cast<hipStream_t>(stream)))) != DSA_OK)
+            return st;
+        return debug_check("dsa_indexer_topk", batch, idx, k, static_cast<hipStream_t>(stream));
+    });
 }
 
 dsa_status dsa_sparse_mla_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv,
                               const int32_t *idx, int k, int H, int D, int Dv, float scale,
                               uint16_t *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
-    dsa_status st = check_batch(batch);
-    if (st != DSA_OK) return st;
-    if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
-    if ((st = check_k(k)) != DSA_OK) return st;
-    if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
-    if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
-    if (batch->total_q == 0) return DSA_OK;
-    if (!q || !idx || !out || !lse) return DSA_ERR_INVALID_ARG;
-    if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
-    if (!al16(q) || !al16(idx) || !al16(out) || !al16(lse) || (kv && !al16(kv)))
-        return DSA_ERR_INVALID_ARG;
-    const size_t need = mla_ws(batch, k);
-    if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
-    MlaParams p = make_mla(batch, q, kv, idx, k, scale, out, lse, ws);
-    return hip_status(launch_sparse_mla(p, batch->total_q, static_cast<hipStream_t>(stream)));
+    return traced("dsa_sparse_mla_fwd", batch, k, ws_bytes, [&]() -> dsa_status {
+        dsa_status st = check_batch(batch);
+        if (st != DSA_OK) return st;
+        if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
+        if ((st = check_k(k)) != DSA_OK) return st;
+        if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
+        if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
+        if (batch->total_q == 0) return DSA_OK;
+        if (!q || !idx || !out || !lse) return DSA_ERR_INVALID_ARG;
+        if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
+        if (!al16(q) || !al16(idx) || !al16(out) || !al16(lse) || (kv && !al16(kv)))
+            return DSA_ERR_INVALID_ARG;
+        const size_t need = mla_ws(batch, k);
+        if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
+        MlaParams p = make_mla(batch, q, kv, idx, k, scale, out, lse, ws);
+        return hip_status(launch_sparse_mla(p, batch->total_q, static_cast<hipStream_t>(stream)));
+    });
 }
 
 dsa_status dsa_dense_mla_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, int H, int D,
                              int Dv, float scale, uint16_t *out, float *lse, void *ws, size_t ws_bytes,
                              void *stream) {
-    dsa_status st = check_batch(batch);
-    if (st != DSA_OK) return st;
-    if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
-    if (batch->max_kv > kKMax) return DSA_ERR_UNSUPPORTED;
-    if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
-    if (batch->total_q == 0) return DSA_OK;
-    if (!q || !out || !lse) return DSA_ERR_INVALID_ARG;
-    if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
-    if (!al16(q) || !al16(out) || !al16(lse) || (kv && !al16(kv))) return DSA_ERR_INVALID_ARG;
-    const int kd = dense_slots(batch);
-    const size_t need = mla_ws(batch, kd);
-    if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
-    MlaParams p = make_mla(batch, q, kv, nullptr, kd, scale, out, lse, ws, 1);
-    return hip_status(launch_sparse_mla(p, batch->total_q, static_cast<hipStream_t>(stream)));
+    return traced("dsa_dense_mla_fwd", batch, 0, ws_bytes, [&]() -> dsa_status {
+        dsa_status st = check_batch(batch);
+        if (st != DSA_OK) return st;
+        if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
+        if (batch->max_kv > kKMax) return DSA_ERR_UNSUPPORTED;
+        if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
+        if (batch->total_q == 0) return DSA_OK;
+        if (!q || !out || !lse) return DSA_ERR_INVALID_ARG;
+        if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
+        if (!al16(q) || !al16(out) || !al16(lse) || (kv && !al16(kv))) return DSA_ERR_INVALID_ARG;
+        const int kd = dense_slots(batch);
+        const size_t need = mla_ws(batch, kd);
+        if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
+        MlaParams p = make_mla(batch, q, kv, nullptr, kd, scale, out, lse, ws, 1);
+        return hip_status(launch_sparse_mla(p, batch->total_q, static_cast<hipStream_t>(stream)));
+    });
 }
 
 dsa_status dsa_indexer_kl_fwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, const float *lse,
                               int H, int D, float scale, const float *scores, int64_t ld, const int32_t *idx,
                               int k, float *kl, float *p_out, void *ws, size_t ws_bytes, void *stream) {
-    dsa_status st = check_batch(batch);
-    if (st != DSA_OK) return st;
-    if (H != kH || D != kD) return DSA_ERR_UNSUPPORTED;
-    if (idx && (st = check_k(k)) != DSA_OK) return st;
-    if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
-    if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
-    if (batch->total_q == 0) return DSA_OK;
-    if (!q || !lse || !scores || !kl) return DSA_ERR_INVALID_ARG;
-    if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
-    if (ld < batch->max_kv || ld < 1) return DSA_ERR_INVALID_ARG;
-    if (!al16(q) || !al16(lse) || !al16(scores) || !al16(kl) || (kv && !al16(kv)) || (idx && !al16(idx)) ||
-        (p_out && !al16(p_out)))
-        return DSA_ERR_INVALID_ARG;
-    const size_t need = kl_ws(batch, idx ? k : 1);
-    if (!ws || ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
-    KlParams p;
-    p.cu_q = batch->cu_q;
-    p.cu_kv = batch->cu_kv;
-    p.pos0 = batch->pos0;
-    p.B = batch->batch;
-    p.total_kv = batch->total_kv;
-    p.max_kv = batch->max_kv;
-    p.q = q;
-    p.kv = kv;
-    p.lse = lse;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    p.scores = scores;
-    p.ld = ld;
-    p.idx = idx;
-    p.k = idx ? k : 0;
-    p.kl = kl;
-    p.p_out = p_out;
-    const int64_t slots = idx ? k : batch->max_kv;
-    p.splits = kl_splits(batch->total_q, slots);
-    const int64_t nblk = (slots + KL_BK - 1) / KL_BK;
-    p.blocks_per_split = (int)((nblk + p.splits - 1) / p.splits);
-    if (p.blocks_per_split < 1) p.blocks_per_split = 1;
-    p.part = static_cast<float *>(ws);
-    return hip_status(launch_indexer_kl(p, batch->total_q, static_cast<hipStream_t>(stream)));
+    return traced("dsa_indexer_kl_fwd", batch, k, ws_bytes, [&]() -> dsa_status {
+        dsa_status st = check_batch(batch);
+        if (st != DSA_OK) return st;
+        if (H != kH || D != kD) return DSA_ERR_UNSUPPORTED;
+        if (idx && (st = check_k(k)) != DSA_OK) return st;
+        if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
+        if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
+        if (batch->total_q == 0) return DSA_OK;
+        if (!q || !lse || !scores || !kl) return DSA_ERR_INVALID_ARG;
+        if (batch->total_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
+        if (ld < batch->max_kv || ld < 1) return DSA_ERR_INVALID_ARG;
+        if (!al16(q) || !al16(lse) || !al16(scores) || !al16(kl) || (kv && !al16(kv)) || (idx && !al16(idx)) ||
+            (p_out && !al16(p_out)))
+            return DSA_ERR_INVALID_ARG;
+        const size_t need = kl_ws(batch, idx ? k : 1);
+        if (!ws || ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
+        KlParams p;
+        p.cu_q = batch->cu_q;
+        p.cu_kv = batch->cu_kv;
+        p.pos0 = batch->pos0;
+        p.B = batch->batch;
+        p.total_kv = batch->total_kv;
+        p.max_kv = batch->max_kv;
+        p.q = q;
+        p.kv = kv;
+        p.lse = lse;
+        p.scale_log2 = scale * 1.4426950408889634f;
+        p.scores = scores;
+        p.ld = ld;
+        p.idx = idx;
+        p.k = idx ? k : 0;
+        p.kl = kl;
+        p.p_out = p_out;
+        const int64_t slots = idx ? k : batch->max_kv;
+        p.splits = kl_splits(batch->total_q, slots);
+        const int64_t nblk = (slots + KL_BK - 1) / KL_BK;
+        p.blocks_per_split = (int)((nblk + p.splits - 1) / p.splits);
+        if (p.blocks_per_split < 1) p.blocks_per_split = 1;
+        p.part = static_cast<float *>(ws);
+        return hip_status(launch_indexer_kl(p, batch->total_q, static_cast<hipStream_t>(stream)));
+    });
 }
 
 dsa_status dsa_sparse_mla_bwd(const dsa_batch *batch, const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                               int k, int H, int D, int Dv, float scale, const uint16_t *out, const float *lse,
                               const uint16_t *dout, float *dq, float *dkv, void *ws, size_t ws_bytes,
                               void *stream) {
-    dsa_status st = check_batch(batch);
-    if (st != DSA_OK) return st;
-    if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
-    if ((st = check_k(k)) != DSA_OK) return st;
-    if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
-    if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
-    if (batch->total_q == 0 && batch->total_kv == 0) return DSA_OK;
-    if (batch->total_kv > 0 && (!kv || !dkv)) return DSA_ERR_INVALID_ARG;
-    if (batch->total_q > 0 && (!q || !idx || !out || !lse || !dout || !dq)) return DSA_ERR_INVALID_ARG;
-    const void *ptrs[] = {q, kv, idx, out, lse, dout, dq, dkv};
-    for (const void *ptr : ptrs)
-        if (ptr && !al16(ptr)) return DSA_ERR_INVALID_ARG;
-    const size_t need = bwd_ws(batch, k);
-    if (batch->total_q > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
-    BwdParams p;
-    p.cu_q = batch->cu_q;
-    p.cu_kv = batch->cu_kv;
-    p.pos0 = batch->pos0;
-    p.B = batch->batch;
-    p.total_kv = batch->total_kv;
-    p.max_kv = batch->max_kv;
-    p.q = q;
-    p.kv = kv;
-    p.idx = idx;
-    p.k = k;
-    p.kpad = bwd_kpad(k);
-    p.scale = scale;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    p.out = out;
-    p.lse = lse;
-    p.dout = dout;
-    p.dq = dq;
-    p.dkv = dkv;
-    char *w = static_cast<char *>(ws);
-    const BwdWs lay = bwd_layout(batch, k);
-    p.t0 = 0;
-    p.tc = 0;
-    p.ps = w ? reinterpret_cast<uint16_t *>(w + lay.ps) : nullptr;
-    p.dzs = w ? reinterpret_cast<uint16_t *>(w + lay.dzs) : nullptr;
-    p.g = w ? reinterpret_cast<uint16_t *>(w + lay.g) : nullptr;
-    p.list = w ? reinterpret_cast<int32_t *>(w + lay.list) : nullptr;
-    p.cnt = w ? reinterpret_cast<int32_t *>(w + lay.cnt) : nullptr;
-    p.cur = w ? reinterpret_cast<int32_t *>(w + lay.cur) : nullptr;
-    p.bsum = w ? reinterpret_cast<int32_t *>(w + lay.bsum) : nullptr;
-    return hip_status(launch_sparse_mla_bwd(p, batch->total_q, static_cast<hipStream_t>(stream)));
+    return traced("dsa_sparse_mla_bwd", batch, k, ws_bytes, [&]() -> dsa_status {
+        dsa_status st = check_batch(batch);
+        if (st != DSA_OK) return st;
+        if (H != kH || D != kD || Dv != kDv) return DSA_ERR_UNSUPPORTED;
+        if ((st = check_k(k)) != DSA_OK) return st;
+        if (batch->max_kv > MAX_KV_ATTN) return DSA_ERR_UNSUPPORTED;
+        if (!valid_scale(scale)) return DSA_ERR_INVALID_ARG;
+        if (batch->total_q == 0 && batch->total_kv == 0) return DSA_OK;
+        if (batch->total_kv > 0 && (!kv || !dkv)) return DSA_ERR_INVALID_ARG;
+        if (batch->total_q > 0 && (!q || !idx || !out || !lse || !dout || !dq)) return DSA_ERR_INVALID_ARG;
+        const void *ptrs[] = {q, kv, idx, out, lse, dout, dq, dkv};
+        for (const void *ptr : ptrs)
+            if (ptr && !al16(ptr)) return DSA_ERR_INVALID_ARG;
+        const size_t need = bwd_ws(batch, k);
+        if (batch->total_q > 0 && (!ws || ws_bytes < need || !al16(ws))) return DSA_ERR_WORKSPACE;
+        BwdParams p;
+        p.cu_q = batch->cu_q;
+        p.cu_kv = batch->cu_kv;
+        p.pos0 = batch->pos0;
+        p.B = batch->batch;
+        p.total_kv = batch->total_kv;
+        p.max_kv = batch->max_kv;
+        p.q = q;
+        p.kv = kv;
+        p.idx = idx;
+        p.k = k;
+        p.kpad = bwd_kpad(k);
+        p.scale = scale;
+        p.scale_log2 = scale * 1.4426950408889634f;
+        p.out = out;
+        p.lse = lse;
+        p.dout = dout;
+        p.dq = dq;
+        p.dkv = dkv;
+        char *w = static_cast<char *>(ws);
+        const BwdWs lay = bwd_layout(batch, k);
+        p.t0 = 0;
+        p.tc = 0;
+        p.ps = w ? reinterpret_cast<uint16_t *>(w + lay.ps) : nullptr;
+        p.dzs = w ? reinterpret_cast<uint16_t *>(w + lay.dzs) : nullptr;
+        p.g = w ? reinterpret_cast<uint16_t *>(w + lay.g) : nullptr;
+        p.list = w ? reinterpret_cast<int32_t *>(w + lay.list) : nullptr;
+        p.cnt = w ? reinterpret_cast<int32_t *>(w + lay.cnt) : nullptr;
+        p.cur = w ? reinterpret_cast<int32_t *>(w + lay.cur) : nullptr;
+        p.bsum = w ? reinterpret_cast<int32_t *>(w + lay.bsum) : nullptr;
+        return hip_status(launch_sparse_mla_bwd(p, batch->total_q, static_cast<hipStream_t>(stream)));
+    });
 }
 
 dsa_status dsa_prefill_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse, int32_t *idx_out,
                            void *ws, size_t ws_bytes, void *stream) {
-    return run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, false);
+    const dsa_batch *b = args ? &args->batch : nullptr;
+    return traced("dsa_prefill_fwd", b, args ? args->k : 0, ws_bytes, [&]() -> dsa_status {
+        return run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, false);
+    });
 }
 
 dsa_status dsa_decode_fwd(const dsa_fwd_args *args, uint16_t *out, float *lse, int32_t *idx_out,
                           void *ws, size_t ws_bytes, void *stream) {
-    return run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, true);
+    const dsa_batch *b = args ? &args->batch : nullptr;
+    return traced("dsa_decode_fwd", b, args ? args->k : 0, ws_bytes, [&]() -> dsa_status {
+        return run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, true);
+    });
 }
 
 dsa_status dsa_decode_fwd_noalloc(const dsa_fwd_args *args, uint16_t *out, float *lse, int32_t *idx_out,
                                   void *stream) {
-    if (!args) return DSA_ERR_INVALID_ARG;
-    dsa_status st = check_batch(&args->batch);
-    if (st != DSA_OK) return st;
-    if ((st = check_k(args->k)) != DSA_OK) return st;
-    if (args->batch.max_kv > kMaxKvTopk) return DSA_ERR_UNSUPPORTED;
-    if (args->batch.total_q == 0) return DSA_OK;
-    if (fwd_ws(&args->batch, args->k, true) > kScratchBytes) return DSA_ERR_WORKSPACE;
-    void *ws = scratch_on_current_device();
-    if (!ws) return DSA_ERR_HIP;
-    return run_fwd(args, out, lse, idx_out, ws, kScratchBytes, stream, true);
+    const dsa_batch *b = args ? &args->batch : nullptr;
+    return traced("dsa_decode_fwd_noalloc", b, args ? args->k : 0, kScratchBytes, [&]() -> dsa_status {
+        if (!args) return DSA_ERR_INVALID_ARG;
+        dsa_status st = check_batch(&args->batch);
+        if (st != DSA_OK) return st;
+        if ((st = check_k(args->k)) != DSA_OK) return st;
+        if (args->batch.max_kv > kMaxKvTopk) return DSA_ERR_UNSUPPORTED;
+        if (args->batch.total_q == 0) return DSA_OK;
+        if (fwd_ws(&args->batch, args->k, true) > kScratchBytes) return DSA_ERR_WORKSPACE;
+        void *ws = scratch_on_current_device();
+        if (!ws) return DSA_ERR_HIP;
+        return run_fwd(args, out, lse, idx_out, ws, kScratchBytes, stream, true);
+    });
 }
 
 size_t dsa_decode_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+dsa_status dsa_check_selection(const dsa_batch *batch, const int32_t *idx, int k, void *stream, int *bad_rows) {
+    return traced("dsa_check_selection", batch, k, 0, [&]() -> dsa_status {
+        if (!bad_rows) return DSA_ERR_INVALID_ARG;
+        *bad_rows = 0;
+        dsa_status st = check_batch(batch);
+        if (st != DSA_OK) return st;
+        if ((st = check_k(k)) != DSA_OK) return st;
+        if (batch->total_q == 0) return DSA_OK;
+        if (!idx || !al16(idx)) return DSA_ERR_INVALID_ARG;
+        return hip_status(check_selection(batch->cu_q, batch->cu_kv, batch->pos0, batch->batch, batch->total_kv,
+                                          batch->max_kv, batch->total_q, idx, k, static_cast<hipStream_t>(stream),
+                                          bad_rows));
+    });
+}
 
 dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, float *lse, int32_t *idx_out,
                            void *ws, size_t ws_bytes, void *stream, dsa_kernel_time *times, int max_times,
@@ -696,6 +810,7 @@ const char *dsa_status_string(dsa_status s) {
         case DSA_ERR_UNSUPPORTED: return "unsupported shape";
         case DSA_ERR_WORKSPACE: return "workspace missing or too small";
         case DSA_ERR_HIP: return "HIP runtime error at launch";
+        case DSA_ERR_CHECK: return "debug check failed: an output breaks its contract";
     }
     return "unknown status";
 }

@@ -167,6 +167,11 @@ hipError_t launch_indexer_topk(const IdxTopkParams &p, int T, int max_q, bool de
                                LaunchMarks *m = nullptr);
 hipError_t launch_topk(const TopkParams &p, int T, hipStream_t s, LaunchMarks *m = nullptr);
 hipError_t launch_select_all_visible(const TopkParams &p, int T, hipStream_t s);
+// Debug mode: counts (into *bad_out, after draining the stream) the rows of
+// idx [T, k] that are not min(k, visible) ascending visible positions followed
+// by -1.
+hipError_t check_selection(const int32_t *cu_q, const int64_t *cu_kv, const int32_t *pos0, int B, int64_t total_kv,
+                           int max_kv, int T, const int32_t *idx, int k, hipStream_t s, int *bad_out);
 hipError_t launch_sparse_mla(const MlaParams &p, int T, hipStream_t s, LaunchMarks *m = nullptr);
 hipError_t launch_sparse_mla_bwd(const BwdParams &p, int T, hipStream_t s);
 hipError_t launch_indexer_kl(const KlParams &p, int T, hipStream_t s);

@@ -38,6 +38,7 @@ def test_status_strings_and_version(dsa):
     assert dsa.status_string(0) == "ok"
     assert "unsupported" in dsa.status_string(2)
     assert "workspace" in dsa.status_string(3)
+    assert "debug check" in dsa.status_string(5)
     assert "gfx950" in dsa.version()
 
 
@@ -289,3 +290,37 @@ def test_profile_entry_validation(dsa):
                                ctypes.byref(n)) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_fwd_profile(ctypes.byref(a), 0, FAKE, FAKE, None, FAKE, 1 << 40, None, times, 4,
                                None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_log_lines(dsa, capfd, monkeypatch):
+    """DSA_LOG=1: one stderr line per call with the batch, k, workspace and
+    status (read at every call); nothing without it."""
+    lib = dsa.raw_lib()
+    b = _batch(dsa)
+    monkeypatch.delenv("DSA_LOG", raising=False)
+    assert lib.dsa_topk(ctypes.byref(b), None, 4096, 2048, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert "[dsa]" not in capfd.readouterr().err
+    monkeypatch.setenv("DSA_LOG", "1")
+    assert lib.dsa_topk(ctypes.byref(b), None, 4096, 2048, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_prefill_fwd(None, FAKE, FAKE, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    err = capfd.readouterr().err
+    assert "[dsa] dsa_topk B=1 total_q=4096 max_q=4096 max_kv=4096 total_kv=4096 k=2048 ws=0 -> invalid argument" \
+        in err, err
+    assert "[dsa] dsa_prefill_fwd -> invalid argument" in err, err
+    monkeypatch.setenv("DSA_LOG", "0")
+    assert lib.dsa_topk(ctypes.byref(b), None, 4096, 2048, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert "[dsa]" not in capfd.readouterr().err
+
+
+def test_check_selection_validation(dsa):
+    lib = dsa.raw_lib()
+    b = _batch(dsa)
+    bad = ctypes.c_int(-7)
+    assert lib.dsa_check_selection(ctypes.byref(b), FAKE, 2048, None, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_check_selection(ctypes.byref(b), None, 2048, None, ctypes.byref(bad)) == dsa.DSA_ERR_INVALID_ARG
+    assert bad.value == 0
+    assert lib.dsa_check_selection(ctypes.byref(b), FAKE + 4, 2048, None, ctypes.byref(bad)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_check_selection(ctypes.byref(b), FAKE, 0, None, ctypes.byref(bad)) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_check_selection(None, FAKE, 2048, None, ctypes.byref(bad)) == dsa.DSA_ERR_INVALID_ARG
+    empty = _batch(dsa, T=0, N=10, max_q=0, max_kv=10)
+    assert lib.dsa_check_selection(ctypes.byref(empty), None, 16, None, ctypes.byref(bad)) == dsa.DSA_OK
