@@ -130,8 +130,13 @@ def test_indexer_topk_recompute_all_equal_scores(dsa):
     capacity (16384 candidates) are recomputed; the exact ties select the k
     lowest positions.  Prefill-shaped and decode-shaped batches."""
     say("[indexer_topk] recompute: all scores equal")
+    # (up to 1024 rows: the workgroup select queues a row for the recompute
+    # kernel; 1100 rows: the wave select hands it to the workgroup select,
+    # which queues it)
     for name, bt in (("decode", synth.Batch.decode([3000, 16384, 16385, 40000])),
-                     ("prefill", synth.Batch.prefill(20, 20000, 19980))):
+                     ("prefill", synth.Batch.prefill(20, 20000, 19980)),
+                     ("prefill_300", synth.Batch.prefill(300, 20000, 19700)),
+                     ("prefill_1100", synth.Batch.prefill(1100, 18000, 16900))):
         inp = synth.make_inputs(bt, seed=157, k=2048, per_seq=(name == "decode"))
         b = inp.batch
         inp.ki[:] = inp.ki[0]
