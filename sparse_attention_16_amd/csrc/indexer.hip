@@ -218,7 +218,8 @@ constexpr int DC_LOADS = 9;                 // loads per group: 8 x 1 KB of keys
 // candidates (the visible keys whose score is >= the row's threshold) fill
 // one region in column order; the region holds all of them (cap 512).
 template <bool CAND>
-__global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerParams p) {
+__global__ __launch_bounds__(64 * DC_WAVES) __attribute__((amdgpu_waves_per_eu(4)))
+void indexer_decode_kernel(IndexerParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t kst[DC_WAVES][DC_NBUF][DC_GROUP];
     __shared__ __attribute__((aligned(16))) float sst[DC_WAVES][DC_NBUF][64];
     const int t = blockIdx.x;
@@ -251,26 +252,31 @@ __global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerPa
     const int row = l & 15, grp = l >> 4;
     const uint64_t kbase = uniform_u64((uint64_t)(uintptr_t)(p.k + ri.kv0 * DI));
     const uint64_t sbase = uniform_u64((uint64_t)(uintptr_t)(p.k_scale + ri.kv0));
-    // Loads of group g0 into ring slot b.  Keys past the visible end load key
-    // c0 instead (their scores are not stored), so that every group issues
-    // exactly DC_LOADS loads, which the vmcnt waits below count on.
-    auto issue = [&](int g0, int b) {
-        // this wave's LDS reads of slot b (an earlier group) have completed
+    // Loads of group g0 into the wave's slot, in two halves: keys 0..31
+    // (4 loads) and keys 32..63 with the scales (5 loads).  Keys past the
+    // visible end load key c0 instead (their scores are not stored), so that
+    // every half issues exactly its count of loads, which the vmcnt waits
+    // below count on.  A half is refilled with the next group's keys as soon
+    // as its two 16-key blocks are scored, so that a wave has loads in flight
+    // while it scores.
+    auto issue_half = [&](int g0, int h) {
+        // this wave's LDS reads of the half (of the previous group) have completed
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {   // keys 8j .. 8j+7 of the group, lane l: key 8j + l/8, bytes 16*(l%8)
+        for (int j = 4 * h; j < 4 * h + 4; ++j) {   // keys 8j .. 8j+7 of the group, lane l: key 8j + l/8, bytes 16*(l%8)
             const int key = g0 + 8 * j + (l >> 3);
             const uint32_t kk = (uint32_t)(key < comp_end ? key : c0);
-            dma_b128_nt(kbase, kk * DI + 16 * (l & 7), (const DSA_LDS void *)&kst[wave][b][j * 1024]);
+            dma_b128_nt(kbase, kk * DI + 16 * (l & 7), (const DSA_LDS void *)&kst[wave][0][j * 1024]);
         }
-        const int key = g0 + l;
-        dma_b32(sbase, 4u * (uint32_t)(key < comp_end ? key : c0), (const DSA_LDS void *)&sst[wave][b][0]);
+        if (h == 1) {
+            const int key = g0 + l;
+            dma_b32(sbase, 4u * (uint32_t)(key < comp_end ? key : c0), (const DSA_LDS void *)&sst[wave][0][0]);
+        }
     };
-    auto compute = [&](int g0, int b) {
-        float part[4];
+    auto score_half = [&](int h, float (&part)[4]) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const uint8_t *kr = &kst[wave][b][(16 * st + row) * DI + 32 * grp];
+        for (int st = 2 * h; st < 2 * h + 2; ++st) {
+            const uint8_t *kr = &kst[wave][0][(16 * st + row) * DI + 32 * grp];
             const i32x4 lo = *reinterpret_cast<const i32x4 *>(kr);
             const i32x4 hi = *reinterpret_cast<const i32x4 *>(kr + 16);
             const i32x8 kb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -278,8 +284,10 @@ __global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerPa
             block_mfma(qa, kb, c);
             part[st] = block_epilogue(c, wq);
         }
+    };
+    auto finish = [&](int g0, const float (&part)[4]) {
         const float v = reduce_scatter4(part);
-        const float ks = sst[wave][b][l];
+        const float ks = sst[wave][0][l];
         const int key = g0 + l;
         if constexpr (CAND) {
             const float sc = v * ks;
@@ -288,25 +296,25 @@ __global__ __launch_bounds__(64 * DC_WAVES) void indexer_decode_kernel(IndexerPa
             p.scores[(int64_t)t * p.ld + key] = key < comp_end ? v * ks : -INFINITY;
         }
     };
-    int g0 = gstart;
-#pragma unroll
-    for (int j = 0; j < DC_NBUF; ++j)
-        if (g0 + j * STRIDE < gend) issue(g0 + j * STRIDE, j);
-    for (int i = 0; g0 < gend; g0 += STRIDE, ++i) {
-        // wait for this group's loads; the later groups' loads (at most
-        // DC_NBUF - 1 groups, issued after this one) may still fly
-        static_assert(DC_NBUF >= 1 && DC_NBUF <= 3, "vmcnt waits written for a ring of 1 to 3 groups");
-        const int ahead = (gend - 1 - g0) / STRIDE;   // groups after this one
-        const int fly = ahead < DC_NBUF - 1 ? ahead : DC_NBUF - 1;   // of them already issued
-        if (fly >= 2)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DC_LOADS - 16) | (1 << 14));   // vmcnt(2 * DC_LOADS) = 18
-        else if (fly == 1)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | DC_LOADS);   // vmcnt(DC_LOADS)
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
-        const int b = i % DC_NBUF;
-        compute(g0, b);
-        if (g0 + DC_NBUF * STRIDE < gend) issue(g0 + DC_NBUF * STRIDE, b);
+    static_assert(DC_NBUF == 1 && DC_LOADS == 9, "the waits below count 4 + 5 loads per group");
+    if (gstart < gend) {
+        issue_half(gstart, 0);
+        issue_half(gstart, 1);
+    }
+    for (int g0 = gstart; g0 < gend; g0 += STRIDE) {
+        const bool nxt = g0 + STRIDE < gend;
+        float part[4];
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 5);   // vmcnt(5): this group's first half landed
+        score_half(0, part);
+        if (nxt) {
+            issue_half(g0 + STRIDE, 0);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | 4);   // vmcnt(4): this group's second half landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
+        }
+        score_half(1, part);
+        finish(g0, part);
+        if (nxt) issue_half(g0 + STRIDE, 1);
     }
     if constexpr (CAND) {
         if (l == 0 && seg < p.nseg) p.cand_cnt[(int64_t)t * p.nseg + seg] = cnt;
