@@ -102,9 +102,12 @@ __device__ __forceinline__ GatherSlots gather_slots(const DSA_LDS int32_t *sel, 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     GatherSlots g;
     const i32x4 a = *reinterpret_cast<const DSA_LDS i32x4 *>(sel + blk * BK + 4 * wave);
+    // (an unusable slot, -1, loads row 0; the validity masks exclude it)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) g.base[i] = kvb + (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(a[i]) * ROWB;
-    const uint32_t sr = (uint32_t)sel[blk * BK + 8 * (wave & 3) + (l >> 3)];
+    for (int i = 0; i < 4; ++i)
+        g.base[i] = kvb + (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(a[i] < 0 ? 0 : a[i]) * ROWB;
+    const int sv = sel[blk * BK + 8 * (wave & 3) + (l >> 3)];
+    const uint32_t sr = (uint32_t)(sv < 0 ? 0 : sv);
     g.soff = sr * ROWB + 1024 + 16 * ((l & 7) ^ (l >> 3));
     g.kvb = kvb;
     return g;
@@ -174,10 +177,30 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     const int32_t *__restrict__ idx_row = idx + (int64_t)t * p.k + j0;
     int nblk = (nsel + BK - 1) / BK;
 
-    // query operands: lane holds head h0 + 16*ht + row16, dims 32*ks + 8*grp .. +7
+    // the slice's slot positions, padded to whole blocks; -1 marks an
+    // unusable slot (outside the slice or outside [0, ctx)).  All of a
+    // thread's index loads are issued before its first store.
+    {
+        static_assert(MAX_SEL % NTHREADS == 0, "slot fill");
+        int v[MAX_SEL / NTHREADS];
+#pragma unroll
+        for (int u = 0; u < MAX_SEL / NTHREADS; ++u) {
+            const int j = (int)threadIdx.x + u * NTHREADS;
+            v[u] = j < nsel ? (p.dense ? j0 + j : idx_row[j]) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < MAX_SEL / NTHREADS; ++u) {
+            const int j = (int)threadIdx.x + u * NTHREADS;
+            if (j < nblk * BK) sel[j] = (v[u] >= 0 && v[u] < ri.ctx) ? v[u] : -1;
+        }
+    }
+
+    // query operands: lane holds head h0 + 16*ht + row16, dims 32*ks + 8*grp .. +7.
+    // Issued now and waited for only once the first blocks' gathers are out,
+    // so that the two latencies overlap.  (The two rope k-steps go to LDS,
+    // each wave reading back its own.)
     const int h0 = wave * 16;
-    // (the two rope k-steps are kept in LDS, each wave reading back its own)
-    bf16x8 qb[NHT][16];
+    bf16x8 qb[NHT][16], qr_in[NHT][2];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
         const uint16_t *qrow = p.q + ((int64_t)t * H + h0 + 16 * ht + row16) * D + 8 * grp;
@@ -185,26 +208,17 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
         for (int ks = 0; ks < 16; ++ks)
             qb[ht][ks] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
 #pragma unroll
-        for (int ks = 16; ks < KSTEPS; ++ks)
-            *reinterpret_cast<bf16x8 *>(qrope + (wave * 2 + ks - 16) * 1024 + 16 * l) =
-                *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
+        for (int ks = 16; ks < KSTEPS; ++ks) qr_in[ht][ks - 16] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks);
     }
     const DSA_LDS uint8_t *lqr = (const DSA_LDS uint8_t *)qrope + wave * 2048 + 16 * l;
-    // the slice's slot positions, clamped to [0, ctx) and padded to whole
-    // blocks (unusable slots load row 0; the masks below exclude them)
-    for (int j = threadIdx.x; j < nblk * BK; j += NTHREADS) {
-        const int v = j < nsel ? (p.dense ? j0 + j : idx_row[j]) : -1;
-        sel[j] = (v >= 0 && v < ri.ctx) ? v : 0;
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query operands resident before the pipeline
-    __syncthreads();
+    lds_barrier();   // the slot positions are visible (the query loads keep flying)
 
-    // validity masks: lane b holds bit i = slot b*BK + i is a usable row
-    // (inside the slice, inside [0, ctx)); read per block with readlane
+    // validity masks: lane b holds bit i = slot b*BK + i is a usable row; read
+    // per block with readlane
     uint32_t maskv = 0;
     for (int it = 0; it * kWave < nsel; ++it) {
         const int j = it * kWave + l;
-        const bool ok = j < nsel && (p.dense || (uint32_t)idx_row[j] < (uint32_t)ri.ctx);
+        const bool ok = j < nsel && sel[j] >= 0;
         const uint64_t m = __ballot(ok);
         maskv = l == 2 * it ? (uint32_t)m : (l == 2 * it + 1 ? (uint32_t)(m >> 32) : maskv);
     }
@@ -234,6 +248,26 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
     lds_u8 *lb0 = (lds_u8 *)buf0;
     lds_u8 *lb1 = (lds_u8 *)buf1;
     lds_u8 *lb2 = (lds_u8 *)buf2;
+
+    // pass 0's first two blocks go out now; then the query operands are
+    // waited for (with them), and the rope operands stored
+    auto issue_first_blocks = [&]() {
+        const GatherSlots g0 = gather_slots(lsel, 0, l, kvb);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) gather_issue(g0, i, l, lb0);
+        if (nblk > 1) {
+            const GatherSlots g1 = gather_slots(lsel, 1, l, kvb);
+#pragma unroll
+            for (int i = 0; i < 5; ++i) gather_issue(g1, i, l, lb1);
+        }
+    };
+    if (nblk > 0) issue_first_blocks();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query operands (and the first blocks) landed
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            *reinterpret_cast<bf16x8 *>(qrope + (wave * 2 + r) * 1024 + 16 * l) = qr_in[ht][r];
 
     f32x4 o[HT_ALL][CT_W];   // O^T tiles: all heads x this wave's value columns
     float m_run[NHT], l_run[NHT], m_seen[NHT], rise[NHT];
@@ -366,23 +400,16 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
         // probabilities (plds by block parity).  The last step runs the
         // softmax stages on an empty block (every slot masked: no effect).
         if (nblk > 0) {
-            {
-                const GatherSlots g0 = gather_slots(lsel, 0, l, kvb);
-#pragma unroll
-                for (int i = 0; i < 5; ++i) gather_issue(g0, i, l, lb0);
-            }
-            if (nblk > 1) {
-                const GatherSlots g1 = gather_slots(lsel, 1, l, kvb);
-#pragma unroll
-                for (int i = 0; i < 5; ++i) gather_issue(g1, i, l, lb1);
-            }
-            if (nblk > 1) {
-                if (wave < 4)
-                    __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
-                else
-                    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-            } else {
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            if (pass > 0) {   // (pass 0's first blocks were issued with the query loads)
+                issue_first_blocks();
+                if (nblk > 1) {
+                    if (wave < 4)
+                        __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+                    else
+                        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+                } else {
+                    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                }
             }
             lds_barrier();   // block 0 landed and visible to every wave
             f32x4 sacc[NHT][MT];
