@@ -57,6 +57,45 @@ __device__ __forceinline__ int sample_offset(int block, int seq, int stride) {
     return (int)(((uint32_t)block * 2654435761u + (uint32_t)seq * 40503u) % (uint32_t)stride);
 }
 
+// The rank-th largest of a wave's keys kr (0 = no key; 1 <= rank <= the
+// number of keys): radix select on 8-bit digits from the most significant.
+// Per digit, a 256-bin histogram (LDS atomics into the wave's own `hist`) of
+// the keys that match the digits fixed so far, then the largest digit with at
+// least `need` of them at or above it.  Equal to the largest x with
+// #(keys >= x) >= rank (what a bisection on the key bits finds), in 4 rounds
+// instead of 32.
+template <int N>
+__device__ uint32_t wave_rank_key(const uint32_t (&kr)[N], int rank, uint32_t *hist) {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    const int l = lane_id();
+    uint32_t prefix = 0u, pmask = 0u;
+    uint32_t need = (uint32_t)rank;
+    for (int d = 3; d >= 0; --d) {
+        const int sh = 8 * d;
+        *reinterpret_cast<u32x4 *>(hist + 4 * l) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const uint32_t x = kr[i];
+            if (x != 0u && (x & pmask) == prefix) atomicAdd(&hist[(x >> sh) & 255u], 1u);
+        }
+        const u32x4 c = *reinterpret_cast<const u32x4 *>(hist + 4 * l);   // bins 4l .. 4l+3
+        const uint32_t incl = wave_scan_add(c[0] + c[1] + c[2] + c[3]);
+        const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;   // keys in bins > 4l+3
+        const uint32_t g3 = above + c[3], g2 = g3 + c[2], g1 = g2 + c[1], g0 = g1 + c[0];
+        const uint64_t m = __ballot(g0 >= need);
+        if (m == 0ull) return 0u;   // (fewer keys than rank: not called so)
+        const int L = 63 - (int)__builtin_clzll(m);
+        const int j = g3 >= need ? 3 : (g2 >= need ? 2 : (g1 >= need ? 1 : 0));
+        const uint32_t gb = j == 3 ? g3 : (j == 2 ? g2 : (j == 1 ? g1 : g0));
+        const uint32_t cb = c[j];
+        const int jl = __builtin_amdgcn_readlane(j, L);
+        need -= (uint32_t)__builtin_amdgcn_readlane((int)gb, L) - (uint32_t)__builtin_amdgcn_readlane((int)cb, L);
+        prefix |= (uint32_t)(4 * L + jl) << sh;
+        pmask |= 255u << sh;
+    }
+    return prefix;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -64,8 +103,8 @@ __device__ __forceinline__ int sample_offset(int block, int seq, int stride) {
 // rows as in the prefill indexer.  The block samples the keys o + i * stride,
 // i < m, of its longest row (m = clamp(n / 32, 512, 1024)); each row uses the
 // sampled keys it can see.  The sampled scores go to LDS as keys; each wave
-// then takes the r-th largest of its rows' samples by bisection on the key
-// bits (ballot counts), with no further barrier.
+// then takes the r-th largest of its rows' samples (wave_rank_key), with no
+// further barrier.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
     const IndexerParams &p = tp.ix;
@@ -179,18 +218,9 @@ __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
         if (n > NO_SAMPLE && n > k && mt > 0) {
             const float mu = (float)k * (float)mt / (float)n;
             const int rank = (int)ceilf(mu + SMP_SIGMA * sqrtf(mu)) + 1;
-            if (rank <= mt) {
-                // the largest x with #(keys >= x) >= rank: the rank-th largest sampled key
-                uint32_t x = 0u;
-                for (int bit = 31; bit >= 0; --bit) {
-                    const uint32_t y = x | (1u << bit);
-                    int cnt = 0;
-#pragma unroll
-                    for (int j = 0; j < SMP_MAX / kWave; ++j) cnt += __popcll(__ballot(kr[j] >= y));
-                    if (cnt >= rank) x = y;
-                }
-                tau = x;
-            }
+            // the rank-th largest sampled key (the key tile is free now: each
+            // wave's histogram takes 1 KB of it)
+            if (rank <= mt) tau = wave_rank_key(kr, rank, reinterpret_cast<uint32_t *>(ktile) + 256 * wave);
         }
         if (l == 0) tp.tau[q0 + tb + 2 * wave + r] = tau;
     }
@@ -200,10 +230,11 @@ __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
 // sequence has a single query row and a 16-row block would score 15 empty
 // rows).  Same sample grid as above for a block of one row (so the same
 // threshold); the 8 waves each gather and score 128 sampled keys in one pass
-// (B operands loaded straight into registers), wave 0 bisects.  Grid: x = row.
+// (B operands loaded straight into registers), wave 0 selects.  Grid: x = row.
 __global__ __launch_bounds__(512) void indexer_sample_row_kernel(IdxTopkParams tp) {
     const IndexerParams &p = tp.ix;
     __shared__ uint32_t samp[SMP_MAX];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[256];
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         for (int i = 0; i < FB_LIST; ++i) tp.fb[i] = 0;   // queues empty, counts 0 (this kernel runs first)
     }
@@ -261,18 +292,7 @@ __global__ __launch_bounds__(512) void indexer_sample_row_kernel(IdxTopkParams t
     for (int j = 0; j < SMP_MAX / kWave; ++j) kr[j] = samp[j * kWave + l];
     const float mu = (float)k * (float)m / (float)n;
     const int rank = (int)ceilf(mu + SMP_SIGMA * sqrtf(mu)) + 1;
-    uint32_t tau = 0u;
-    if (rank <= m) {
-        uint32_t x = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t y = x | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int j = 0; j < SMP_MAX / kWave; ++j) cnt += __popcll(__ballot(kr[j] >= y));
-            if (cnt >= rank) x = y;
-        }
-        tau = x;
-    }
+    const uint32_t tau = rank <= m ? wave_rank_key(kr, rank, hist) : 0u;
     if (l == 0) tp.tau[t] = tau;
 }
 
