@@ -25,7 +25,8 @@ namespace dsa {
 // Prefill variant: one workgroup = 16 consecutive query rows of one sequence
 // (8 waves x 2 rows) x one chunk of keys.  Key tiles of 128 rows are staged
 // once per workgroup in LDS (row pitch 144 B so that the 16 rows read by one
-// B operand land on disjoint banks) and shared by all 16 query rows.
+// B operand land on disjoint banks; two tiles, so that one barrier per tile
+// suffices) and shared by all 16 query rows.
 // Grid: x = row block, y = key chunk, z = sequence.
 //
 // Candidate mode (CAND): the score is not stored; a visible key whose score
@@ -41,8 +42,9 @@ constexpr int PF_PITCH = 144;
 
 template <bool CAND>
 __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t ktile[PF_KT * PF_PITCH];
-    __shared__ float kscale[PF_KT];
+    // two key tiles: the next one is written while this one is read
+    __shared__ __attribute__((aligned(16))) uint8_t ktiles[2][PF_KT * PF_PITCH];
+    __shared__ float kscales[2][PF_KT];
 
     const int b = blockIdx.z;
     const int q0 = p.cu_q[b];
@@ -104,17 +106,28 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
         if (tid < PF_KT) sstage = (kbase + tid < comp_end) ? p.k_scale[kv0 + kbase + tid] : 0.f;
     };
 
-    if (c0 < comp_end) fetch(c0);
-    for (int kbase = c0; kbase < comp_end; kbase += PF_KT) {
-        __syncthreads();
+    auto put = [&](int buf) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int c = tid + 512 * r;
-            *reinterpret_cast<i32x4 *>(&ktile[(c >> 3) * PF_PITCH + (c & 7) * 16]) = stage[r];
+            *reinterpret_cast<i32x4 *>(&ktiles[buf][(c >> 3) * PF_PITCH + (c & 7) * 16]) = stage[r];
         }
-        if (tid < PF_KT) kscale[tid] = sstage;
+        if (tid < PF_KT) kscales[buf][tid] = sstage;
+    };
+    // One barrier per tile: tile i is read from buffer i&1 while tile i+1
+    // goes from registers into the other buffer (whose last readers, tile
+    // i-1's, all passed the previous barrier).
+    if (c0 < comp_end) {
+        fetch(c0);
+        put(0);
         __syncthreads();
-        if (kbase + PF_KT < comp_end) fetch(kbase + PF_KT);
+    }
+    int cur = 0;
+    for (int kbase = c0; kbase < comp_end; kbase += PF_KT, cur ^= 1) {
+        const bool more = kbase + PF_KT < comp_end;
+        if (more) fetch(kbase + PF_KT);
+        const uint8_t *ktile = ktiles[cur];
+        const float *kscale = kscales[cur];
 
         // 8 blocks of 16 keys, software-pipelined: the MFMAs of block st+1
         // are issued before the epilogue of block st.  Rows past the end of
@@ -172,6 +185,8 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
             // every block's MFMAs to the front and runs out of registers
             __builtin_amdgcn_sched_barrier(0);
         }
+        if (more) put(cur ^ 1);
+        __syncthreads();
     }
 
     if constexpr (CAND) {
