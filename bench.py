@@ -60,34 +60,38 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     ("prefill_32k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "2423c28a6c907887", "fetch_kib": 11506404, "write_kib": 4352066},
+        "sha256_16": "861f4191827a5b1d", "fetch_kib": 11597204, "write_kib": 4352064},
     ("prefill_32k", "indexer_prefill_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
-        "sha256_16": "30709b0b4c3eb008", "fetch_kib": 209826, "write_kib": 864312},
+        "sha256_16": "57f92643179bc90f", "fetch_kib": 209832, "write_kib": 862174},
     ("prefill_4k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "2423c28a6c907887", "fetch_kib": 475900, "write_kib": 544233},
+        "sha256_16": "861f4191827a5b1d", "fetch_kib": 475717, "write_kib": 544228},
     ("decode_64k", "indexer_decode_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
-        "sha256_16": "30709b0b4c3eb008", "fetch_kib": 289903, "write_kib": 6202},
+        "sha256_16": "57f92643179bc90f", "fetch_kib": 288538, "write_kib": 2679},
+    ("decode_64k", "sparse_mla_kernel"): {
+        "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
+        "sha256_16": "861f4191827a5b1d", "fetch_kib": 79244, "write_kib": 33953},
     ("chunked_128k", "indexer_prefill_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
-        "sha256_16": "30709b0b4c3eb008", "fetch_kib": 207023, "write_kib": 308923},
-    # taken before the shared headers gained the fused select's fields (their
-    # hash no longer matches: reported as null until retaken)
+        "sha256_16": "57f92643179bc90f", "fetch_kib": 207034, "write_kib": 308968},
+    ("chunked_128k", "sparse_mla_kernel"): {
+        "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
+        "sha256_16": "861f4191827a5b1d", "fetch_kib": 3985131, "write_kib": 543858},
     ("short_prefill_2k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "d2c03ab62fc0b1a3", "fetch_kib": 192977, "write_kib": 272100},
+        "sha256_16": "861f4191827a5b1d", "fetch_kib": 192858, "write_kib": 272156},
     ("indexer_kl_32k", "indexer_kl_kernel"): {
         "sources": ("indexer_kl.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "9b7feb36ad51a4c0", "fetch_kib": 18264248, "write_kib": 1335},
+        "sha256_16": "0470cf295c4b0e5a", "fetch_kib": 18103251, "write_kib": 1320},
     # the whole backward (its 10 kernels, 8 row chunks), summed per call
     ("sparse_bwd_32k", "dsa_sparse_mla_bwd"): {
         "sources": ("sparse_mla_bwd.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "b63a5d5b42ec31b1", "fetch_kib": 93422305, "write_kib": 120081451},
+        "sha256_16": "pending", "fetch_kib": 93014109, "write_kib": 120002290},
     ("quant_append_32k", "quant_groups_kernel<8192,256>"): {
         "sources": ("quant.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "c43dabe9778ea7f3", "fetch_kib": 524403, "write_kib": 270336},
+        "sha256_16": "67a99849d77975ae", "fetch_kib": 524402, "write_kib": 270336},
 }
 
 def measured_traffic(workload, kernel):

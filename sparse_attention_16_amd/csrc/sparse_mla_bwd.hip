@@ -123,13 +123,27 @@ __device__ __forceinline__ uint64_t uniform_base(const void *ptr) {
            (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
 }
 
-// One 8 KB block [32 slots][128 heads] of a workspace array into LDS (wave w:
-// slots 4w .. 4w+3, one 1 KB load).
+// LDS layout of a [32 slots][128 heads] bf16 block: slot rows of 256 bytes
+// (the 64 banks exactly), the 16-byte chunk c of row r stored at chunk
+// c ^ zsw(r).  The swizzle spreads the rows a read touches over distinct
+// banks: the 16 rows of a 16-byte A-operand read (zsw is a permutation of
+// 0..15 over r mod 16), and the 4 rows x 32 bytes of a transpose read
+// (zsw(r) differs above bit 0 between the 4 rows 4g .. 4g+3).
+__device__ __forceinline__ int zsw(int r) { return ((r << 1) | ((r >> 3) & 1)) & 15; }
+__device__ __forceinline__ int zoff(int r, int byte) {
+    return r * ZP + 16 * ((byte >> 4) ^ zsw(r)) + (byte & 15);
+}
+
+// One 8 KB block [32 slots][128 heads] of a workspace array into LDS in that
+// layout (wave w: slots 4w .. 4w+3, one 1 KB load; lane l fills LDS chunk
+// l%16 of slot row 4w + l/16 with the chunk of the row that belongs there).
 __device__ __forceinline__ void load_zblock(const uint16_t *src, int wave, int l, lds_u8 *buf) {
     uint64_t base = (uint64_t)(uintptr_t)src + (uint64_t)wave * 1024;
     base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
            (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
-    dma16s(base, 16u * (uint32_t)l, buf + wave * 1024);
+    const int r = 4 * wave + (l >> 4);
+    const uint32_t voff = 256u * (uint32_t)(l >> 4) + 16u * (uint32_t)((l & 15) ^ zsw(r));
+    dma16s(base, voff, buf + wave * 1024);
 }
 
 __device__ __forceinline__ bf16x8 tr_pair(const lds_u8 *lo, const lds_u8 *hi) {
@@ -326,7 +340,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int T = 0; T < 8; ++T) {
             const int c0 = 2 * (16 * T + tcol);
-            const bf16x8 bz = tr_pair(zbuf + trow * ZP + c0, zbuf + (16 + trow) * ZP + c0);
+            const bf16x8 bz = tr_pair(zbuf + zoff(trow, c0), zbuf + zoff(16 + trow, c0));
 #pragma unroll
             for (int i = 0; i < 5; ++i)
                 if (i < nct) acc[i][T] = mfma_bf16_16x16x32(a[i], bz, acc[i][T]);
@@ -443,7 +457,7 @@ __global__ __launch_bounds__(NT) void bwd_g_kernel(BwdParams p) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 // A: slot 16*mt + row16, heads 32*ks + 8*grp .. +7
-                const int off = (16 * mt + row16) * ZP + 2 * (32 * ks + 8 * grp);
+                const int off = zoff(16 * mt + row16, 2 * (32 * ks + 8 * grp));
                 const bf16x8 az = *reinterpret_cast<const DSA_LDS bf16x8 *>(zbuf + off);
                 const bf16x8 ap = *reinterpret_cast<const DSA_LDS bf16x8 *>(pbuf + off);
 #pragma unroll
