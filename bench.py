@@ -88,7 +88,7 @@ COUNTERS = {
     # the whole backward (its 10 kernels, 8 row chunks), summed per call
     ("sparse_bwd_32k", "dsa_sparse_mla_bwd"): {
         "sources": ("sparse_mla_bwd.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "pending", "fetch_kib": 93014109, "write_kib": 120002290},
+        "sha256_16": "ae1df37de268b0aa", "fetch_kib": 93224874, "write_kib": 120111233},
     ("quant_append_32k", "quant_groups_kernel<8192,256>"): {
         "sources": ("quant.hip", "dsa_device.h", "kernels.h"),
         "sha256_16": "67a99849d77975ae", "fetch_kib": 524402, "write_kib": 270336},
