@@ -653,7 +653,7 @@ def kernel_roof(name, wl, entry, nvis, ms_mean, ms_median, splits=1, items=-1):
         # keys (128 code bytes + 4 scale bytes) of rows that see more than k, their query rows
         work = (DI + 4) * float(np.sum(nvis[long_rows])) + float(np.sum(long_rows)) * (HI * DI + HI * 8)
         bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.5
-    elif name == "cand_select_wave_kernel":
+    elif name in ("cand_select_wave_kernel", "cand_select_wave_contig_kernel"):
         # candidate keys read, the selected positions read, idx written
         work = 4.0 * max(items, 0) + 8.0 * k * T
         bound, peak, unit, target = "hbm", PEAK_HBM_GBS, "GB/s", 0.6

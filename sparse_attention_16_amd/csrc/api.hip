@@ -776,7 +776,9 @@ dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, 
             times[i].kernel = tl.name[i];
             times[i].ms = ms;
             times[i].items = -1;
-            if (std::strcmp(tl.name[i], "cand_select_wave_kernel") == 0) times[i].items = fb[2];
+            if (std::strcmp(tl.name[i], "cand_select_wave_kernel") == 0 ||
+                std::strcmp(tl.name[i], "cand_select_wave_contig_kernel") == 0)
+                times[i].items = fb[2];
             if (std::strcmp(tl.name[i], "idx_fallback_kernel") == 0) times[i].items = fb[0];
             *n_times = i + 1;
         }

@@ -561,6 +561,226 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
         if ((take >> i) & 1ull) out[slot++] = (int32_t)kr[i];
 }
 
+// cand_select_wave_contig_kernel: the same select with candidate j = 64 i + l
+// in register i of lane l, so that each load and store instruction covers 64
+// consecutive candidates ((register, lane) order is column order).  Used when
+// every row has one candidate region (then a candidate's slot is the region's
+// base + j; with several regions a binary search finds the region, which costs
+// more than the lane-run layout's forward walk, so such batches take the
+// kernel above).
+__global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_contig_kernel(IdxTopkParams tp, int T) {
+    const IndexerParams &p = tp.ix;
+    __shared__ int32_t npre_s[SEL_WAVES][MAX_SEG + 1];
+    __shared__ int16_t nreg_s[SEL_WAVES][MAX_SEG];
+    __shared__ uint32_t hist_s[SEL_WAVES][SEL_BINS];
+    __shared__ uint32_t list_s[SEL_WAVES][kWave];
+    const int wave = threadIdx.x >> 6, l = lane_id(), k = tp.k;
+    const int t = blockIdx.x * SEL_WAVES + wave;
+    if (t >= T) return;
+    int32_t *npre = npre_s[wave];
+    int16_t *nreg = nreg_s[wave];
+    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
+    const int n = ri.nvis;
+    int32_t *out = tp.idx + (int64_t)t * k;
+    if (n <= k) {   // every visible key, ascending, then -1
+        for (int j = l; j < k; j += kWave) out[j] = j < n ? j : -1;
+        return;
+    }
+    // the row's non-empty regions: npre[e] = first candidate, nreg[e] = region
+    const int nseg_t = (n + p.seg_w - 1) / p.seg_w;
+    const int64_t rows0 = (int64_t)t * p.nseg;
+    uint32_t off = 0, nr = 0;
+    bool ovf = false;
+    for (int base = 0; base < nseg_t; base += kWave) {
+        const int r = base + l;
+        int cnt = r < nseg_t ? p.cand_cnt[rows0 + r] : 0;
+        if (cnt > p.cap || cnt < 0) {
+            ovf = true;
+            cnt = 0;
+        }
+        const uint32_t incl = wave_scan_add((uint32_t)cnt);
+        const uint64_t nz = __ballot(cnt > 0);
+        const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(nz >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)nz, 0u));
+        if (cnt > 0) {
+            npre[nr + rank] = (int32_t)(off + incl - (uint32_t)cnt);
+            nreg[nr + rank] = (int16_t)r;
+        }
+        off += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        nr += (uint32_t)__popcll(nz);
+    }
+    if (l == 0) npre[nr] = (int32_t)off;
+    const int c = (int)off;
+    const uint32_t tau = tp.tau[t];
+    if (__ballot(ovf) != 0ull || (tau != 0u && c < k) || (tau == 0u && c != n) || c > CAND_SELECT_MAX) {
+        if (l == 0) {
+            const int slot = atomicAdd(&tp.fb[0], 1);
+            tp.fb[FB_LIST + slot] = t;
+        }
+        return;
+    }
+    if (l == 0) atomicAdd(&tp.fb[2], c);
+    if (c > SEL_WAVE_MAX) {   // too many for one wave's registers: the workgroup select takes it
+        if (l == 0) {
+            const int slot = atomicAdd(&tp.fb[3], 1);
+            tp.fb[FB_LIST + T + slot] = t;
+        }
+        return;
+    }
+    // Candidate j = 64 i + l is register i of lane l (R = ceil(c / 64)
+    // registers in use): each load instruction reads 64 consecutive
+    // candidates, and (register, lane) order is column order.  A candidate's
+    // slot is its region's base plus its offset there (the region found by a
+    // binary search over the non-empty regions when there are several).
+    const int R = (c + kWave - 1) / kWave;
+    const int64_t a_safe = (rows0 + nreg[0]) * p.cap;   // a valid slot (the first candidate)
+    auto slot_of = [&](int jj) -> int64_t {
+        int e = 0;
+        if (nr > 1) {
+            int hi = (int)nr - 1;
+            while (e < hi) {
+                const int mid = (e + hi + 1) >> 1;
+                if (npre[mid] <= jj) e = mid; else hi = mid - 1;
+            }
+        }
+        return (rows0 + nreg[e]) * p.cap + (jj - npre[e]);
+    };
+    // (the loads are all issued before any of their values is used)
+    uint32_t kr[SEL_R];
+#pragma unroll
+    for (int i = 0; i < SEL_R; ++i) {
+        const int jj = kWave * i + l;
+        kr[i] = p.cand_key[i < R && jj < c ? (nr == 1 ? a_safe + jj : slot_of(jj)) : a_safe];
+    }
+#pragma unroll
+    for (int i = 0; i < SEL_R; ++i) kr[i] = (i < R && kWave * i + l < c) ? score_key(__uint_as_float(kr[i])) : 0u;
+    // kappa, the k-th largest key.  A 256-bin histogram of the keys by value
+    // over [min, max] (a non-decreasing map, so bins keep the order) names the
+    // bin b1 that holds it; b1's keys (a few dozen on spread-out scores) are
+    // gathered into one register per lane and bisected.  A range that cannot
+    // be binned, or a crowded b1 (many equal scores), takes the bisection over
+    // all keys instead.
+    uint32_t kappa = 0u;
+    bool found = false;
+    {
+        uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
+#pragma unroll
+        for (int i = 0; i < SEL_R; ++i) {
+            lmn = kr[i] != 0u && kr[i] < lmn ? kr[i] : lmn;
+            lmx = kr[i] > lmx ? kr[i] : lmx;
+        }
+        const uint32_t kmin = (uint32_t)__builtin_amdgcn_readlane(
+            (int)wave_scan(lmn, 0xFFFFFFFFu, [](uint32_t a, uint32_t b2) { return a < b2 ? a : b2; }), 63);
+        const uint32_t kmax = (uint32_t)__builtin_amdgcn_readlane(
+            (int)wave_scan(lmx, 0u, [](uint32_t a, uint32_t b2) { return a > b2 ? a : b2; }), 63);
+        const float vmin = key_value(kmin), vmax = key_value(kmax);
+        const float range = vmax - vmin;
+        const float inv = (float)SEL_BINS / range;
+        if (range > 0.f && range < INFINITY && inv < INFINITY) {
+            uint32_t *hist = hist_s[wave];
+#pragma unroll
+            for (int q = 0; q < SEL_BINS / kWave; ++q) hist[q * kWave + l] = 0u;
+            auto bin_of = [&](uint32_t key) {
+                return (uint32_t)fminf((key_value(key) - vmin) * inv, (float)(SEL_BINS - 1));
+            };
+#pragma unroll
+            for (int i = 0; i < SEL_R; ++i)
+                if (kr[i] != 0u) atomicAdd(&hist[bin_of(kr[i])], 1u);
+            // lane l owns bins top - 4l - q (q < 4), scanned from the top
+            uint32_t c4[SEL_BINS / kWave], sum = 0;
+#pragma unroll
+            for (int q = 0; q < SEL_BINS / kWave; ++q) {
+                c4[q] = hist[SEL_BINS - 1 - (SEL_BINS / kWave) * l - q];
+                sum += c4[q];
+            }
+            uint32_t above = wave_excl_add(sum);
+            int my_b1 = -1;
+            uint32_t my_rem = 0;
+#pragma unroll
+            for (int q = 0; q < SEL_BINS / kWave; ++q) {
+                if (above < (uint32_t)k && (uint32_t)k <= above + c4[q]) {
+                    my_b1 = SEL_BINS - 1 - (SEL_BINS / kWave) * l - q;
+                    my_rem = (uint32_t)k - above;
+                }
+                above += c4[q];
+            }
+            const uint64_t own = __ballot(my_b1 >= 0);   // exactly one lane
+            const int src = (int)__builtin_ctzll(own);
+            const uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane(my_b1, src);
+            const uint32_t rem = (uint32_t)__builtin_amdgcn_readlane((int)my_rem, src);
+            const uint32_t nb1 = hist[b1];
+            if (nb1 <= (uint32_t)kWave) {
+                uint32_t *lst = list_s[wave];
+                uint32_t cnt = 0;
+#pragma unroll
+                for (int i = 0; i < SEL_R; ++i) {
+                    const bool inb = kr[i] != 0u && bin_of(kr[i]) == b1;
+                    const uint64_t m = __ballot(inb);
+                    if (inb) {
+                        const uint32_t r2 = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        lst[cnt + r2] = kr[i];
+                    }
+                    cnt += (uint32_t)__popcll(m);
+                }
+                const uint32_t xk = (uint32_t)l < nb1 ? lst[l] : 0u;
+                // the rem-th largest of b1's keys
+                uint32_t x = 0u;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t y = x | (1u << bit);
+                    if ((uint32_t)__popcll(__ballot(xk >= y)) >= rem) x = y;
+                }
+                kappa = x;
+                found = true;
+            }
+        }
+    }
+    if (!found) {
+        // the largest x with #(keys >= x) >= k, i.e. the k-th largest key
+        uint32_t x = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t y = x | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < SEL_R; ++i) cnt += __popcll(__ballot(kr[i] >= y));
+            if (cnt >= k) x = y;
+        }
+        kappa = x;
+    }
+    // keys > kappa, then keys == kappa in column order until k are selected
+    uint32_t gt = 0;
+#pragma unroll
+    for (int i = 0; i < SEL_R; ++i) gt += kr[i] > kappa ? 1u : 0u;
+    const uint32_t gt_all = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_add(gt), 63);
+    uint32_t eq_left = (uint32_t)k - gt_all;
+    uint64_t take = 0ull;
+#pragma unroll
+    for (int i = 0; i < SEL_R; ++i) {
+        const bool e = kr[i] == kappa;
+        const uint64_t me = __ballot(e);
+        const uint32_t er = __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+        const bool tk = kr[i] > kappa || (e && er < eq_left);
+        const uint32_t ne = (uint32_t)__popcll(me);
+        eq_left -= ne < eq_left ? ne : eq_left;
+        take |= (uint64_t)(tk ? 1u : 0u) << i;
+    }
+    // the selected candidates' positions (loads first, into the key
+    // registers), then the writes in (register, lane) order: ascending
+#pragma unroll
+    for (int i = 0; i < SEL_R; ++i) {
+        const int jj = kWave * i + l;
+        kr[i] = (uint32_t)p.cand_pos[(take >> i) & 1ull ? (nr == 1 ? a_safe + jj : slot_of(jj)) : a_safe];
+    }
+    uint32_t base = 0;
+#pragma unroll
+    for (int i = 0; i < SEL_R; ++i) {
+        const bool tk = (take >> i) & 1ull;
+        const uint64_t mt = __ballot(tk);
+        const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mt, 0u));
+        if (tk) out[base + r] = (int32_t)kr[i];
+        base += (uint32_t)__popcll(mt);
+    }
+}
+
 // cand_select_kernel: the register select of select_core.h over one row's
 // candidates (up to 16384) per 1024-thread workgroup.  Two modes: every row
 // (grid = rows; batches of few rows, e.g. decode, where one workgroup per row
@@ -818,10 +1038,14 @@ hipError_t launch_indexer_topk(const IdxTopkParams &tp, int T, int max_q, bool d
         if (marks) marks->after("cand_select_kernel", s);
     } else {
         // many rows: one wave per row; rows with too many candidates for a wave queued
-        hipLaunchKernelGGL(cand_select_wave_kernel, dim3((T + SEL_WAVES - 1) / SEL_WAVES), dim3(64 * SEL_WAVES), 0,
-                           s, tp, T);
+        if (p.nseg == 1)   // one region per row: the coalesced layout
+            hipLaunchKernelGGL(cand_select_wave_contig_kernel, dim3((T + SEL_WAVES - 1) / SEL_WAVES),
+                               dim3(64 * SEL_WAVES), 0, s, tp, T);
+        else
+            hipLaunchKernelGGL(cand_select_wave_kernel, dim3((T + SEL_WAVES - 1) / SEL_WAVES),
+                               dim3(64 * SEL_WAVES), 0, s, tp, T);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (marks) marks->after("cand_select_wave_kernel", s);
+        if (marks) marks->after(p.nseg == 1 ? "cand_select_wave_contig_kernel" : "cand_select_wave_kernel", s);
         hipLaunchKernelGGL(cand_select_kernel, dim3(T < 2 * ncu ? T : 2 * ncu), dim3(TPB), 0, s, tp, T, 1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (marks) marks->after("cand_select_kernel", s);
