@@ -204,3 +204,33 @@ def test_indexer_topk_wave_select(dsa, name):
     _, _, _, _, nvis = oracle.visible(b.cu_q, b.cu_kv, b.pos0)
     differ = check_idx_sets(g[rows], ref_idx, ref_s, A, nvis[rows], inp.k, name)
     say(f"  {b.T} rows identical to the three steps; {len(differ)} of {len(rows)} oracle rows differ at near-ties")
+
+
+def test_threshold_keeps_candidates_near_k_without_recompute(dsa):
+    """The sampled threshold (the rank-th largest sampled score, rank = mu +
+    5 sqrt(mu) + 1) on N(0,1) inputs: no row is recomputed (the threshold is
+    never above the k-th score) and the candidates per row stay near the
+    expected (rank / mu) k, about 1.6 k here.  A threshold drawn wrong either
+    way fails one of the two: too high sends rows to the recompute, too low
+    floods the select.  Prefill (wave select) and decode (workgroup select)."""
+    say("[threshold] candidates per row and recomputed rows")
+    pre = synth.make_inputs(synth.Batch.prefill(1536, 20000, 18464), seed=158, k=2048)
+    dec = synth.make_inputs(synth.Batch.decode(synth.decode_contexts(159, 32, 20000, 100000)), seed=159, k=2048,
+                            per_seq=True)
+    for name, inp, decode in (("prefill", pre, False), ("decode", dec, True)):
+        b = inp.batch
+        d = DevInputs(inp, dsa)
+        args = dsa.fwd_args(d.batch, d.qi, d.qs, d.w, d.ki, d.ks, d.q, d.kv, inp.k, inp.scale)
+        out = torch.empty((b.T, inp.H, inp.Dv), dtype=torch.int16, device="cuda")
+        lse = torch.empty((b.T, inp.H), device="cuda")
+        prof = dsa.fwd_profile(args, d.batch, out, lse, decode=decode)
+        items = {name_: it for name_, _, it in prof}
+        assert items.get("idx_fallback_kernel") == 0, f"{name}: rows recomputed: {prof}"
+        if not decode:
+            cands = [it for n_, _, it in prof if n_.startswith("cand_select_wave")]
+            assert cands, prof
+            per_row = cands[0] / b.T
+            say(f"  {name}: {per_row:.0f} candidates per row, none recomputed")
+            assert 1.2 * inp.k <= per_row <= 2.2 * inp.k, per_row
+        else:
+            say(f"  {name}: none recomputed")
