@@ -152,8 +152,10 @@ CandLayout cand_layout(const dsa_batch *b, int k, bool decode) {
     c.tau = 0;
     c.cnt = c.tau + up(T * 4);
     c.key = c.cnt + up(T * c.nseg * 4);
-    c.pos = c.key + up(slots * 4);
-    c.fb = c.pos + up(slots * 4);
+    // (64 slots of padding after each array: a select register's 64 loads may
+    // run past the last row's last candidate)
+    c.pos = c.key + up((slots + 64) * 4);
+    c.fb = c.pos + up((slots + 64) * 4);
     c.total = c.fb + up((FB_LIST + 2 * T) * 4);
     return c;
 }

@@ -563,9 +563,9 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
 
 // cand_select_wave_contig_kernel: the same select with candidate j = 64 i + l
 // in register i of lane l, so that each load and store instruction covers 64
-// consecutive candidates ((register, lane) order is column order).  Used when
-// every row has one candidate region (then a candidate's slot is the region's
-// base + j; with several regions a binary search finds the region, which costs
+// consecutive candidates ((register, lane) order is column order).  Launched
+// when every row has one candidate region (a candidate's slot is then the
+// region's base + j; with several regions finding a candidate's region costs
 // more than the lane-run layout's forward walk, so such batches take the
 // kernel above).
 __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_contig_kernel(IdxTopkParams tp, int T) {
@@ -628,29 +628,20 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_contig_kernel
     }
     // Candidate j = 64 i + l is register i of lane l (R = ceil(c / 64)
     // registers in use): each load instruction reads 64 consecutive
-    // candidates, and (register, lane) order is column order.  A candidate's
-    // slot is its region's base plus its offset there (the region found by a
-    // binary search over the non-empty regions when there are several).
+    // candidates, and (register, lane) order is column order.  The row has one
+    // region (the kernel is launched for one region per row), so candidate j
+    // sits at the region's base + j; the candidate arrays are padded by 64
+    // slots, so a register's 64 loads stay inside them even past the row's
+    // last candidate (values there are discarded), and every load is a fixed
+    // offset from one lane address.  (The loads are all issued before any of
+    // their values is used.)
     const int R = (c + kWave - 1) / kWave;
-    const int64_t a_safe = (rows0 + nreg[0]) * p.cap;   // a valid slot (the first candidate)
-    auto slot_of = [&](int jj) -> int64_t {
-        int e = 0;
-        if (nr > 1) {
-            int hi = (int)nr - 1;
-            while (e < hi) {
-                const int mid = (e + hi + 1) >> 1;
-                if (npre[mid] <= jj) e = mid; else hi = mid - 1;
-            }
-        }
-        return (rows0 + nreg[e]) * p.cap + (jj - npre[e]);
-    };
-    // (the loads are all issued before any of their values is used)
+    const int64_t a_safe = (rows0 + nreg[0]) * p.cap;   // the region's first slot
+    const uint32_t *ckey = p.cand_key + a_safe;
+    const int32_t *cpos = p.cand_pos + a_safe;
     uint32_t kr[SEL_R];
 #pragma unroll
-    for (int i = 0; i < SEL_R; ++i) {
-        const int jj = kWave * i + l;
-        kr[i] = p.cand_key[i < R && jj < c ? (nr == 1 ? a_safe + jj : slot_of(jj)) : a_safe];
-    }
+    for (int i = 0; i < SEL_R; ++i) kr[i] = i < R ? ckey[kWave * i + l] : 0u;
 #pragma unroll
     for (int i = 0; i < SEL_R; ++i) kr[i] = (i < R && kWave * i + l < c) ? score_key(__uint_as_float(kr[i])) : 0u;
     // kappa, the k-th largest key.  A 256-bin histogram of the keys by value
@@ -766,10 +757,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_contig_kernel
     // the selected candidates' positions (loads first, into the key
     // registers), then the writes in (register, lane) order: ascending
 #pragma unroll
-    for (int i = 0; i < SEL_R; ++i) {
-        const int jj = kWave * i + l;
-        kr[i] = (uint32_t)p.cand_pos[(take >> i) & 1ull ? (nr == 1 ? a_safe + jj : slot_of(jj)) : a_safe];
-    }
+    for (int i = 0; i < SEL_R; ++i) kr[i] = (take >> i) & 1ull ? (uint32_t)cpos[kWave * i + l] : 0u;
     uint32_t base = 0;
 #pragma unroll
     for (int i = 0; i < SEL_R; ++i) {
