@@ -152,6 +152,8 @@ def _finite_topk_case(name):
         b = synth.Batch.prefill(2100, 2100, 0)
     elif name == "finite_long_rows":
         b = synth.Batch.decode([32768, 32769, 40000, 70001, 131072, 2049])
+    elif name == "binary_scores":
+        b = synth.Batch.decode([32768, 40000, 9000, 70001])
     else:
         b = synth.Batch.decode([3000, 17000, 30721, 32768, 50000])
     _, _, ctx, _, nvis = oracle.visible(b.cu_q, b.cu_kv, b.pos0)
@@ -168,6 +170,11 @@ def _finite_topk_case(name):
             n = int(nvis[r])
             order = np.argsort(-s[r, :n], kind="stable")
             s[r, order[k - 1 - t:k - 1 + t]] = s[r, order[k - 1]]
+    elif name == "binary_scores":
+        # 30% of the scores 1, the rest 0: the k-th largest is tied with about
+        # 10k keys of a 32768-column chunk, more candidates than the sampled
+        # threshold path takes, so the chunk goes through the radix fallback
+        s = (rng.random(s.shape) < 0.3).astype(np.float32)
     elif name == "sub_ulp_bins":
         # a range of a few float ulps: value bins narrower than the spacing of
         # the scores, most scores tied
@@ -180,7 +187,7 @@ def _finite_topk_case(name):
 
 
 @pytest.mark.parametrize("name", ["finite_small_k", "finite_prefill_2100", "finite_long_rows", "kappa_ties_300",
-                                  "kappa_ties_900", "sub_ulp_bins"])
+                                  "kappa_ties_900", "sub_ulp_bins", "binary_scores"])
 def test_topk_bit_exact_finite_scores(dsa, name):
     say(f"[topk] {name}")
     b, k, s = _finite_topk_case(name)
