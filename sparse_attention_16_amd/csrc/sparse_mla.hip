@@ -559,34 +559,50 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
     const int c = 8 * (threadIdx.x & 63);
     const int S = p.splits;
     const float *lp = p.lse_part + (int64_t)t * S * H + h;
-    float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, lp[(int64_t)s * H]);
+    const uint16_t *op = p.o_part + ((int64_t)t * S * H + h) * DV + c;
+    // the first four splits' partials and lse values are loaded together,
+    // before anything depends on them (one memory round trip instead of two)
+    bf16x8 v4[4];
+    float l4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        v4[u] = u < S ? *reinterpret_cast<const bf16x8 *>(op + (int64_t)u * H * DV) : bf16x8{};
+        l4[u] = u < S ? lp[(int64_t)u * H] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(l4[0], l4[1]), fmaxf(l4[2], l4[3]));
+    for (int s = 4; s < S; ++s) mx = fmaxf(mx, lp[(int64_t)s * H]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float L = -INFINITY;
     if (mx != -INFINITY) {
         float den = 0.f;
-        for (int s = 0; s < S; ++s) den += expf(lp[(int64_t)s * H] - mx);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) den += expf(l4[u] - mx);   // (exp(-inf) = 0 past S)
+        for (int s = 4; s < S; ++s) den += expf(lp[(int64_t)s * H] - mx);
         L = mx + logf(den);
-        const uint16_t *op = p.o_part + ((int64_t)t * S * H + h) * DV + c;
-        auto weight = [&](int s) {
-            const float ls = lp[(int64_t)s * H];
-            return ls == -INFINITY ? 0.f : expf(ls - L);
-        };
-        int s = 0;
+        auto weight = [&](float ls) { return ls == -INFINITY ? 0.f : expf(ls - L); };
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (u < S) {
+                const float wgt = weight(l4[u]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += (float)v4[u][e] * wgt;
+            }
+        }
+        int s = 4;
         for (; s + 4 <= S; s += 4) {
             bf16x8 v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const bf16x8 *>(op + (int64_t)(s + u) * H * DV);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float wgt = weight(s + u);
+                const float wgt = weight(lp[(int64_t)(s + u) * H]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e] * wgt;
             }
         }
         for (; s < S; ++s) {
             const bf16x8 v = *reinterpret_cast<const bf16x8 *>(op + (int64_t)s * H * DV);
-            const float wgt = weight(s);
+            const float wgt = weight(lp[(int64_t)s * H]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] += (float)v[e] * wgt;
         }
