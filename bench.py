@@ -60,31 +60,31 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     ("prefill_32k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "861f4191827a5b1d", "fetch_kib": 11597204, "write_kib": 4352064},
+        "sha256_16": "7466d4447ad1d198", "fetch_kib": 11541614, "write_kib": 4352080},
     ("prefill_32k", "indexer_prefill_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
-        "sha256_16": "57f92643179bc90f", "fetch_kib": 209832, "write_kib": 862174},
+        "sha256_16": "57f92643179bc90f", "fetch_kib": 209425, "write_kib": 836719},
     ("prefill_4k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "861f4191827a5b1d", "fetch_kib": 475717, "write_kib": 544228},
+        "sha256_16": "7466d4447ad1d198", "fetch_kib": 475715, "write_kib": 544211},
     ("decode_64k", "indexer_decode_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
-        "sha256_16": "57f92643179bc90f", "fetch_kib": 288538, "write_kib": 2679},
+        "sha256_16": "57f92643179bc90f", "fetch_kib": 288537, "write_kib": 2527},
     ("decode_64k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "861f4191827a5b1d", "fetch_kib": 79244, "write_kib": 33953},
+        "sha256_16": "7466d4447ad1d198", "fetch_kib": 79244, "write_kib": 33951},
     ("chunked_128k", "indexer_prefill_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
-        "sha256_16": "57f92643179bc90f", "fetch_kib": 207034, "write_kib": 308968},
+        "sha256_16": "57f92643179bc90f", "fetch_kib": 207034, "write_kib": 305279},
     ("chunked_128k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "861f4191827a5b1d", "fetch_kib": 3985131, "write_kib": 543858},
+        "sha256_16": "7466d4447ad1d198", "fetch_kib": 3987913, "write_kib": 543847},
     ("short_prefill_2k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "861f4191827a5b1d", "fetch_kib": 192858, "write_kib": 272156},
+        "sha256_16": "7466d4447ad1d198", "fetch_kib": 192862, "write_kib": 272131},
     ("indexer_kl_32k", "indexer_kl_kernel"): {
         "sources": ("indexer_kl.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "0470cf295c4b0e5a", "fetch_kib": 18103251, "write_kib": 1320},
+        "sha256_16": "0470cf295c4b0e5a", "fetch_kib": 18004830, "write_kib": 1317},
     # the whole backward (its 10 kernels, 8 row chunks), summed per call
     ("sparse_bwd_32k", "dsa_sparse_mla_bwd"): {
         "sources": ("sparse_mla_bwd.hip", "dsa_device.h", "kernels.h"),
