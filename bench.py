@@ -533,6 +533,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=5,
                     help="timed launches of the dominant kernel")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the attainable-peak loops (dsa_measure_peaks) after the workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -571,8 +573,45 @@ def main(argv=None):
         line["decode_64k"]["tokens_per_s"] = dec["value"]
     else:
         line = fwd_bench(args, dsa, args.workload, args.steps, args.warmup)
+    if not args.no_peaks and line.get("roofline"):
+        peaks = attainable_peaks(dsa)
+        line["attainable_peaks"] = peaks
+        attach_attainable(line["roofline"], peaks)
+        if "decode_64k" in line:
+            attach_attainable(line["decode_64k"]["roofline"], peaks)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def attainable_peaks(dsa):
+    """What this GPU reaches on the instructions the rooflines price
+    (dsa_measure_peaks: MFMA loops, a streaming read and copy over 2 GiB),
+    next to the spec-sheet peaks the fractions divide by."""
+    import torch
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    p = dsa.measure_peaks(buf)
+    del buf
+    say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+    say(f"[bench] attainable on this GPU: bf16 MFMA {p['bf16_tflops']:.0f} TFLOP/s "
+        f"({100 * p['bf16_tflops'] / PEAK_BF16_TFLOPS:.0f}% of the spec sheet), FP8 MFMA {p['fp8_tflops']:.0f} "
+        f"({100 * p['fp8_tflops'] / PEAK_FP8_TFLOPS:.0f}%), HBM read {p['hbm_read_gbs']:.0f} GB/s "
+        f"({100 * p['hbm_read_gbs'] / PEAK_HBM_GBS:.0f}%), copy {p['hbm_copy_gbs']:.0f} GB/s")
+    return {k: round(v, 1) for k, v in p.items()} | {
+        "note": "best of 3 runs: 8 independent MFMA chains per wave, 16 waves per compute unit; non-temporal "
+                "16-byte streaming read of 2 GiB and copy of 1 GiB (read + write bytes)"}
+
+
+def attach_attainable(roof, peaks):
+    """The roofline's rate against what this GPU attains for its bound: the
+    MFMA loop of its own data type, or the better of the streaming read and copy."""
+    if roof.get("bound") == "mfma":
+        a = peaks["fp8_tflops"] if roof.get("peak") == PEAK_FP8_TFLOPS else peaks["bf16_tflops"]
+    elif roof.get("bound") == "hbm":
+        a = max(peaks["hbm_read_gbs"], peaks["hbm_copy_gbs"])
+    else:
+        return
+    roof["attainable_peak"] = round(a, 1)
+    roof["frac_attainable"] = round(roof["achieved"] / a, 4) if a > 0 else None
 
 
 # ------------------------------------------------------ fused forward (A1-A9)

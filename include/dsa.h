@@ -295,6 +295,26 @@ dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, 
                            int32_t *idx_out, void *ws, size_t ws_bytes, void *stream,
                            dsa_kernel_time *times, int max_times, int *n_times);
 
+/* Measurement helper (not part of the hot path's data flow): the rates this
+ * GPU attains, under its own clock and power limits, for the work the
+ * rooflines price against the spec-sheet peaks: the 16x16x32 bf16 MFMA (the
+ * attention's product) and the 16x16x128 FP8 MFMA (the indexer's), each in
+ * 8 independent accumulator chains per wave, 16 waves per compute unit; a
+ * streaming read and a streaming copy (16-byte non-temporal loads and
+ * stores) over `buf`.  `buf` is caller-owned device memory of `bytes` bytes
+ * (at least 64 MiB, 16-byte aligned; several times the 256 MB Infinity
+ * Cache for a memory-bound figure), used as scratch: its contents are
+ * overwritten.  Each loop runs 3 times on `stream`, the fastest run counts;
+ * the call WAITS for `stream`.  The copy rate counts the bytes read plus
+ * the bytes written.  Events are created and destroyed inside the call. */
+typedef struct {
+    double bf16_tflops;
+    double fp8_tflops;
+    double hbm_read_gbs;
+    double hbm_copy_gbs;
+} dsa_peaks;
+dsa_status dsa_measure_peaks(void *buf, size_t bytes, void *stream, dsa_peaks *out);
+
 /* Validation of a selection against the contract of Top-k ([R] "Отбор и
  * основное внимание": the k top-scored visible keys of each query row):
  * every row t of idx [T, k] int32 (device) must hold exactly min(k, n_t)

@@ -38,7 +38,8 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 EXPORTS = ("dsa_indexer_scores", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_dense_mla_fwd", "dsa_indexer_kl_fwd",
            "dsa_sparse_mla_bwd", "dsa_prefill_fwd",
            "dsa_decode_fwd", "dsa_decode_fwd_noalloc", "dsa_decode_fwd_noalloc_max_bytes", "dsa_fwd_profile",
-           "dsa_check_selection", "dsa_quantize_queries", "dsa_append_cache", "dsa_workspace_size",
+           "dsa_check_selection", "dsa_measure_peaks", "dsa_quantize_queries", "dsa_append_cache",
+           "dsa_workspace_size",
            "dsa_status_string", "dsa_version")
 
 
@@ -68,6 +69,11 @@ class dsa_kernel_time(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_char_p), ("ms", ctypes.c_float), ("items", ctypes.c_int64)]
 
 
+class dsa_peaks(ctypes.Structure):
+    _fields_ = [("bf16_tflops", ctypes.c_double), ("fp8_tflops", ctypes.c_double),
+                ("hbm_read_gbs", ctypes.c_double), ("hbm_copy_gbs", ctypes.c_double)]
+
+
 _P, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 _BP = ctypes.POINTER(dsa_batch)
 _lib.dsa_indexer_scores.argtypes = [_BP, _P, _P, _P, _P, _P, _I, _I, _P, _I64, _P]
@@ -84,6 +90,7 @@ _lib.dsa_decode_fwd_noalloc_max_bytes.restype = _SZ
 _lib.dsa_fwd_profile.argtypes = [ctypes.POINTER(dsa_fwd_args), _I, _P, _P, _P, _P, _SZ, _P,
                                  ctypes.POINTER(dsa_kernel_time), _I, ctypes.POINTER(ctypes.c_int)]
 _lib.dsa_check_selection.argtypes = [_BP, _P, _I, _P, ctypes.POINTER(ctypes.c_int)]
+_lib.dsa_measure_peaks.argtypes = [_P, _SZ, _P, ctypes.POINTER(dsa_peaks)]
 _lib.dsa_workspace_size.argtypes = [_I, _BP, _I, _I, _I]
 _lib.dsa_quantize_queries.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
 _lib.dsa_append_cache.argtypes = [_P, _P, _I64, _I, _I, _P, _P, _P, _P, _I64, _P]
@@ -319,6 +326,17 @@ def check_selection(batch: Batch, idx, k: int = None, stream=None) -> int:
     st = _lib.dsa_check_selection(ctypes.byref(batch.c), _ptr(idx), int(k), _stream(stream), ctypes.byref(bad))
     _check(st, "dsa_check_selection")
     return bad.value
+
+
+def measure_peaks(buf, stream=None) -> dict:
+    """Attainable bf16 / FP8 MFMA TFLOP/s and HBM read / copy GB/s on this
+    GPU (see dsa_measure_peaks; `buf` is a device scratch tensor of at least
+    64 MiB whose contents are overwritten; waits for the stream)."""
+    r = dsa_peaks()
+    st = _lib.dsa_measure_peaks(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream), ctypes.byref(r))
+    _check(st, "dsa_measure_peaks")
+    return {"bf16_tflops": r.bf16_tflops, "fp8_tflops": r.fp8_tflops, "hbm_read_gbs": r.hbm_read_gbs,
+            "hbm_copy_gbs": r.hbm_copy_gbs}
 
 
 def raw_lib():

@@ -454,6 +454,11 @@ void *scratch_on_current_device() {
 
 }  // namespace
 
+namespace dsa {
+// (peaks.hip) attainable MFMA and HBM rates; waits for `s`
+hipError_t measure_peaks(void *buf, size_t bytes, hipStream_t s, dsa_peaks *out);
+}  // namespace dsa
+
 extern "C" {
 
 dsa_status dsa_quantize_queries(const float *q, int64_t T, int HI, int DI, uint8_t *q_fp8,
@@ -743,6 +748,14 @@ dsa_status dsa_check_selection(const dsa_batch *batch, const int32_t *idx, int k
         return hip_status(check_selection(batch->cu_q, batch->cu_kv, batch->pos0, batch->batch, batch->total_kv,
                                           batch->max_kv, batch->total_q, idx, k, static_cast<hipStream_t>(stream),
                                           bad_rows));
+    });
+}
+
+dsa_status dsa_measure_peaks(void *buf, size_t bytes, void *stream, dsa_peaks *out) {
+    return traced("dsa_measure_peaks", nullptr, 0, bytes, [&]() -> dsa_status {
+        if (!out || !buf || !al16(buf) || bytes < ((size_t)64 << 20)) return DSA_ERR_INVALID_ARG;
+        *out = dsa_peaks{0.0, 0.0, 0.0, 0.0};
+        return hip_status(measure_peaks(buf, bytes, static_cast<hipStream_t>(stream), out));
     });
 }
 

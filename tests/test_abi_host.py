@@ -324,3 +324,14 @@ def test_check_selection_validation(dsa):
     assert lib.dsa_check_selection(None, FAKE, 2048, None, ctypes.byref(bad)) == dsa.DSA_ERR_INVALID_ARG
     empty = _batch(dsa, T=0, N=10, max_q=0, max_kv=10)
     assert lib.dsa_check_selection(ctypes.byref(empty), None, 16, None, ctypes.byref(bad)) == dsa.DSA_OK
+
+
+def test_measure_peaks_validation(dsa):
+    # argument checks come before any GPU call: no device needed
+    lib = dsa.raw_lib()
+    r = dsa.dsa_peaks()
+    big = 256 << 20
+    assert lib.dsa_measure_peaks(None, big, None, ctypes.byref(r)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_measure_peaks(FAKE, big, None, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_measure_peaks(FAKE + 4, big, None, ctypes.byref(r)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_measure_peaks(FAKE, (64 << 20) - 16, None, ctypes.byref(r)) == dsa.DSA_ERR_INVALID_ARG
