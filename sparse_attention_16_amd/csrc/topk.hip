@@ -64,6 +64,7 @@ constexpr int TK_WCOLS = TOPK_CHUNK / NWAVE;   // 2048 columns per wave
 constexpr int TK_R = TK_WCOLS / kWave;         // 32 keys per lane
 constexpr int TK_CAP = 8 * TPB;                // candidates the select takes (8 per thread)
 constexpr float TK_SIGMAS = 5.f;               // sample rank margin, in standard deviations
+constexpr uint32_t kNegInfKey = 0x007FFFFFu;   // score_key(-inf): the lowest real key
 constexpr int TK_NB = 2048;                    // value bins of the candidate select
 static_assert(TK_R == 4 * CH_V4 && TK_CAP <= 65536, "register layout");
 static_assert(TK_NB <= NBIN && TK_CAP / 32 <= 2 * TPB && TK_CAP % (NWAVE * 32) == 0 &&
@@ -306,10 +307,13 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8))) void t
         for (int i = 0; i < TK_R; ++i) kr[i] = 0u;
     }
 
-    // 1. sample: lane l's key of register 4 (l % 8), spread over the wave's columns
+    // 1. sample: lane l's key of register 4 (l % 8), spread over the wave's
+    // columns.  A -inf score is left out of the sample: it would make the
+    // sampled range infinite (no threshold) and can never pass a finite one.
     uint32_t sk = 0u;
 #pragma unroll
     for (int i = 0; i < TK_R; i += 4) sk = (l & 7) == i / 4 ? kr[i] : sk;
+    sk = sk == kNegInfKey ? 0u : sk;
     {
         const uint32_t mn = wave_scan(sk != 0u ? sk : 0xFFFFFFFFu, 0xFFFFFFFFu,
                                       [](uint32_t a, uint32_t b2) { return a < b2 ? a : b2; });
