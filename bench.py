@@ -576,9 +576,11 @@ def main(argv=None):
     if not args.no_peaks and line.get("roofline"):
         peaks = attainable_peaks(dsa)
         line["attainable_peaks"] = peaks
-        attach_attainable(line["roofline"], peaks)
-        if "decode_64k" in line:
-            attach_attainable(line["decode_64k"]["roofline"], peaks)
+        for part in (line, line.get("decode_64k")):
+            if part:
+                attach_attainable(part["roofline"], peaks)
+                for r in part.get("kernels", []):
+                    attach_attainable(r, peaks)
     print(json.dumps(line), flush=True)
     return 0
 
@@ -609,6 +611,8 @@ def attach_attainable(roof, peaks):
     elif roof.get("bound") == "hbm":
         a = max(peaks["hbm_read_gbs"], peaks["hbm_copy_gbs"])
     else:
+        return
+    if "achieved" not in roof:
         return
     roof["attainable_peak"] = round(a, 1)
     roof["frac_attainable"] = round(roof["achieved"] / a, 4) if a > 0 else None
