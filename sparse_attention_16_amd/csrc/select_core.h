@@ -372,6 +372,171 @@ __device__ __forceinline__ void select_regs(uint32_t (&kr)[4 * NV4], int G, uint
     lds_barrier();   // selection in sh.ocol / sh.okey
 }
 
+__device__ __forceinline__ uint32_t lane_rank(uint64_t m) {   // set bits of m below this lane
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The bin holding the rank-th largest of the values counted in hist[0, NB)
+// (bins ordered like the values; 1 <= rank <= the total): b, with rem = its
+// rank inside the bin and above = the count in the bins above it.  Wave w
+// sums the group of bins [GB w, GB w + GB) into gsum[w]; after one barrier
+// every wave finds the group from the 16 sums and then the bin inside it on
+// its own (the same answer in every wave, no barrier after).  Each lane reads
+// a handful of words.
+template <int NB>
+__device__ __forceinline__ void block_pick_bin(const uint32_t *hist, uint32_t *gsum, uint32_t rank, uint32_t &b,
+                                               uint32_t &rem, uint32_t &above) {
+    constexpr int GB = NB / NWAVE;   // bins per group
+    constexpr int PL = GB / kWave;   // bins per lane
+    static_assert(PL * kWave * NWAVE == NB && NWAVE <= kWave, "bin groups");
+    const int l = lane_id(), w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < PL; ++q) sum += hist[GB * w + PL * l + q];
+    sum = wave_scan_add(sum);
+    if (l == 63) gsum[w] = sum;   // (the inclusive scan's last lane: the wave's total)
+    lds_barrier();
+    // the group: lane g holds group NWAVE - 1 - g (from the top)
+    const uint32_t gv = l < NWAVE ? gsum[NWAVE - 1 - l] : 0u;
+    const uint32_t gx = wave_scan_add(gv) - gv;
+    const uint64_t gown = __ballot(l < NWAVE && gx < rank && rank <= gx + gv);   // exactly one lane
+    const int gl = (int)__builtin_ctzll(gown);
+    const int grp = NWAVE - 1 - gl;
+    const uint32_t gabove = (uint32_t)__builtin_amdgcn_readlane((int)gx, gl);
+    const uint32_t grank = rank - gabove;
+    // the bin inside the group: lane l holds bins top - PL l - q, q < PL
+    const int top = GB * grp + GB - 1;
+    uint32_t c[PL], lsum = 0;
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+        c[q] = hist[top - PL * l - q];
+        lsum += c[q];
+    }
+    uint32_t acc = wave_scan_add(lsum) - lsum;
+    int mine = -1;
+    uint32_t mrem = 0, mabove = 0;
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+        if (acc < grank && grank <= acc + c[q]) {
+            mine = top - PL * l - q;
+            mrem = grank - acc;
+            mabove = acc;
+        }
+        acc += c[q];
+    }
+    const uint64_t own = __ballot(mine >= 0);   // exactly one lane
+    const int src = (int)__builtin_ctzll(own);
+    b = (uint32_t)__builtin_amdgcn_readlane(mine, src);
+    rem = (uint32_t)__builtin_amdgcn_readlane((int)mrem, src);
+    above = gabove + (uint32_t)__builtin_amdgcn_readlane((int)mabove, src);
+}
+
+// Exact k largest of nc candidate keys held in LDS in column order (ckey[j],
+// order-preserving keys, j < nc, k < nc <= CAP), ties to the lower index:
+//   * a 2048-bin value histogram over [vlo, vhi] (clamped at both ends, so
+//     non-decreasing in the key; vlo / vhi bound the keys' values), and the
+//     bin b1 of the k-th largest (block_pick_bin: per-wave group sums, one
+//     barrier, then every wave on its own);
+//   * every key of a bin above b1 is taken; b1's keys (a few on spread-out
+//     scores) are listed and ranked by every wave on its own (key descending,
+//     then index), and the first rem = k - #above are taken;
+//   * wave w owns the slots [S w, S w + S), S = the candidates per wave
+//     rounded up to 64, and calls emit(r, j) for each taken candidate j with
+//     its output slot r (its rank in index order).
+// Returns false, having emitted nothing, when [vlo, vhi] cannot be binned or
+// b1 holds more than 64 keys (many equal scores): the caller then selects
+// another way (sh free again: the call ends with a barrier, or has not
+// touched it).  Uses sh.hist, sh.ncand, sh.ckey/cpos[0, 64), sh.tbits as a
+// CAP-bit map, gsum and wcnt [NWAVE].
+template <int CAP, class Emit>
+__device__ __forceinline__ bool lds_cand_select(const uint32_t *ckey, int nc, int k, float vlo, float vhi,
+                                                SelectShared &sh, uint32_t *gsum, uint32_t *wcnt, Emit &&emit) {
+    constexpr int NB = NBIN;
+    constexpr int SPW_MAX = CAP / NWAVE;
+    static_assert(CAP % (NWAVE * kWave) == 0 && CAP / 32 <= 2 * TPB && CCAP >= kWave, "candidate select tables");
+    const float crange = vhi - vlo;
+    const float cinv = (float)NB / crange;
+    if (!(crange > 0.f && crange < INFINITY && cinv < INFINITY)) return false;
+    const int tid = threadIdx.x, l = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nu = (nc + NWAVE * kWave - 1) / (NWAVE * kWave);   // slots per lane
+    const int S = kWave * nu;
+    uint32_t *chist = sh.hist;
+    uint32_t *selb = reinterpret_cast<uint32_t *>(sh.tbits);
+    for (int i = tid; i < NB; i += TPB) chist[i] = 0u;
+    if (tid == 0) sh.ncand = 0u;
+    auto kbin = [&](uint32_t key) {
+        return (uint32_t)fminf(fmaxf((key_value(key) - vlo) * cinv, 0.f), (float)(NB - 1));
+    };
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < SPW_MAX / kWave; ++u) {
+        const int j = S * w + kWave * u + l;
+        if (u < nu && j < nc) atomicAdd(&chist[kbin(ckey[j])], 1u);
+    }
+    lds_barrier();
+    uint32_t b1, rem, above;
+    block_pick_bin<NB>(chist, gsum, (uint32_t)k, b1, rem, above);
+    uint32_t gtw = 0;
+#pragma unroll
+    for (int u = 0; u < SPW_MAX / kWave; ++u) {
+        const int j = S * w + kWave * u + l;
+        const bool ok = u < nu && j < nc;
+        const uint32_t bj = ok ? kbin(ckey[j]) : 0u;
+        gtw += (uint32_t)__popcll(__ballot(ok && bj > b1));
+        if (ok && bj == b1) {
+            const uint32_t q = atomicAdd(&sh.ncand, 1u);
+            if (q < (uint32_t)kWave) {
+                sh.ckey[q] = ckey[j];
+                sh.cpos[q] = (uint32_t)j;
+            }
+        }
+    }
+    if (l == 0) wcnt[w] = gtw;
+    lds_barrier();
+    const uint32_t nb1 = sh.ncand;
+    if (nb1 > (uint32_t)kWave) {
+        lds_barrier();   // every thread has read nb1
+        return false;
+    }
+    // lane e holds b1's entry e
+    const uint32_t key = (uint32_t)l < nb1 ? sh.ckey[l] : 0u;
+    const uint32_t pos = (uint32_t)l < nb1 ? sh.cpos[l] : 0u;
+    uint32_t before = 0;
+    for (uint32_t e = 0; e < nb1; ++e) {
+        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)key, (int)e);
+        const uint32_t op = (uint32_t)__builtin_amdgcn_readlane((int)pos, (int)e);
+        before += (o > key || (o == key && op < pos)) ? 1u : 0u;
+    }
+    const bool sel = (uint32_t)l < nb1 && before < rem;
+    // this wave's first output slot: the keys above b1 in the waves before
+    // it, and the taken b1 keys at lower indices
+    uint32_t slot = (uint32_t)__popcll(__ballot(sel && pos < (uint32_t)(S * w)));
+#pragma unroll
+    for (int x = 0; x < NWAVE; ++x) slot += x < w ? wcnt[x] : 0u;
+    // the taken b1 keys of this wave's slots, as bits of its own words of
+    // selb (written and read by this wave only: LDS keeps a wave's operations
+    // in order)
+    if (l < S / 32) selb[(S / 32) * w + l] = 0u;
+    if (sel && pos / (uint32_t)S == (uint32_t)w) atomicOr(&selb[pos >> 5], 1u << (pos & 31u));
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+#pragma unroll
+    for (int u = 0; u < SPW_MAX / kWave; ++u) {
+        if (u >= nu) break;
+        const int j = S * w + kWave * u + l;
+        bool tk = false;
+        if (j < nc) {
+            const uint32_t bj = kbin(ckey[j]);
+            tk = bj > b1 || (bj == b1 && ((selb[j >> 5] >> (j & 31)) & 1u));
+        }
+        const uint64_t mt = __ballot(tk);
+        const uint32_t r = slot + lane_rank(mt);
+        if (tk && r < (uint32_t)k) emit(r, j);   // (exactly k are taken)
+        slot += (uint32_t)__popcll(mt);
+    }
+    return true;
+}
+
 }  // namespace
 
 }  // namespace dsa

@@ -65,70 +65,9 @@ constexpr int TK_R = TK_WCOLS / kWave;         // 32 keys per lane
 constexpr int TK_CAP = 8 * TPB;                // candidates the select takes (8 per thread)
 constexpr float TK_SIGMAS = 5.f;               // sample rank margin, in standard deviations
 constexpr uint32_t kNegInfKey = 0x007FFFFFu;   // score_key(-inf): the lowest real key
-constexpr int TK_NB = 2048;                    // value bins of the candidate select
 static_assert(TK_R == 4 * CH_V4 && TK_CAP <= 65536, "register layout");
-static_assert(TK_NB <= NBIN && TK_CAP / 32 <= 2 * TPB && TK_CAP % (NWAVE * 32) == 0 &&
-                  TK_CAP / (NWAVE * 32) <= kWave && CCAP >= kWave,
-              "candidate select tables");
 
-__device__ __forceinline__ uint32_t lane_rank(uint64_t m) {   // set bits of m below this lane
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
 
-// The bin holding the rank-th largest of the values counted in hist[0, NB)
-// (bins ordered like the values; 1 <= rank <= the total): b, with rem = its
-// rank inside the bin and above = the count in the bins above it.  Wave w
-// sums the group of bins [GB w, GB w + GB) into gsum[w]; after one barrier
-// every wave finds the group from the 16 sums and then the bin inside it on
-// its own (the same answer in every wave, no barrier after).  Each lane reads
-// a handful of words.
-template <int NB>
-__device__ __forceinline__ void block_pick_bin(const uint32_t *hist, uint32_t *gsum, uint32_t rank, uint32_t &b,
-                                               uint32_t &rem, uint32_t &above) {
-    constexpr int GB = NB / NWAVE;   // bins per group
-    constexpr int PL = GB / kWave;   // bins per lane
-    static_assert(PL * kWave * NWAVE == NB && NWAVE <= kWave, "bin groups");
-    const int l = lane_id(), w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    uint32_t sum = 0;
-#pragma unroll
-    for (int q = 0; q < PL; ++q) sum += hist[GB * w + PL * l + q];
-    sum = wave_scan_add(sum);
-    if (l == 63) gsum[w] = sum;   // (the inclusive scan's last lane: the wave's total)
-    lds_barrier();
-    // the group: lane g holds group NWAVE - 1 - g (from the top)
-    const uint32_t gv = l < NWAVE ? gsum[NWAVE - 1 - l] : 0u;
-    const uint32_t gx = wave_scan_add(gv) - gv;
-    const uint64_t gown = __ballot(l < NWAVE && gx < rank && rank <= gx + gv);   // exactly one lane
-    const int gl = (int)__builtin_ctzll(gown);
-    const int grp = NWAVE - 1 - gl;
-    const uint32_t gabove = (uint32_t)__builtin_amdgcn_readlane((int)gx, gl);
-    const uint32_t grank = rank - gabove;
-    // the bin inside the group: lane l holds bins top - PL l - q, q < PL
-    const int top = GB * grp + GB - 1;
-    uint32_t c[PL], lsum = 0;
-#pragma unroll
-    for (int q = 0; q < PL; ++q) {
-        c[q] = hist[top - PL * l - q];
-        lsum += c[q];
-    }
-    uint32_t acc = wave_scan_add(lsum) - lsum;
-    int mine = -1;
-    uint32_t mrem = 0, mabove = 0;
-#pragma unroll
-    for (int q = 0; q < PL; ++q) {
-        if (acc < grank && grank <= acc + c[q]) {
-            mine = top - PL * l - q;
-            mrem = grank - acc;
-            mabove = acc;
-        }
-        acc += c[q];
-    }
-    const uint64_t own = __ballot(mine >= 0);   // exactly one lane
-    const int src = (int)__builtin_ctzll(own);
-    b = (uint32_t)__builtin_amdgcn_readlane(mine, src);
-    rem = (uint32_t)__builtin_amdgcn_readlane((int)mrem, src);
-    above = gabove + (uint32_t)__builtin_amdgcn_readlane((int)mabove, src);
-}
 
 // A wave's keys: score_key(wsrc[64 i + l]) in kr[i - i0] of lane l for the
 // registers i in [i0, i0 + N), 0 for columns at or past wlen (wlen >= 1 - the
@@ -347,14 +286,11 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8))) void t
         block_pick_bin<NBIN>(sh.hist, gsum, rank, b, rem, above);   // the bin of the rank-th largest sample
         tkey = score_key(vmin + ((float)b - 0.25f) * (range / (float)NBIN));
     }
-    // value bins of the candidates (3. below), over the sampled range from the
-    // threshold (or the smallest sample) to the largest sample, clamped at
-    // both ends: non-decreasing in the key.  (Bins of the key bits would be
-    // far too coarse wherever the range crosses zero or several exponents.)
+    // value bins of the candidates (3. below) span the sampled range from the
+    // threshold (or the smallest sample) to the largest sample.  (Bins of the
+    // key bits would be far too coarse wherever the range crosses zero or
+    // several exponents.)
     const float cvlo = tkey > 1u ? key_value(tkey) : vmin;
-    const float crange = vmax - cvlo;
-    const float cinv = (float)TK_NB / crange;
-    const bool cbinned = crange > 0.f && crange < INFINITY && cinv < INFINITY;
 
     // 2. candidates: counts per wave, then keys and columns into LDS in column order
     // (registers from nreg on hold key 0, below every threshold: the loops
@@ -391,97 +327,16 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8))) void t
             }
         }
     }
-    if (nc > (uint32_t)k && nc <= (uint32_t)TK_CAP && cbinned) {
-        // 3. exact select over the candidates: every key of a bin above the
-        // bin b1 of the k-th largest, and the first rem of b1's keys ranked by
-        // key descending, then column; written in column order.  Wave w owns
-        // the candidate slots [SPW w, SPW w + SPW), SPW = the candidates per
-        // wave rounded up to 64 (at most 512): the work is spread over all
-        // the waves whatever the count.
-        constexpr int SPW_MAX = TK_CAP / NWAVE;
-        const int nu = ((int)nc + NWAVE * kWave - 1) / (NWAVE * kWave);   // slots per lane, 1..8
-        const int SPW = kWave * nu;
-        uint32_t *chist = sh.hist;                               // [TK_NB] key-bin counts
-        uint32_t *selb = reinterpret_cast<uint32_t *>(sh.tbits);  // [TK_CAP / 32] b1 keys taken, by slot
-        for (int i = tid; i < TK_NB; i += TPB) chist[i] = 0u;
-        if (tid == 0) sh.ncand = 0u;
-        auto kbin = [&](uint32_t key) {
-            return (uint32_t)fminf(fmaxf((key_value(key) - cvlo) * cinv, 0.f), (float)(TK_NB - 1));
-        };
-        lds_barrier();
-#pragma unroll
-        for (int u = 0; u < SPW_MAX / kWave; ++u) {
-            const int j = SPW * w + kWave * u + l;
-            if (u < nu && j < (int)nc) atomicAdd(&chist[kbin(ckey[j])], 1u);
-        }
-        lds_barrier();
-        uint32_t b1, rem, above;
-        block_pick_bin<TK_NB>(chist, gsum, (uint32_t)k, b1, rem, above);
-        // per wave: the keys of bins above b1 (counted), b1's keys (a few on
-        // spread-out scores) to a list
-        uint32_t gtw = 0;
-#pragma unroll
-        for (int u = 0; u < SPW_MAX / kWave; ++u) {
-            const int j = SPW * w + kWave * u + l;
-            const bool ok = u < nu && j < (int)nc;
-            const uint32_t bj = ok ? kbin(ckey[j]) : 0u;
-            gtw += (uint32_t)__popcll(__ballot(ok && bj > b1));
-            if (ok && bj == b1) {
-                const uint32_t q = atomicAdd(&sh.ncand, 1u);
-                if (q < (uint32_t)kWave) {
-                    sh.ckey[q] = ckey[j];
-                    sh.cpos[q] = (uint32_t)j;
-                }
-            }
-        }
-        if (l == 0) wcnt[w] = gtw;
-        lds_barrier();
-        const uint32_t nb1 = sh.ncand;
-        if (nb1 <= (uint32_t)kWave) {
-            // every wave ranks b1's keys on its own (key descending, then slot =
-            // column ascending): lane e holds entry e
-            const uint32_t key = (uint32_t)l < nb1 ? sh.ckey[l] : 0u;
-            const uint32_t pos = (uint32_t)l < nb1 ? sh.cpos[l] : 0u;
-            uint32_t before = 0;
-            for (uint32_t e = 0; e < nb1; ++e) {
-                const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)key, (int)e);
-                const uint32_t op = (uint32_t)__builtin_amdgcn_readlane((int)pos, (int)e);
-                before += (o > key || (o == key && op < pos)) ? 1u : 0u;
-            }
-            const bool sel = (uint32_t)l < nb1 && before < rem;
-            // this wave's first output slot: the keys above b1 in the waves
-            // before it, and the taken b1 keys at lower slots
-            uint32_t slot = (uint32_t)__popcll(__ballot(sel && pos < (uint32_t)(SPW * w)));
-#pragma unroll
-            for (int x = 0; x < NWAVE; ++x) slot += x < w ? wcnt[x] : 0u;
-            // the taken b1 keys of this wave's slots, as bits of its own words
-            // of selb (written and read by this wave only: LDS keeps a wave's
-            // operations in order)
-            if (l < SPW / 32) selb[(SPW / 32) * w + l] = 0u;
-            if (sel && pos / (uint32_t)SPW == (uint32_t)w) atomicOr(&selb[pos >> 5], 1u << (pos & 31u));
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
-            uint32_t *ck = multi ? p.cand_key + ((int64_t)it.t * p.nchunk + it.c) * k : nullptr;
-            int32_t *cp = multi ? p.cand_pos + ((int64_t)it.t * p.nchunk + it.c) * k : out;
-#pragma unroll
-            for (int u = 0; u < SPW_MAX / kWave; ++u) {
-                if (u >= nu) break;
-                const int j = SPW * w + kWave * u + l;
-                bool tk = false;
-                if (j < (int)nc) {
-                    const uint32_t bj = kbin(ckey[j]);
-                    tk = bj > b1 || (bj == b1 && ((selb[j >> 5] >> (j & 31)) & 1u));
-                }
-                const uint64_t mt = __ballot(tk);
-                const uint32_t r = slot + lane_rank(mt);
-                if (tk && r < (uint32_t)k) {   // (exactly k are taken)
-                    cp[r] = c0 + ccol[j];
-                    if (multi) ck[r] = ckey[j];
-                }
-                slot += (uint32_t)__popcll(mt);
-            }
+    if (nc > (uint32_t)k && nc <= (uint32_t)TK_CAP) {
+        // 3. exact select over the candidates (lds_cand_select), written in
+        // column order
+        uint32_t *ck = multi ? p.cand_key + ((int64_t)it.t * p.nchunk + it.c) * k : nullptr;
+        int32_t *cp = multi ? p.cand_pos + ((int64_t)it.t * p.nchunk + it.c) * k : out;
+        if (lds_cand_select<TK_CAP>(ckey, (int)nc, k, cvlo, vmax, sh, gsum, wcnt, [&](uint32_t r, int j) {
+                cp[r] = c0 + ccol[j];
+                if (multi) ck[r] = ckey[j];
+            }))
             return;
-        }
-        lds_barrier();   // every thread has read nb1
     }
     if (nc > (uint32_t)k && nc <= (uint32_t)TK_CAP) {
         // b1 crowded (many equal or near-equal scores) or the range not
