@@ -1,6 +1,7 @@
-// select_core.h — exact top-k select of register-held uint32 keys by one
-// 1024-thread workgroup, shared by the top-k kernels (topk.hip) and the fused
-// indexer + select (indexer_topk.hip).  Selection rule (page "Техотчёт
+// select_core.h — exact top-k selects by one 1024-thread workgroup: of
+// register-held uint32 keys (select_regs: the top-k merge, the fused path's
+// workgroup select and recompute, and the top-k kernel's tie fallback), and of
+// candidate keys staged in LDS (lds_cand_select: the top-k kernel).  Selection rule (page "Техотчёт
 // DeepSeek-V3.2 (2025): разреженное внимание DSA и масштабирование RL",
 // section "Отбор и основное внимание", Top-k(I_{t,:})): the k largest keys,
 // ties to the lower array position; keys are order-preserving images of fp32
