@@ -13,20 +13,23 @@
 // register i of lane l of wave w, so every load instruction reads 64
 // consecutive columns and (wave, register, lane) order is column order):
 //   1. sample  : one key per lane (1024 per full chunk, spread over the
-//                chunk); the rank-th largest sample, rank = mu + 5 sqrt(mu) +
-//                1 with mu = k * samples / columns (the expected number of
-//                samples among the chunk's top k), located by a value
-//                histogram of the samples, gives a threshold a quarter bin
-//                below it.  About 1.6 k keys pass it.
+//                chunk; -inf scores left out); the rank-th largest sample,
+//                rank = mu + 5 sqrt(mu) + 1 with mu = k * samples / columns
+//                (the expected number of samples among the chunk's top k),
+//                located by a value histogram of the samples, gives a
+//                threshold a quarter bin below it.  About 1.6 k keys pass it.
 //   2. compact : the keys at or above the threshold (counted per wave, one
-//                block scan) and their columns go to LDS in column order.
+//                barrier for the offsets) and their columns go to LDS in
+//                column order.
 //   3. select  : when more than k and at most 8192 keys passed, the exact
-//                select of the k largest among them (select_core.h: value
-//                histogram, keys around the k-th one ranked, ascending
-//                output by a block scan), 8 candidates per thread.  Every key
-//                of the exact top k is at or above the k-th largest key,
-//                which is at or above the threshold whenever more than k
-//                keys pass it, so the candidates hold the whole answer.
+//                select of the k largest among them (lds_cand_select of
+//                select_core.h: a value histogram, the bin of the k-th
+//                largest, its few keys ranked, each wave writing its own
+//                slots in column order); with many equal scores in that bin,
+//                the register select of select_core.h.  Every key of the
+//                exact top k is at or above the k-th largest key, which is at
+//                or above the threshold whenever more than k keys pass it, so
+//                the candidates hold the whole answer.
 //   4. fallback: otherwise (a sample that missed, or many equal scores) the
 //                k-th largest key kappa by radix passes over the register
 //                keys, then the keys > kappa and the first keys == kappa in
