@@ -308,6 +308,102 @@ def kl_bench(args, dsa):
     return 0
 
 
+TOPK_METRIC = "standalone top-2048 rows/s over a 32K prefill's index scores (dsa_topk)"
+
+
+def topk_bench(args, dsa):
+    """One step = dsa_topk over the index scores of a 32K prefill (every row
+    of the causal 32768 x 32768 score matrix, the three-step API's select).
+    The scores come from dsa_indexer_scores on the prefill_32k inputs, run
+    once before the timed region."""
+    import torch
+    say = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+    wl, _ = make_workload("prefill_32k")
+    b = wl.batch
+    t0 = time.time()
+    dev = wl.device("cuda")
+    batch = dsa.Batch.from_host(b.cu_q, b.cu_kv, b.pos0)
+    ld = ((b.max_kv + 63) // 64) * 64
+    scores = torch.empty((b.T, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty((b.T, wl.k), dtype=torch.int32, device="cuda")
+    dsa.indexer_scores(batch, dev["qi"], dev["qs"], dev["w"], dev["ki"], dev["ks"], scores)
+    for key in ("qi", "qs", "w", "q", "kv"):
+        dev.pop(key, None)
+    ws = torch.empty(max(1, dsa.workspace_size(dsa.WS_TOPK, batch, wl.k)), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    say(f"[bench] workload topk_32k: T={b.T} k={wl.k}; index scores ready ({time.time() - t0:.1f} s)")
+
+    def step():
+        dsa.topk(batch, scores, wl.k, idx, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    ms_per_step = elapsed * 1e3 / args.steps
+    rows_per_s = b.T * args.steps / elapsed
+    say(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, {rows_per_s:,.0f} rows/s")
+
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(20, args.profile_reps))]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    times = [e0.elapsed_time(e1) for e0, e1 in evs]
+    nvis = visible_counts(b.cu_q, b.cu_kv, b.pos0)
+    roof = kernel_roof("topk_chunk_kernel", wl, "prefill", nvis, float(np.mean(times)), float(np.median(times)))
+    roof["traffic"] = None
+    roof["chosen_by"] = "the entry's only launch (one 32768-column chunk per row)"
+    say(f"[bench] topk_chunk_kernel: {roof['avg_ms']:.4f} ms mean, {roof['median_ms']:.4f} median  "
+        f"{roof['achieved']} GB/s ({100 * roof['frac']:.1f}% of peak, target {100 * roof['target_frac']:.0f}%)")
+    bad = dsa.check_selection(batch, idx)
+    assert bad == 0, f"{bad} rows break the selection contract"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        say("[bench] timing the CPU oracle on a sample of the workload ...")
+        threads = oracle.num_threads()
+        rows_all = np.linspace(0, b.T - 1, 4096).astype(np.int64)
+        host = scores[torch.from_numpy(rows_all).cuda()].cpu().numpy()
+
+        def run(n):
+            sel = np.unique(np.linspace(0, len(rows_all) - 1, n).astype(np.int64))
+            rows = rows_all[sel]
+            s_rows = np.ascontiguousarray(host[sel])
+            t2 = time.perf_counter()
+            oracle.topk(b.cu_q, b.cu_kv, b.pos0, s_rows, wl.k, rows=rows)
+            return len(rows), time.perf_counter() - t2
+        n0, dt = run(64)
+        n = int(min(len(rows_all), max(64, args.cpu_seconds / max(dt / n0, 1e-9))))
+        n, dt = run(n)
+        cpu = {"value": n / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n} query rows evenly spaced over the {b.T} of the workload (the GPU's index "
+                         f"scores of those rows copied to the host first, untimed), {dt:.1f} s wall"}
+        cpu.update(cpu_info())
+        say(f"[bench] CPU oracle: {cpu['value']:.2f} rows/s on {threads} threads")
+
+    cfg = {"workload": "topk_32k", "batch": b.B, "query_tokens": b.T, "max_context": b.max_kv, "topk": wl.k,
+           "score_columns": ld, "entry": "dsa_topk (three-step API)"}
+    line = {"metric": TOPK_METRIC, "value": round(rows_per_s, 1), "unit": "rows/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32 (u32 keys)",
+            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+    if not args.no_peaks:
+        peaks = attainable_peaks(dsa)
+        line["attainable_peaks"] = peaks
+        attach_attainable(roof, peaks)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 BWD_METRIC = "sparse MLA backward tokens/s (dq and dkv over the top-2048 selection), 32K prefill"
 SEED_DOUT = 0xD5A8         # seed of the attention output gradient
 
@@ -523,7 +619,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "prefill_32k", "prefill_4k", "decode_64k", "chunked_128k",
-                             "quant_append_32k", "short_prefill_2k", "indexer_kl_32k", "sparse_bwd_32k"],
+                             "quant_append_32k", "short_prefill_2k", "indexer_kl_32k", "sparse_bwd_32k",
+                             "topk_32k"],
                     help="headline (default): prefill_32k with the decode_64k figures nested in the same line")
     ap.add_argument("--decode-steps", type=int, default=200,
                     help="timed steps of the nested decode_64k figures (at least --steps)")
@@ -560,6 +657,8 @@ def main(argv=None):
 
     if args.workload == "quant_append_32k":
         return quant_append_bench(args, dsa)
+    if args.workload == "topk_32k":
+        return topk_bench(args, dsa)
     if args.workload == "indexer_kl_32k":
         return kl_bench(args, dsa)
     if args.workload == "sparse_bwd_32k":
