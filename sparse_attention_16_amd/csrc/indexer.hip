@@ -91,7 +91,13 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
         }
     }
 
-    // register staging of the next key tile: 1024 16-byte chunks over 512 threads
+    // register staging of the next key tile: 1024 16-byte chunks over 512
+    // threads.  A key row past comp_end loads row c0 instead (a real key
+    // row): the scores of such keys are never used (the candidate test, the
+    // score store and the -inf fill all check key < comp_end), and their
+    // scale is 0.  The loaded values are touched only by put: a select on
+    // them right after the load would make the wave wait for the load, and
+    // with it for every candidate store issued before it.
     i32x4 stage[2];
     float sstage = 0.f;
     auto fetch = [&](int kbase) {
@@ -100,8 +106,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
             const int c = tid + 512 * r;
             const int key = c >> 3, byte = (c & 7) * 16;
             const bool in = kbase + key < comp_end;
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(p.k + (kv0 + (in ? kbase + key : c0)) * DI + byte);
-            stage[r] = in ? v : i32x4{0, 0, 0, 0};
+            stage[r] = *reinterpret_cast<const i32x4 *>(p.k + (kv0 + (in ? kbase + key : c0)) * DI + byte);
         }
         if (tid < PF_KT) sstage = (kbase + tid < comp_end) ? p.k_scale[kv0 + kbase + tid] : 0.f;
     };
@@ -116,7 +121,10 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
     };
     // One barrier per tile: tile i is read from buffer i&1 while tile i+1
     // goes from registers into the other buffer (whose last readers, tile
-    // i-1's, all passed the previous barrier).
+    // i-1's, all passed the previous barrier).  The write to the other buffer
+    // comes before the tile's last group of candidate stores, so that the
+    // wait for the tile loads (issued at the top of the tile) does not also
+    // wait for stores issued just before it.
     if (c0 < comp_end) {
         fetch(c0);
         put(0);
@@ -124,8 +132,11 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
     }
     int cur = 0;
     for (int kbase = c0; kbase < comp_end; kbase += PF_KT, cur ^= 1) {
-        const bool more = kbase + PF_KT < comp_end;
-        if (more) fetch(kbase + PF_KT);
+        // the next tile's loads, issued even after the last tile (they then
+        // read row c0 and fill a buffer nobody reads): unconditional loads
+        // and writes let the compiler see that no load is in flight at the
+        // top of the loop, so it adds no wait there
+        fetch(kbase + PF_KT);
         const uint8_t *ktile = ktiles[cur];
         const float *kscale = kscales[cur];
 
@@ -164,6 +175,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
                 part[r][st & 3] = block_epilogue(ca[st & 1][r], wq[r]);
                 asm volatile("" : "+v"(part[r][st & 3]));
             }
+            if (st == PF_KT / 16 - 1) put(cur ^ 1);
             if ((st & 3) == 3) {
                 // lane l: key kbase + 16*(st-3) + l
                 const int key = kbase + 16 * (st - 3) + l;
@@ -185,7 +197,6 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
             // every block's MFMAs to the front and runs out of registers
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) put(cur ^ 1);
         __syncthreads();
     }
 
