@@ -108,8 +108,8 @@ __device__ uint32_t wave_rank_key(const uint32_t (&kr)[N], int rank, uint32_t *h
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
     const IndexerParams &p = tp.ix;
-    __shared__ __attribute__((aligned(16))) uint8_t ktile[ST_KT * ST_PITCH];
-    __shared__ float kscale[ST_KT];
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[2][ST_KT * ST_PITCH];
+    __shared__ float kscale[2][ST_KT];
     __shared__ uint32_t samp[ST_ROWS][SMP_MAX];
 
     if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
@@ -161,23 +161,43 @@ __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
         load_query(p, (int64_t)(q0 + (valid[r] ? tl : tb)), valid[r], qa[r], wq[r]);
     }
 
-    for (int i0 = 0; i0 < m; i0 += ST_KT) {
-        __syncthreads();
+    // Sampled key tiles of 128 rows (1024 16-byte pieces over 512 threads),
+    // double-buffered: the next tile's loads fly while this tile is scored,
+    // and go from registers to the other LDS buffer after it.  A piece past
+    // the m sampled keys loads the first sampled row instead: its score is
+    // never stored (i < m below), and nothing touches the loaded registers
+    // before their LDS write, so the wave waits for the loads only there.
+    i32x4 stage[2];
+    float sst = 0.f;
+    auto fetch = [&](int i0) {
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {   // 1024 16-byte pieces of 128 gathered key rows
+        for (int rr = 0; rr < 2; ++rr) {
             const int c = tid + 512 * rr;
             const int key = c >> 3, byte = (c & 7) * 16;
             const int i = i0 + key;
             const int s = i < m ? o + i * stride : o;
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(p.k + (kv0 + s) * DI + byte);
-            *reinterpret_cast<i32x4 *>(&ktile[key * ST_PITCH + byte]) = i < m ? v : i32x4{0, 0, 0, 0};
+            stage[rr] = *reinterpret_cast<const i32x4 *>(p.k + (kv0 + s) * DI + byte);
         }
-        if (tid < ST_KT) kscale[tid] = i0 + tid < m ? p.k_scale[kv0 + o + (i0 + tid) * stride] : 0.f;
-        __syncthreads();
+        if (tid < ST_KT) sst = i0 + tid < m ? p.k_scale[kv0 + o + (i0 + tid) * stride] : 0.f;
+    };
+    auto put = [&](int buf) {
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int c = tid + 512 * rr;
+            *reinterpret_cast<i32x4 *>(&ktile[buf][(c >> 3) * ST_PITCH + (c & 7) * 16]) = stage[rr];
+        }
+        if (tid < ST_KT) kscale[buf][tid] = sst;
+    };
+    fetch(0);
+    put(0);
+    __syncthreads();
+    int cur = 0;
+    for (int i0 = 0; i0 < m; i0 += ST_KT, cur ^= 1) {
+        fetch(i0 + ST_KT);   // (past the last tile: the first sampled row, into a buffer nobody reads)
         float part[2][4];
 #pragma unroll
         for (int st = 0; st < ST_KT / 16; ++st) {
-            const uint8_t *src = &ktile[(16 * st + (l & 15)) * ST_PITCH + 32 * (l >> 4)];
+            const uint8_t *src = &ktile[cur][(16 * st + (l & 15)) * ST_PITCH + 32 * (l >> 4)];
             const i32x4 lo = *reinterpret_cast<const i32x4 *>(src);
             const i32x4 hi = *reinterpret_cast<const i32x4 *>(src + 16);
             const i32x8 kb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -191,7 +211,7 @@ __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
                 const int j = 16 * (st - 3) + l;   // lane l: sampled key i0 + j
                 const int i = i0 + j;
                 const int s = o + i * stride;
-                const float ks = kscale[j];
+                const float ks = kscale[cur][j];
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const float v = reduce_scatter4(part[r]);
@@ -199,8 +219,9 @@ __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
                 }
             }
         }
+        put(cur ^ 1);
+        __syncthreads();
     }
-    __syncthreads();
 
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -220,7 +241,7 @@ __global__ __launch_bounds__(512) void indexer_sample_kernel(IdxTopkParams tp) {
             const int rank = (int)ceilf(mu + SMP_SIGMA * sqrtf(mu)) + 1;
             // the rank-th largest sampled key (the key tile is free now: each
             // wave's histogram takes 1 KB of it)
-            if (rank <= mt) tau = wave_rank_key(kr, rank, reinterpret_cast<uint32_t *>(ktile) + 256 * wave);
+            if (rank <= mt) tau = wave_rank_key(kr, rank, reinterpret_cast<uint32_t *>(ktile[0]) + 256 * wave);
         }
         if (l == 0) tp.tau[q0 + tb + 2 * wave + r] = tau;
     }
