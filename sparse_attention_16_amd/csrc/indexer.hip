@@ -67,7 +67,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams p) {
     if (CAND && vis_max <= p.topk_k) return;   // every row of the block selects all it sees
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = lane_id();
 
     // two query rows per wave

@@ -116,7 +116,9 @@ __device__ __forceinline__ float threshold_value(uint32_t tau) {
 // Appends this lane's score to the region at rbase when c holds: one ballot,
 // the lane's rank among the wave's candidates, and a wave-uniform running
 // count (slots past the region's capacity are counted but not written).  The
-// score is stored as its fp32 bits; the select turns it into its key.
+// score is stored as its fp32 bits; the select turns it into its key.  rbase
+// is wave-uniform, so the stores take a scalar base and a 32-bit lane byte
+// offset (slot < cap, and 4 * cap fits 32 bits).
 __device__ __forceinline__ void emit_candidate(const IndexerParams &p, bool c, float score, int key, int64_t rbase,
                                                int &cnt) {
     const uint64_t m = __ballot(c);
@@ -125,8 +127,9 @@ __device__ __forceinline__ void emit_candidate(const IndexerParams &p, bool c, f
                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         const int slot = cnt + rank;
         if (c && slot < p.cap) {
-            p.cand_key[rbase + slot] = __float_as_uint(score);
-            p.cand_pos[rbase + slot] = key;
+            const uint32_t off = 4u * (uint32_t)slot;
+            *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(p.cand_key + rbase) + off) = __float_as_uint(score);
+            *reinterpret_cast<int32_t *>(reinterpret_cast<char *>(p.cand_pos + rbase) + off) = key;
         }
         cnt += __popcll(m);
     }
