@@ -63,19 +63,19 @@ COUNTERS = {
         "sha256_16": "7466d4447ad1d198", "fetch_kib": 11541614, "write_kib": 4352080},
     ("prefill_32k", "indexer_prefill_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
-        "sha256_16": "57f92643179bc90f", "fetch_kib": 209425, "write_kib": 836719},
+        "sha256_16": "57034646161a94bc", "fetch_kib": 208660, "write_kib": 838595},
     ("prefill_4k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
         "sha256_16": "7466d4447ad1d198", "fetch_kib": 475715, "write_kib": 544211},
     ("decode_64k", "indexer_decode_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
-        "sha256_16": "57f92643179bc90f", "fetch_kib": 288537, "write_kib": 2527},
+        "sha256_16": "57034646161a94bc", "fetch_kib": 288538, "write_kib": 2537},
     ("decode_64k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
         "sha256_16": "7466d4447ad1d198", "fetch_kib": 79244, "write_kib": 33951},
     ("chunked_128k", "indexer_prefill_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
-        "sha256_16": "57f92643179bc90f", "fetch_kib": 207034, "write_kib": 305279},
+        "sha256_16": "57034646161a94bc", "fetch_kib": 206919, "write_kib": 282724},
     ("chunked_128k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
         "sha256_16": "7466d4447ad1d198", "fetch_kib": 3987913, "write_kib": 543847},
