@@ -57,16 +57,19 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-// Position of slot (blk * BK + (l & 31)) of the split, or -1 for an unusable
-// slot (past the split's range; a negative or out-of-context idx entry).
-__device__ __forceinline__ int slot_pos(const int32_t *__restrict__ idx_row, int j0, int nsel, int blk, int l,
-                                        int ctx) {
+// Entry of slot (blk * BK + (l & 31)) of the split as loaded: the index
+// entry, the position itself in the dense mode, or -1 past the split's range.
+// slot_checked turns it into a position, or -1 for an unusable slot (a
+// negative or out-of-context entry).  The two are apart so that a freshly
+// issued index load is not consumed at once: that would make the wave wait
+// for it, and with it for every gather load issued before it.
+__device__ __forceinline__ int slot_entry(const int32_t *__restrict__ idx_row, int j0, int nsel, int blk, int l) {
     const int j = blk * BK + (l & 31);
     if (j >= nsel) return -1;
     if (!idx_row) return j0 + j;
-    const int v = idx_row[j];
-    return (v >= 0 && v < ctx) ? v : -1;
+    return idx_row[j];
 }
+__device__ __forceinline__ int slot_checked(int v, int ctx) { return (v >= 0 && v < ctx) ? v : -1; }
 
 // Loads one block's rows into buf: wave w the latent parts of rows
 // 8w .. 8w+7 (one 1 KB load each) and the rope slab of the same rows (lane l:
@@ -157,8 +160,8 @@ __global__ __launch_bounds__(NT, 2) void indexer_kl_kernel(KlParams p) {
     float aQ = 0.f, aA = 0.f, aB = 0.f, mI = -INFINITY, sI = 0.f;
     const float *__restrict__ srow = p.scores + (int64_t)t * p.ld;
 
-    int pcur = nblk > 0 ? slot_pos(idx_row, j0, nsel, 0, l, ri.ctx) : -1;
-    int pnext = nblk > 1 ? slot_pos(idx_row, j0, nsel, 1, l, ri.ctx) : -1;
+    int pcur = nblk > 0 ? slot_checked(slot_entry(idx_row, j0, nsel, 0, l), ri.ctx) : -1;
+    int pnext = nblk > 1 ? slot_checked(slot_entry(idx_row, j0, nsel, 1, l), ri.ctx) : -1;
     float icur = 0.f, inext = 0.f;
     if (nblk > 0) {
         gather_block(pcur, wave, l, kvb, (lds_u8 *)kb[0]);
@@ -175,7 +178,9 @@ __global__ __launch_bounds__(NT, 2) void indexer_kl_kernel(KlParams p) {
             gather_block(pnext, wave, l, kvb, (lds_u8 *)kb[cur ^ 1]);
             if (wave == 0 && pnext >= 0) inext = srow[pnext];
         }
-        const int pn2 = b + 2 < nblk ? slot_pos(idx_row, j0, nsel, b + 2, l, ri.ctx) : -1;
+        // (block b+2's entries are checked only after the block's barrier,
+        // which waits for every load of the wave anyway)
+        int pn2 = b + 2 < nblk ? slot_entry(idx_row, j0, nsel, b + 2, l) : -1;
 
         // S^T = K Q^T: lane holds head (32*wave + 16*ht + row16), keys 16*mt + 4*grp + r
         f32x4 s[2][2];
@@ -226,6 +231,8 @@ __global__ __launch_bounds__(NT, 2) void indexer_kl_kernel(KlParams p) {
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of block b+1
         lds_barrier();
+        asm volatile("" : "+v"(pn2));   // (keeps the check below the wait)
+        pn2 = slot_checked(pn2, ri.ctx);
 
         // wave 0: fold block b into the row's sums
         if (wave == 0 && l < BK && pcur >= 0) {
