@@ -84,7 +84,7 @@ COUNTERS = {
         "sha256_16": "7466d4447ad1d198", "fetch_kib": 192862, "write_kib": 272131},
     ("indexer_kl_32k", "indexer_kl_kernel"): {
         "sources": ("indexer_kl.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "0470cf295c4b0e5a", "fetch_kib": 18004830, "write_kib": 1317},
+        "sha256_16": "6597be1718ec62a9", "fetch_kib": 21677312, "write_kib": 1361},
     # the whole backward (its 10 kernels, 8 row chunks), summed per call
     ("sparse_bwd_32k", "dsa_sparse_mla_bwd"): {
         "sources": ("sparse_mla_bwd.hip", "dsa_device.h", "kernels.h"),
