@@ -656,7 +656,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_contig_kernel
     // last candidate (values there are discarded), and every load is a fixed
     // offset from one lane address.  (The loads are all issued before any of
     // their values is used.)
-    const int R = (c + kWave - 1) / kWave;
+    const int R = __builtin_amdgcn_readfirstlane((c + kWave - 1) / kWave);   // (wave-uniform: scalar branches below)
     const int64_t a_safe = (rows0 + nreg[0]) * p.cap;   // the region's first slot
     const uint32_t *ckey = p.cand_key + a_safe;
     const int32_t *cpos = p.cand_pos + a_safe;
