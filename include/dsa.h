@@ -284,8 +284,10 @@ size_t dsa_decode_fwd_noalloc_max_bytes(void);
  * [max_times] and `n_times` are host memory; kernel names are static
  * strings.  Events are created and destroyed inside the call.  `items`
  * counts what the library itself tallies for a kernel: for the fused
- * select, the candidates it selected over (all rows); for the on-chip
- * recompute, the rows it recomputed; -1 for the others. */
+ * wave select, the candidates it selected over (all rows); for the
+ * workgroup select, the rows it selected (every row of a batch of few rows,
+ * else those the wave select handed on); for the on-chip recompute, the rows
+ * it recomputed; -1 for the others. */
 typedef struct {
     const char *kernel;
     float ms;

@@ -777,8 +777,9 @@ dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, 
     if (st == DSA_OK) st = run_fwd(args, out, lse, idx_out, ws, ws_bytes, stream, decode != 0, &tl);
     if (st == DSA_OK && tl.n > 0) {
         if (!tl.ok || hipEventSynchronize(tl.ev[tl.n]) != hipSuccess) st = DSA_ERR_HIP;
-        // the fused select's counts: queued rows and candidates (its queue header)
-        int32_t fb[3] = {-1, -1, -1};
+        // the fused select's counts (its queue header): rows queued for the
+        // recompute, -, candidates selected, rows handed to the workgroup select
+        int32_t fb[4] = {-1, -1, -1, -1};
         const dsa_batch *b = &args->batch;
         if (st == DSA_OK && b->max_kv > args->k && b->total_q > 0) {
             const CandLayout c = cand_layout(b, args->k, decode != 0);
@@ -797,6 +798,14 @@ dsa_status dsa_fwd_profile(const dsa_fwd_args *args, int decode, uint16_t *out, 
             if (std::strcmp(tl.name[i], "idx_fallback_kernel") == 0) times[i].items = fb[0];
             *n_times = i + 1;
         }
+        // the workgroup select took every row (few rows) or the rows the wave
+        // select handed on (then a wave select ran before it)
+        bool wave_sel = false;
+        for (int i = 0; i < *n_times; ++i)
+            wave_sel |= std::strncmp(times[i].kernel, "cand_select_wave", 16) == 0;
+        for (int i = 0; st == DSA_OK && i < *n_times; ++i)
+            if (std::strcmp(times[i].kernel, "cand_select_kernel") == 0 && fb[3] >= 0)
+                times[i].items = wave_sel ? fb[3] : args->batch.total_q;
     }
     for (int i = 0; i < made; ++i) (void)hipEventDestroy(tl.ev[i]);
     return st;
