@@ -331,8 +331,15 @@ __global__ __launch_bounds__(512) void indexer_sample_row_kernel(IdxTopkParams t
 // rows whose candidates cannot be complete go to the recompute queue.
 // ---------------------------------------------------------------------------
 constexpr int SEL_WAVES = 4;        // rows per workgroup of the wave select
-constexpr int SEL_R = 64;           // candidates per lane, at most
+constexpr int SEL_R = 64;           // candidates per lane, at most (the contiguous select)
 constexpr int SEL_WAVE_MAX = SEL_R * kWave;
+// The multi-region select holds RR candidates per lane, its taken-register
+// mask in two words: 64 for contexts up to 32768 keys (rows keep ~3.4k
+// candidates), 88 beyond (~3.9k at 64K, ~4.7k at 128K, which would overflow
+// 64 and go to the workgroup select; 88 still fits two waves per SIMD).
+constexpr int SEL_R_LONG = 88;
+constexpr int SEL_LONG_CTX = 32768;   // longest context that takes the 64-register select
+static_assert(SEL_R <= 64 && SEL_R_LONG <= 128, "taken-register masks");
 constexpr int SEL_BINS = 256;      // value bins of the wave select's histogram
 constexpr int SEL_BLOCK_ROWS = 4;   // batches of at most this many rows per compute unit: workgroup select
 
@@ -343,7 +350,9 @@ __device__ __forceinline__ uint32_t wave_excl_add(uint32_t v) { return wave_scan
 
 }  // namespace
 
+template <int SEL_R_MR>
 __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTopkParams tp, int T) {
+    constexpr int SEL_WAVE_MAX_MR = SEL_R_MR * kWave;
     const IndexerParams &p = tp.ix;
     __shared__ int32_t npre_s[SEL_WAVES][MAX_SEG + 1];
     __shared__ int16_t nreg_s[SEL_WAVES][MAX_SEG];
@@ -394,7 +403,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
         return;
     }
     if (l == 0) atomicAdd(&tp.fb[2], c);
-    if (c > SEL_WAVE_MAX) {   // too many for one wave's registers: the workgroup select takes it
+    if (c > SEL_WAVE_MAX_MR) {   // too many for one wave's registers: the workgroup select takes it
         if (l == 0) {
             const int slot = atomicAdd(&tp.fb[3], 1);
             tp.fb[FB_LIST + T + slot] = t;
@@ -417,10 +426,10 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
     // Slot of each of this lane's candidates, walking the (non-empty) regions
     // forward: consecutive candidates cross at most one boundary.  The loads
     // are all issued before any of their values is used.
-    uint32_t kr[SEL_R];
+    uint32_t kr[SEL_R_MR];
     if (nr == 1) {   // the whole row in one region (prefill layout): consecutive slots
 #pragma unroll
-        for (int i = 0; i < SEL_R; ++i) {
+        for (int i = 0; i < SEL_R_MR; ++i) {
             const int j = j0 + i;
             kr[i] = p.cand_key[i < R && j < c ? a_safe + j : a_safe];
         }
@@ -428,7 +437,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
         int e = e0, bnd = npre[e0 + 1];
         int64_t dlt = (rows0 + nreg[e0]) * p.cap - npre[e0];
 #pragma unroll
-        for (int i = 0; i < SEL_R; ++i) {
+        for (int i = 0; i < SEL_R_MR; ++i) {
             const int j = j0 + i;
             const bool in = i < R && j < c;
             if (in && j >= bnd) {
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
         }
     }
 #pragma unroll
-    for (int i = 0; i < SEL_R; ++i) kr[i] = (i < R && j0 + i < c) ? score_key(__uint_as_float(kr[i])) : 0u;
+    for (int i = 0; i < SEL_R_MR; ++i) kr[i] = (i < R && j0 + i < c) ? score_key(__uint_as_float(kr[i])) : 0u;
     // kappa, the k-th largest key.  A 256-bin histogram of the keys by value
     // over [min, max] (a non-decreasing map, so bins keep the order) names the
     // bin b1 that holds it; b1's keys (a few dozen on spread-out scores) are
@@ -452,7 +461,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
     {
         uint32_t lmn = 0xFFFFFFFFu, lmx = 0u;
 #pragma unroll
-        for (int i = 0; i < SEL_R; ++i) {
+        for (int i = 0; i < SEL_R_MR; ++i) {
             lmn = kr[i] != 0u && kr[i] < lmn ? kr[i] : lmn;
             lmx = kr[i] > lmx ? kr[i] : lmx;
         }
@@ -471,7 +480,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
                 return (uint32_t)fminf((key_value(key) - vmin) * inv, (float)(SEL_BINS - 1));
             };
 #pragma unroll
-            for (int i = 0; i < SEL_R; ++i)
+            for (int i = 0; i < SEL_R_MR; ++i)
                 if (kr[i] != 0u) atomicAdd(&hist[bin_of(kr[i])], 1u);
             // lane l owns bins top - 4l - q (q < 4), scanned from the top
             uint32_t c4[SEL_BINS / kWave], sum = 0;
@@ -500,7 +509,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
                 uint32_t *lst = list_s[wave];
                 uint32_t cnt = 0;
 #pragma unroll
-                for (int i = 0; i < SEL_R; ++i) {
+                for (int i = 0; i < SEL_R_MR; ++i) {
                     const bool inb = kr[i] != 0u && bin_of(kr[i]) == b1;
                     const uint64_t m = __ballot(inb);
                     if (inb) {
@@ -529,14 +538,14 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
             const uint32_t y = x | (1u << bit);
             int cnt = 0;
 #pragma unroll
-            for (int i = 0; i < SEL_R; ++i) cnt += __popcll(__ballot(kr[i] >= y));
+            for (int i = 0; i < SEL_R_MR; ++i) cnt += __popcll(__ballot(kr[i] >= y));
             if (cnt >= k) x = y;
         }
         kappa = x;
     }
     uint32_t gt = 0, eq = 0;
 #pragma unroll
-    for (int i = 0; i < SEL_R; ++i) {
+    for (int i = 0; i < SEL_R_MR; ++i) {
         gt += kr[i] > kappa ? 1u : 0u;
         eq += kr[i] == kappa ? 1u : 0u;
     }
@@ -549,24 +558,24 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
     uint32_t slot = wave_excl_add(gt + eq_take);
     // selected candidates as a bit mask, then their positions (loads first,
     // into the key registers), then the ascending writes
-    uint64_t take = 0ull;
+    uint64_t take[2] = {0ull, 0ull};   // bit i % 64 of word i / 64: register i taken
 #pragma unroll
-    for (int i = 0; i < SEL_R; ++i) {
+    for (int i = 0; i < SEL_R_MR; ++i) {
         bool tk = kr[i] > kappa;
         if (kr[i] == kappa && eq_take != 0u) {
             tk = true;
             --eq_take;
         }
-        take |= (uint64_t)(tk ? 1u : 0u) << i;
+        take[i / 64] |= (uint64_t)(tk ? 1u : 0u) << (i % 64);
     }
     if (nr == 1) {
 #pragma unroll
-        for (int i = 0; i < SEL_R; ++i) kr[i] = (uint32_t)p.cand_pos[(take >> i) & 1ull ? a_safe + j0 + i : a_safe];
+        for (int i = 0; i < SEL_R_MR; ++i) kr[i] = (uint32_t)p.cand_pos[(take[i / 64] >> (i % 64)) & 1ull ? a_safe + j0 + i : a_safe];
     } else {
         int e = e0, bnd = npre[e0 + 1];
         int64_t dlt = (rows0 + nreg[e0]) * p.cap - npre[e0];
 #pragma unroll
-        for (int i = 0; i < SEL_R; ++i) {
+        for (int i = 0; i < SEL_R_MR; ++i) {
             const int j = j0 + i;
             const bool in = i < R && j < c;
             if (in && j >= bnd) {
@@ -574,12 +583,12 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void cand_select_wave_kernel(IdxTop
                 bnd = npre[e + 1];
                 dlt = (rows0 + nreg[e]) * p.cap - npre[e];
             }
-            kr[i] = (uint32_t)p.cand_pos[(take >> i) & 1ull ? dlt + j : a_safe];
+            kr[i] = (uint32_t)p.cand_pos[(take[i / 64] >> (i % 64)) & 1ull ? dlt + j : a_safe];
         }
     }
 #pragma unroll
-    for (int i = 0; i < SEL_R; ++i)
-        if ((take >> i) & 1ull) out[slot++] = (int32_t)kr[i];
+    for (int i = 0; i < SEL_R_MR; ++i)
+        if ((take[i / 64] >> (i % 64)) & 1ull) out[slot++] = (int32_t)kr[i];
 }
 
 // cand_select_wave_contig_kernel: the same select with candidate j = 64 i + l
@@ -1051,7 +1060,8 @@ hipError_t launch_indexer_topk(const IdxTopkParams &tp, int T, int max_q, bool d
             hipLaunchKernelGGL(cand_select_wave_contig_kernel, dim3((T + SEL_WAVES - 1) / SEL_WAVES),
                                dim3(64 * SEL_WAVES), 0, s, tp, T);
         else
-            hipLaunchKernelGGL(cand_select_wave_kernel, dim3((T + SEL_WAVES - 1) / SEL_WAVES),
+            hipLaunchKernelGGL(p.max_kv > SEL_LONG_CTX ? cand_select_wave_kernel<SEL_R_LONG> : cand_select_wave_kernel<SEL_R>,
+                               dim3((T + SEL_WAVES - 1) / SEL_WAVES),
                                dim3(64 * SEL_WAVES), 0, s, tp, T);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (marks) marks->after(p.nseg == 1 ? "cand_select_wave_contig_kernel" : "cand_select_wave_kernel", s);
