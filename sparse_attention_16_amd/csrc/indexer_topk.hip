@@ -260,14 +260,27 @@ __global__ __launch_bounds__(512) void indexer_sample_row_kernel(IdxTopkParams t
         for (int i = 0; i < FB_LIST; ++i) tp.fb[i] = 0;   // queues empty, counts 0 (this kernel runs first)
     }
     const int t = blockIdx.x;
-    const RowInfo ri = row_info(p.cu_q, p.cu_kv, p.pos0, p.B, p.total_kv, p.max_kv, t);
-    const int n = ri.nvis, k = tp.k;
+    // the row's sequence and visible keys (row_info's arithmetic, from one
+    // search of cu_q: the sample offset needs the sequence as well)
+    const int b = find_seq(p.cu_q, p.B, t);
+    int n;
+    int64_t kv0;
+    {
+        int64_t a = p.cu_kv[b], e = p.cu_kv[b + 1];
+        a = a < 0 ? 0 : (a > p.total_kv ? p.total_kv : a);
+        e = e < a ? a : (e > p.total_kv ? p.total_kv : e);
+        const int64_t c = e - a;
+        const int ctx = (int)(c > p.max_kv ? p.max_kv : c);
+        const int nv = p.pos0[b] + (t - p.cu_q[b]) + 1;
+        n = nv < 0 ? 0 : (nv > ctx ? ctx : nv);
+        kv0 = a;
+    }
+    const int k = tp.k;
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
     if (n <= NO_SAMPLE || n <= k) {
         if (tid == 0) tp.tau[t] = 0u;
         return;
     }
-    const int b = find_seq(p.cu_q, p.B, t);
     const int block = (t - p.cu_q[b]) / ST_ROWS;
     int m = n / SMP_RATE;
     m = m < SMP_MIN ? SMP_MIN : (m > SMP_MAX ? SMP_MAX : m);
@@ -282,7 +295,7 @@ __global__ __launch_bounds__(512) void indexer_sample_row_kernel(IdxTopkParams t
     for (int st = 0; st < 8; ++st) {
         const int i = 128 * wave + 16 * st + (l & 15);
         const int s = i < m ? o + i * stride : o;
-        const uint8_t *src = p.k + (ri.kv0 + s) * DI + 32 * (l >> 4);
+        const uint8_t *src = p.k + (kv0 + s) * DI + 32 * (l >> 4);
         const i32x4 lo = *reinterpret_cast<const i32x4 *>(src);
         const i32x4 hi = *reinterpret_cast<const i32x4 *>(src + 16);
         kb[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -291,7 +304,7 @@ __global__ __launch_bounds__(512) void indexer_sample_row_kernel(IdxTopkParams t
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int i = 128 * wave + 64 * h + l;
-        ks[h] = i < m ? p.k_scale[ri.kv0 + o + i * stride] : 0.f;
+        ks[h] = i < m ? p.k_scale[kv0 + o + i * stride] : 0.f;
     }
     float part[4];
 #pragma unroll
