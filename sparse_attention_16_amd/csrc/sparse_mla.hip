@@ -520,28 +520,37 @@ __global__ __launch_bounds__(NTHREADS) void sparse_mla_kernel(
         }
     }
     __syncthreads();
-    const int c0 = CT_W * 16 * wave + 4 * grp;
+    // 16-byte stores: lanes grp and grp ^ 1 (l and l ^ 16, the same head)
+    // exchange one 8-byte half, so that for each pair of value tiles
+    // (2u, 2u+1) an even-grp lane holds 8 consecutive columns of tile 2u and
+    // an odd-grp lane 8 of tile 2u+1; half the store instructions of one
+    // 8-byte store per tile and lane
+    static_assert(CT_W % 2 == 0, "value tiles in pairs");
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    const bool odd = (grp & 1) != 0;
+    uint16_t *obase = p.splits == 1 ? out + (int64_t)t * H * DV
+                                    : o_part + ((int64_t)t * p.splits + split) * H * DV;
+    const int cw = CT_W * 16 * wave + 16 * (grp & 1) + 4 * (grp & 2);
 #pragma unroll
     for (int T = 0; T < HT_ALL; ++T) {
         const int h = 16 * T + row16;
         const float l_tot = lsh[h];
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (p.splits == 1) {
-            uint16_t *orow = out + ((int64_t)t * H + h) * DV + c0;
+        uint16_t *orow = obase + (int64_t)h * DV + cw;
 #pragma unroll
-            for (int ct = 0; ct < CT_W; ++ct) {
-                const bf16x4 v = {(__bf16)(o[T][ct][0] * inv), (__bf16)(o[T][ct][1] * inv),
-                                  (__bf16)(o[T][ct][2] * inv), (__bf16)(o[T][ct][3] * inv)};
-                *reinterpret_cast<bf16x4 *>(orow + 16 * ct) = v;
-            }
-        } else {
-            uint16_t *orow = o_part + (((int64_t)t * p.splits + split) * H + h) * DV + c0;
-#pragma unroll
-            for (int ct = 0; ct < CT_W; ++ct) {
-                const bf16x4 v = {(__bf16)(o[T][ct][0] * inv), (__bf16)(o[T][ct][1] * inv),
-                                  (__bf16)(o[T][ct][2] * inv), (__bf16)(o[T][ct][3] * inv)};
-                *reinterpret_cast<bf16x4 *>(orow + 16 * ct) = v;
-            }
+        for (int u = 0; u < CT_W / 2; ++u) {
+            const bf16x4 a = {(__bf16)(o[T][2 * u][0] * inv), (__bf16)(o[T][2 * u][1] * inv),
+                              (__bf16)(o[T][2 * u][2] * inv), (__bf16)(o[T][2 * u][3] * inv)};
+            const bf16x4 b = {(__bf16)(o[T][2 * u + 1][0] * inv), (__bf16)(o[T][2 * u + 1][1] * inv),
+                              (__bf16)(o[T][2 * u + 1][2] * inv), (__bf16)(o[T][2 * u + 1][3] * inv)};
+            const u32x2 ab = __builtin_bit_cast(u32x2, a), bb = __builtin_bit_cast(u32x2, b);
+            // the half the partner needs: tile 2u+1 from an even lane, tile 2u from an odd one
+            const u32x2 give = odd ? ab : bb;
+            const u32x2 got = {(uint32_t)__builtin_amdgcn_ds_swizzle((int)give[0], 0x401F),
+                               (uint32_t)__builtin_amdgcn_ds_swizzle((int)give[1], 0x401F)};
+            const u32x4 v = odd ? u32x4{got[0], got[1], bb[0], bb[1]} : u32x4{ab[0], ab[1], got[0], got[1]};
+            *reinterpret_cast<u32x4 *>(orow + 32 * u) = v;
         }
     }
 }
