@@ -60,28 +60,28 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COUNTERS = {
     ("prefill_32k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "7466d4447ad1d198", "fetch_kib": 11541614, "write_kib": 4352080},
+        "sha256_16": "d6ff1a9654508436", "fetch_kib": 11540942, "write_kib": 4342829},
     ("prefill_32k", "indexer_prefill_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
         "sha256_16": "57034646161a94bc", "fetch_kib": 208660, "write_kib": 838595},
     ("prefill_4k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "7466d4447ad1d198", "fetch_kib": 475715, "write_kib": 544211},
+        "sha256_16": "d6ff1a9654508436", "fetch_kib": 475718, "write_kib": 542843},
     ("decode_64k", "indexer_decode_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
         "sha256_16": "57034646161a94bc", "fetch_kib": 288538, "write_kib": 2537},
     ("decode_64k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "7466d4447ad1d198", "fetch_kib": 79244, "write_kib": 33951},
+        "sha256_16": "d6ff1a9654508436", "fetch_kib": 79250, "write_kib": 33922},
     ("chunked_128k", "indexer_prefill_kernel<cand>"): {
         "sources": ("indexer.hip", "indexer_core.h", "dsa_device.h", "kernels.h"),
         "sha256_16": "57034646161a94bc", "fetch_kib": 206919, "write_kib": 282724},
     ("chunked_128k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "7466d4447ad1d198", "fetch_kib": 3987913, "write_kib": 543847},
+        "sha256_16": "d6ff1a9654508436", "fetch_kib": 3980437, "write_kib": 542764},
     ("short_prefill_2k", "sparse_mla_kernel"): {
         "sources": ("sparse_mla.hip", "dsa_device.h", "kernels.h"),
-        "sha256_16": "7466d4447ad1d198", "fetch_kib": 192862, "write_kib": 272131},
+        "sha256_16": "d6ff1a9654508436", "fetch_kib": 192795, "write_kib": 271420},
     ("indexer_kl_32k", "indexer_kl_kernel"): {
         "sources": ("indexer_kl.hip", "dsa_device.h", "kernels.h"),
         "sha256_16": "6597be1718ec62a9", "fetch_kib": 21677312, "write_kib": 1361},
